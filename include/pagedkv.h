@@ -1,0 +1,227 @@
+/*
+ * pagedkv.h — batched attention over a paged KV cache, C ABI (gfx950).
+ *
+ * What the library does (TensorSharp "高级功能" page):
+ *  - section "连续批处理与分页 KV 缓存": the KV cache is split into fixed-size
+ *    blocks taken from one shared pool, so memory is allocated per block; every
+ *    full block is content-hashed and identical prefixes are shared between
+ *    concurrent and later requests instead of being recomputed;
+ *  - section "原生分页注意力": one native call gathers K/V out of the paged
+ *    buffers for many sequences and runs attention over them, with a variant
+ *    that takes per-head sink logits; the "批量前向" paragraph of that section
+ *    pairs every batched forward with a paged K/V scatter-write;
+ *  - section "内存优化", paged KV pool item: LRU eviction and cross-session
+ *    content-hash reuse of cached blocks.
+ * One call serves single-token decode rows, chunked-prefill rows (section
+ * "性能优化", chunked prefill item) and speculative-verify windows (section
+ * "MTP / NextN 推测解码": all drafted rows are verified in one batched forward).
+ *
+ * Conventions for every entry point:
+ *  - Return value: KV_OK (0) or a negative KV_E* code. The message of the last
+ *    failure on the calling thread is available from kv_last_error() until the
+ *    next failing call on that thread. No C++ exception crosses this boundary.
+ *  - On any error, out-parameters and pool state are left unchanged.
+ *  - Device entry points take device pointers that the caller owns (allocated
+ *    with hipMalloc or by PyTorch); they enqueue work on `hip_stream`
+ *    (a hipStream_t, NULL = default stream) and return without synchronising.
+ *    Buffers must stay valid until that work has completed. The library keeps
+ *    no device pointer after a call returns.
+ *  - Host arguments are validated before anything is enqueued. Contents of
+ *    device arrays (block ids, lengths, offsets) are the caller's contract:
+ *    kernels never read or write outside the buffers whose sizes the host
+ *    arguments describe (out-of-range block ids are treated as empty blocks),
+ *    but results for a row whose metadata breaks the contract are unspecified.
+ *
+ * Pool layout (the pages fix none; this is the library's interface).
+ * X = 16 / sizeof(element): 8 for bf16, 4 for fp32. block_size = 16.
+ *   K_pool [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *   V_pool [num_blocks][num_kv_heads][head_dim][block_size]
+ * Token t of a sequence lives in physical block block_table[t / 16] at offset
+ * t % 16; its slot id is block * 16 + offset. K keeps each token's 16-byte
+ * pieces of the head dimension side by side across the 16 tokens of a block;
+ * V is stored transposed within a block (one row of 16 tokens per channel).
+ * Both make every (block, KV head) tile a contiguous 16 * head_dim element run.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kv_status {
+    KV_OK = 0,
+    KV_EINVAL = -1,        /* invalid host argument (null pointer, size, shape) */
+    KV_ENOMEM = -2,        /* pool has too few free blocks */
+    KV_EUNSUPPORTED = -3,  /* no kernel for this (dtype, head_dim, block_size) */
+    KV_EDEVICE = -4,       /* HIP runtime reported an error at launch */
+    KV_EINTERNAL = -5      /* unexpected internal failure */
+};
+
+enum kv_dtype { KV_F32 = 0, KV_BF16 = 1 };
+
+#define PAGEDKV_ABI_VERSION 1
+
+/* ABI version of the loaded library (PAGEDKV_ABI_VERSION). */
+int kv_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). The pointer is
+ * owned by the library and stays valid until the next failing call on the
+ * thread. */
+const char *kv_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Host block manager (touches no device memory)                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct kv_pool kv_pool;
+
+/*
+ * Create a block manager for a caller-owned device pool of `num_blocks` blocks
+ * of `block_size` tokens ("连续批处理与分页 KV 缓存": fixed-size blocks from a
+ * shared pool). The free list is FIFO; it starts in `initial_free_order`
+ * (a permutation of 0..num_blocks-1, copied) or in ascending order if NULL.
+ * *out receives the new pool, owned by the caller and freed by
+ * kv_pool_destroy. A pool is not thread-safe: callers serialise access.
+ * Errors: KV_EINVAL (non-positive sizes, not a permutation, out == NULL).
+ */
+int kv_pool_create(int32_t num_blocks, int32_t block_size,
+                   const int32_t *initial_free_order, kv_pool **out);
+
+/* Free a pool created by kv_pool_create (NULL is ignored). */
+void kv_pool_destroy(kv_pool *pool);
+
+/*
+ * Append `n_new` tokens (host array `new_token_ids`) to sequence `seq_id`
+ * (created on first use) and place them in blocks ("块哈希前缀共享": every full
+ * block is content-hashed and identical prefixes share physical blocks).
+ *
+ * Policy, in order:
+ *  1. a partially filled last block of the sequence is filled in place;
+ *  2. each new full block whose first token is new gets the chained hash
+ *     h_j = FNV-1a-64(h_{j-1} as 8 little-endian bytes || its block_size token
+ *     ids as int32 little-endian), h_{-1} = 0; if a registered block has that
+ *     hash, the same token ids and the same parent block (same physical block,
+ *     same reuse generation) it is shared: its refcount goes up and, if it sat
+ *     unreferenced in the free list, it is taken out; its tokens get slot -1
+ *     (already resident, nothing to write);
+ *  3. every other block is popped from the front of the free list (a cached
+ *     block that is popped loses its hash entry); a new full block is then
+ *     registered under its hash unless another block already holds that hash.
+ *     Partial blocks are private and unhashed until they fill up.
+ * Because sharing needs an unbroken chain of shared parents, hits only happen
+ * for a run of blocks that starts at a block boundary.
+ *
+ * Outputs (host arrays, caller-owned):
+ *   block_table_row [max_blocks]: the sequence's physical block ids, -1 past
+ *                                 its last block;
+ *   *num_blocks: blocks used; *context_len: tokens after the append;
+ *   slot_mapping [n_new]: slot id of each new token, or -1 if it is already
+ *                         resident in a shared block.
+ * Errors: KV_EINVAL (null pool/pointers with n_new > 0, n_new < 0, sequence
+ * would need more than max_blocks blocks), KV_ENOMEM (free list too short;
+ * nothing is changed).
+ */
+int kv_pool_alloc(kv_pool *pool, int64_t seq_id, const int32_t *new_token_ids, int32_t n_new,
+                  int32_t *block_table_row, int32_t max_blocks, int32_t *num_blocks,
+                  int32_t *context_len, int32_t *slot_mapping);
+
+/*
+ * Drop sequence `seq_id`. Its blocks lose one reference each, last block
+ * first; blocks that reach zero go to the back of the free list and keep their
+ * hash entry, so a later request with the same prefix can still share them
+ * until they are popped again ("内存优化": LRU eviction, cross-session reuse).
+ * Errors: KV_EINVAL (null pool, unknown sequence).
+ */
+int kv_pool_release(kv_pool *pool, int64_t seq_id);
+
+/* Counts: blocks in the free list, of which still hash-addressable (cached),
+ * and blocks with a nonzero refcount. Any output pointer may be NULL. */
+int kv_pool_stats(const kv_pool *pool, int32_t *free_blocks, int32_t *cached_blocks,
+                  int32_t *live_blocks);
+
+/* Test hook: every block hash computed from now on is ANDed with `mask`
+ * (default all ones). A narrow mask forces hash collisions, which must never
+ * make two different token runs share a block, because a hit also compares
+ * the token ids and the parent block. Errors: KV_EINVAL (null pool). */
+int kv_pool_set_hash_mask(kv_pool *pool, uint64_t mask);
+
+/* ------------------------------------------------------------------------ */
+/* Device entry points                                                        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Paged K/V scatter-write ("批量前向" paragraph: paged K/V scatter-write).
+ * For each i < n with slot = slot_mapping[i] >= 0:
+ *   K_pool[slot / 16][h][d / X][slot % 16][d % X] = k_new[i][h][d]
+ *   V_pool[slot / 16][h][d][slot % 16]            = v_new[i][h][d]
+ * for all h < num_kv_heads, d < head_dim: a bit copy. Slots of -1 are skipped;
+ * slots outside the pool are skipped. Slots must be distinct within a call.
+ *   k_new, v_new  device [n][num_kv_heads][head_dim], element type `dtype`
+ *   slot_mapping  device int32 [n]
+ *   k_pool, v_pool device pools in the layout above, num_blocks blocks
+ * Supported: dtype KV_BF16 or KV_F32, head_dim a multiple of 16 up to 256,
+ * block_size 16. Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
+ */
+int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_mapping,
+                      int32_t n, void *k_pool, void *v_pool, int32_t num_blocks,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t dtype, void *hip_stream);
+
+/*
+ * Bytes of device workspace paged_attention_forward needs for these sizes
+ * (0 on invalid sizes). The workspace holds per-split partial results.
+ */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
+                                      int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_context_len);
+
+/*
+ * Batched attention over the paged cache ("原生分页注意力"; sinks: its WithSinks
+ * variant). Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]
+ * (q_len rows) and context_lens[s] keys, which include its q_len new tokens
+ * (scatter them first, on the same stream). Row r of s sits at position
+ * p = context_lens[s] - q_len + r and attends to keys 0..p (causal, bottom-right
+ * aligned: decode rows see the whole context, verify and prefill rows see the
+ * keys up to themselves). Query head h reads KV head h / (num_q_heads /
+ * num_kv_heads). For every row i and query head h:
+ *   x_t = scale * <q[i][h], k_t>,  M = max(max_t x_t, sinks[h] if sinks),
+ *   out[i][h] = sum_t e^{x_t - M} v_t / (sum_t e^{x_t - M} + e^{sinks[h] - M}),
+ * the sink term present only when `sinks` is non-NULL; the sink logit is not
+ * multiplied by `scale` and carries no value vector.
+ *
+ *   q               device [total_q_rows][num_q_heads][head_dim], type `dtype`
+ *   k_pool, v_pool  device pools (layout above), type `dtype`
+ *   block_tables    device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens    device int32 [num_seqs], 1 <= q_len <= context_lens[s]
+ *                   <= max_context_len
+ *   query_start_loc device int32 [num_seqs + 1], ascending, [0] = 0,
+ *                   [num_seqs] = total_q_rows, q_len <= max_q_len
+ *   sinks           device float [num_q_heads] or NULL
+ *   out             device float [total_q_rows][num_q_heads][head_dim]
+ *   workspace       device, >= paged_attention_workspace_size(...) bytes
+ * max_q_len and max_context_len only size the launch and the workspace; they
+ * never change a result. Every row's arithmetic depends only on its own query,
+ * its visible keys and values, scale and sink: the same row gives the same bits
+ * alone, in any batch, and inside any window (a verify window row equals the
+ * same query run as a single decode row over the keys up to it).
+ * Supported: head_dim 64 or 128, block_size 16, dtype KV_BF16 or KV_F32.
+ * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
+ */
+int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *query_start_loc,
+                            int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                            int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                            const float *sinks, float *out, void *workspace,
+                            size_t workspace_bytes, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,252 @@
+"""Batched attention over a paged KV cache on MI355X (gfx950): Python binding.
+
+Thin ctypes binding over ``libpagedkv.so`` (declared in ``include/pagedkv.h``).
+Functions carry the C names and only marshal arguments: torch tensors are
+passed by device pointer, shapes become the size arguments, and every step of
+the computation runs in the library's HIP kernels. PyTorch supplies device
+memory and streams. If the library is missing the import fails: there is no
+fallback path.
+
+Pool layout (see the header): with X = 16 bytes / element size,
+``K_pool [num_blocks, Hkv, D // X, 16, X]`` and ``V_pool [num_blocks, Hkv, D, 16]``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "KV_OK", "KV_EINVAL", "KV_ENOMEM", "KV_EUNSUPPORTED", "KV_EDEVICE", "KV_EINTERNAL",
+    "KV_F32", "KV_BF16", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
+    "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
+    "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_workspace_size",
+    "paged_attention_forward", "empty_pools", "BLOCK_SIZE",
+]
+
+KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
+KV_F32, KV_BF16 = 0, 1
+BLOCK_SIZE = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libpagedkv.so")
+
+if not os.path.exists(lib_path):
+    raise ImportError(f"{lib_path} is missing: build it with __graft_entry__.build() "
+                      "or python paged_kv_attention_block_amd/build.py")
+
+_lib = ctypes.CDLL(lib_path)
+
+_i32, _i64, _u64, _f32, _p, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float,
+                                   ctypes.c_void_p, ctypes.c_size_t)
+_lib.kv_abi_version.restype = ctypes.c_int
+_lib.kv_last_error.restype = ctypes.c_char_p
+_lib.kv_pool_create.argtypes = [_i32, _i32, _p, ctypes.POINTER(_p)]
+_lib.kv_pool_destroy.argtypes = [_p]
+_lib.kv_pool_destroy.restype = None
+_lib.kv_pool_alloc.argtypes = [_p, _i64, _p, _i32, _p, _i32, _p, _p, _p]
+_lib.kv_pool_release.argtypes = [_p, _i64]
+_lib.kv_pool_stats.argtypes = [_p, _p, _p, _p]
+_lib.kv_pool_set_hash_mask.argtypes = [_p, _u64]
+_lib.kv_append_scatter.argtypes = [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]
+_lib.paged_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+_lib.paged_attention_workspace_size.restype = _sz
+_lib.paged_attention_forward.argtypes = [
+    _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    _f32, _p, _p, _p, _sz, _p]
+for _name in ("kv_pool_create", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
+              "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_forward"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+class KVError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+        self.message = message
+
+
+def _check(rc: int):
+    if rc != KV_OK:
+        raise KVError(rc, _lib.kv_last_error().decode(errors="replace"))
+
+
+def kv_abi_version() -> int:
+    return _lib.kv_abi_version()
+
+
+def kv_last_error() -> str:
+    return _lib.kv_last_error().decode(errors="replace")
+
+
+# ---------------------------------------------------------------------------
+# host block manager
+# ---------------------------------------------------------------------------
+
+class _Pool:
+    __slots__ = ("ptr", "num_blocks", "block_size")
+
+    def __init__(self, ptr, num_blocks, block_size):
+        self.ptr, self.num_blocks, self.block_size = ptr, num_blocks, block_size
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            _lib.kv_pool_destroy(self.ptr)
+            self.ptr = None
+
+
+def kv_pool_create(num_blocks: int, block_size: int = BLOCK_SIZE, initial_free_order=None) -> _Pool:
+    out = _p()
+    order = None
+    if initial_free_order is not None:
+        order = np.ascontiguousarray(np.asarray(initial_free_order, dtype=np.int32))
+        if order.size != num_blocks:
+            raise KVError(KV_EINVAL, "initial_free_order must hold num_blocks entries")
+    _check(_lib.kv_pool_create(num_blocks, block_size, None if order is None else order.ctypes.data,
+                               ctypes.byref(out)))
+    return _Pool(out.value, num_blocks, block_size)
+
+
+def kv_pool_destroy(pool: _Pool) -> None:
+    if pool.ptr:
+        _lib.kv_pool_destroy(pool.ptr)
+        pool.ptr = None
+
+
+def kv_pool_alloc(pool: _Pool, seq_id: int, new_token_ids, max_blocks: int):
+    """Returns (block_table_row int32[max_blocks], num_blocks, context_len, slot_mapping int32[n])."""
+    toks = np.ascontiguousarray(np.asarray(new_token_ids, dtype=np.int32).reshape(-1))
+    row = np.empty(max_blocks, dtype=np.int32)
+    slots = np.empty(max(1, toks.size), dtype=np.int32)
+    nb, ctx = _i32(), _i32()
+    _check(_lib.kv_pool_alloc(pool.ptr, seq_id, toks.ctypes.data if toks.size else None, toks.size,
+                              row.ctypes.data, max_blocks, ctypes.byref(nb), ctypes.byref(ctx),
+                              slots.ctypes.data))
+    return row, nb.value, ctx.value, slots[:toks.size]
+
+
+def kv_pool_release(pool: _Pool, seq_id: int) -> None:
+    _check(_lib.kv_pool_release(pool.ptr, seq_id))
+
+
+def kv_pool_stats(pool: _Pool):
+    f, c, l = _i32(), _i32(), _i32()
+    _check(_lib.kv_pool_stats(pool.ptr, ctypes.byref(f), ctypes.byref(c), ctypes.byref(l)))
+    return f.value, c.value, l.value
+
+
+def kv_pool_set_hash_mask(pool: _Pool, mask: int) -> None:
+    _check(_lib.kv_pool_set_hash_mask(pool.ptr, mask & 0xFFFFFFFFFFFFFFFF))
+
+
+# ---------------------------------------------------------------------------
+# device entry points (torch tensors in, device pointers out)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KV_BF16
+    if t.dtype == torch.float32:
+        return KV_F32
+    raise KVError(KV_EUNSUPPORTED, f"unsupported element type {t.dtype}")
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise KVError(KV_EINVAL, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise KVError(KV_EINVAL, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise KVError(KV_EINVAL, f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise KVError(KV_EINVAL, f"{name} must have {ndim} dimensions")
+    return t.data_ptr()
+
+
+def empty_pools(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):
+    """Allocate (K_pool, V_pool) device tensors in the library's layout."""
+    torch = _torch()
+    X = 16 // torch.empty((), dtype=dtype).element_size()
+    k = torch.empty((num_blocks, num_kv_heads, head_dim // X, BLOCK_SIZE, X), dtype=dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=dtype, device=device)
+    return k, v
+
+
+def kv_append_scatter(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None) -> None:
+    """Scatter-write k_new/v_new [n, Hkv, D] into the pools at slot_mapping [n] (int32, -1 = skip)."""
+    torch = _torch()
+    _need(k_new, "k_new", ndim=3)
+    _need(v_new, "v_new", dtype=k_new.dtype, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    _need(k_pool, "k_pool", dtype=k_new.dtype, ndim=5)
+    _need(v_pool, "v_pool", dtype=k_new.dtype, ndim=4)
+    n, hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or slot_mapping.shape[0] != n:
+        raise KVError(KV_EINVAL, "k_new, v_new and slot_mapping sizes disagree")
+    nb = k_pool.shape[0]
+    if tuple(v_pool.shape) != (nb, hkv, d, BLOCK_SIZE) or k_pool.shape[1] != hkv or \
+            k_pool.shape[2] * k_pool.shape[4] != d or k_pool.shape[3] != BLOCK_SIZE:
+        raise KVError(KV_EINVAL, "pool shapes do not match k_new")
+    _check(_lib.kv_append_scatter(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), n,
+                                  k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, d, BLOCK_SIZE,
+                                  _dtype_code(k_new), _stream_ptr(stream)))
+
+
+def paged_attention_workspace_size(num_seqs: int, total_q_rows: int, num_q_heads: int, head_dim: int,
+                                   max_context_len: int) -> int:
+    return int(_lib.paged_attention_workspace_size(num_seqs, total_q_rows, num_q_heads, head_dim,
+                                                   max_context_len))
+
+
+def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
+                            max_context_len: int, scale: float, sinks=None, out=None, workspace=None,
+                            stream=None):
+    """out [total_rows, Hq, D] float32 = attention of q over the paged cache (see pagedkv.h)."""
+    torch = _torch()
+    _need(q, "q", ndim=3)
+    _need(k_pool, "k_pool", dtype=q.dtype, ndim=5)
+    _need(v_pool, "v_pool", dtype=q.dtype, ndim=4)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _need(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
+    total, hq, d = q.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    S = context_lens.shape[0]
+    if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise KVError(KV_EINVAL, "context_lens, query_start_loc and block_tables disagree on num_seqs")
+    if sinks is not None:
+        _need(sinks, "sinks", dtype=torch.float32, ndim=1)
+        if sinks.shape[0] != hq:
+            raise KVError(KV_EINVAL, "sinks must hold num_q_heads values")
+    if out is None:
+        out = torch.empty((total, hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (total, hq, d):
+        raise KVError(KV_EINVAL, "out has the wrong shape")
+    need = paged_attention_workspace_size(S, total, hq, d, max_context_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attention_forward(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), _dtype_code(q), block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len,
+        max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
+        _stream_ptr(stream)))
+    return out

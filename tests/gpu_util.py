@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU tests: the oracle side of a workload and small
+custom workloads. Importing this module needs no GPU."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def oracle_side(w, fill_nan=True):
+    """Oracle allocation (same call order as the device staging), oracle
+    scatter into NaN-filled pools, oracle paged attention."""
+    a = oracle.Allocator(w.num_blocks, w.block_size, w.free_order)
+    maxb = w.max_blocks_per_seq
+    res, step = [], []
+    for s, seq in enumerate(w.seqs):
+        res.append(a.alloc(s, seq.tokens[:seq.ctx - seq.n_step], maxb)[3])
+    tables = []
+    for s, seq in enumerate(w.seqs):
+        row, nb, ctx, slots = a.alloc(s, seq.tokens[seq.ctx - seq.n_step:], maxb)
+        tables.append(row)
+        step.append(slots)
+    nan = np.uint16(0x7FC0) if w.dtype == "bf16" else np.float32(np.nan)
+    kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype,
+                                fill=nan if fill_nan else None)
+    for s, seq in enumerate(w.seqs):
+        n_res = seq.ctx - seq.n_step
+        oracle.scatter(kp, vp, seq.k[:n_res], seq.v[:n_res], res[s])
+        oracle.scatter(kp, vp, seq.k[n_res:], seq.v[n_res:], step[s])
+    tables = np.array(tables, dtype=np.int32)
+    out = oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
+                                 w.num_kv_heads, w.scale, w.sinks, w.dtype)
+    return tables, kp, vp, out
+
+
+def oracle_rows(w, rows):
+    """Oracle output for a subset of global query rows, from the dense K/V."""
+    qsl = w.qsl
+    ks, vs, qsel, qls = [], [], [], []
+    for i in rows:
+        s = int(np.searchsorted(qsl, i, side="right") - 1)
+        seq = w.seqs[s]
+        p = seq.ctx - seq.q_len + (i - int(qsl[s]))
+        ks.append(seq.k[:p + 1])
+        vs.append(seq.v[:p + 1])
+        qsel.append(w.q[i])
+    q = np.stack(qsel)
+    return oracle.attention(q, ks, vs, np.arange(len(rows) + 1, dtype=np.int32), w.num_q_heads,
+                            w.num_kv_heads, w.scale, w.sinks, w.dtype)
+
+
+def custom(dtype, Hq, Hkv, D, ctxs, q_lens, seed, sinks=False, shared_prefix=0, n_shared=0, scale=None):
+    return synth.build("custom", dtype, Hq, Hkv, D, ctxs, q_lens, seed, sinks=sinks,
+                       shared_prefix=shared_prefix, n_shared=n_shared, scale=scale)
+
+
+def run_forward(pk, st, w, k_pool=None, v_pool=None):
+    return pk.paged_attention_forward(
+        st.q, st.k_pools[0] if k_pool is None else k_pool, st.v_pools[0] if v_pool is None else v_pool,
+        st.tables, st.context_lens, st.qsl, st.max_q_len, st.max_context_len, w.scale,
+        sinks=st.sinks, out=st.out, workspace=st.workspace)
+
+
+def max_err(got, want):
+    return float(np.max(np.abs(got.astype(np.float64) - want))) if got.size else 0.0

@@ -1,0 +1,131 @@
+"""Bitwise row invariance of the HIP path (GPU).
+
+The speculative-decoding pages demand that a verify-window row uses exactly
+the arithmetic of the serial step, so that a row computed alone and the same
+row inside a window (or a batch) are bitwise identical. "Alone" here is the
+plainest reading: the same query submitted by itself as a decode row
+(q_len = 1) over the keys up to its position, through the same block table.
+"""
+import copy
+import sys
+
+import numpy as np
+import pytest
+
+from gpu_util import custom, run_forward
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    import paged_kv_attention_block_amd as pk
+    return pk
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bits(t):
+    import torch
+    return t.contiguous().view(torch.int32).cpu().numpy()
+
+
+def alone(pk, st, w, i):
+    """Row i as a single decode row over keys 0..p."""
+    import torch
+    qsl = w.qsl
+    s = int(np.searchsorted(qsl, i, side="right") - 1)
+    seq = w.seqs[s]
+    p = seq.ctx - seq.q_len + (i - int(qsl[s]))
+    dev = st.q.device
+    return pk.paged_attention_forward(
+        st.q[i:i + 1].contiguous(), st.k_pools[0], st.v_pools[0], st.tables[s:s + 1].contiguous(),
+        torch.tensor([p + 1], dtype=torch.int32, device=dev), torch.tensor([0, 1], dtype=torch.int32, device=dev),
+        1, p + 1, w.scale, sinks=st.sinks)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("bf16", 64, 8, 64), ("f32", 4, 2, 64),
+                                             ("bf16", 8, 8, 64)])
+def test_window_rows_equal_rows_alone(pk, dtype, Hq, Hkv, D):
+    import torch
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom(dtype, Hq, Hkv, D, [1000, 4100, 6000, 70], [8, 8, 8, 8], seed=90 + D + Hq, sinks=True)
+    announce(f"window invariance {dtype} {Hq}/{Hkv} D{D}")
+    st = stage(w)
+    full = bits(run_forward(pk, st, w))
+    for i in range(w.total_rows):
+        got = bits(alone(pk, st, w, i))
+        np.testing.assert_array_equal(got[0], full[i], err_msg=f"row {i}")
+
+
+def test_prefill_rows_equal_rows_alone(pk):
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom("bf16", 16, 4, 128, [1500, 300], [200, 300], seed=95, sinks=True)
+    announce("prefill invariance")
+    st = stage(w)
+    full = bits(run_forward(pk, st, w))
+    for i in [0, 1, 15, 16, 17, 63, 64, 199, 200, 201, 299, 350, 499]:
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i}")
+
+
+def test_batch_invariance(pk):
+    """A sequence alone and inside a batch of others gives the same bits."""
+    from paged_kv_attention_block_amd.staging import stage
+    ctxs = [800, 3000, 17, 5000, 1024]
+    qls = [1, 8, 1, 1, 4]
+    w = custom("bf16", 32, 8, 128, ctxs, qls, seed=96)
+    announce("batch invariance")
+    full = bits(run_forward(pk, stage(w), w))
+    start = 0
+    for s in range(len(ctxs)):
+        ws = copy.deepcopy(w)
+        ws.seqs = [w.seqs[s]]
+        ws.q = w.q[start:start + qls[s]]
+        one = bits(run_forward(pk, stage(ws), ws))
+        np.testing.assert_array_equal(one, full[start:start + qls[s]], err_msg=f"seq {s}")
+        start += qls[s]
+
+
+def test_block_placement_invariance(pk):
+    """Another physical placement of the same blocks gives the same bits."""
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom("bf16", 64, 8, 64, [900, 2100, 33], [1, 3, 1], seed=97, sinks=True)
+    announce("placement invariance")
+    a = bits(run_forward(pk, stage(w), w))
+    w2 = copy.deepcopy(w)
+    w2.free_order = np.random.default_rng(5).permutation(w.num_blocks).astype(np.int32)
+    b = bits(run_forward(pk, stage(w2), w2))
+    np.testing.assert_array_equal(a, b)
+
+
+def test_shared_prefix_equals_private_copies(pk):
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom("bf16", 32, 8, 128, [700, 650, 901], [1, 1, 3], seed=98, shared_prefix=600, n_shared=3)
+    announce("shared vs private prefix")
+    st = stage(w)
+    assert (st.tables_np[0, :37] == st.tables_np[1, :37]).all()
+    a = bits(run_forward(pk, st, w))
+    w2 = copy.deepcopy(w)
+    rng = np.random.default_rng(6)
+    for seq in w2.seqs:                      # distinct token ids, same K/V bytes: no sharing
+        seq.tokens = rng.integers(0, 1 << 30, size=seq.ctx).astype(np.int32)
+    w2.num_blocks = 3 * w.num_blocks         # private copies need room for every block
+    w2.free_order = rng.permutation(w2.num_blocks).astype(np.int32)
+    st2 = stage(w2)
+    assert not (st2.tables_np[0, :37] == st2.tables_np[1, :37]).any()
+    np.testing.assert_array_equal(a, bits(run_forward(pk, st2, w2)))
+
+
+def test_run_to_run_determinism(pk):
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom("bf16", 32, 8, 128, [4000, 12000, 100, 7000], [8, 1, 16, 3], seed=99, sinks=True)
+    announce("determinism")
+    st = stage(w)
+    a = bits(run_forward(pk, st, w)).copy()
+    for _ in range(3):
+        np.testing.assert_array_equal(bits(run_forward(pk, st, w)), a)
