@@ -1,0 +1,233 @@
+"""Benchmark: paged-attention decode KV GB/s (% of HBM peak) and seq-tokens/s
+on one MI355X.
+
+One step = one decode step through L attention layers: for every layer, the
+step's new K/V rows are scatter-written into that layer's paged pool
+(kv_append_scatter) and one batched paged_attention_forward runs over it.
+Layers are distinct pool copies sharing one set of block tables, so a step
+touches more memory than the 256 MB last-level cache holds and the reported
+bandwidth is HBM bandwidth. Block allocation (kv_pool_alloc) happens once per
+batch on the host and is timed separately.
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+METRIC = "paged-attn decode KV GB/s (% of HBM peak) + seq-tokens/s, 1 GPU"
+MIN_FOOTPRINT = 1 << 30        # bytes of pool touched per step
+
+
+def unique_kv_bytes(w, tables):
+    """K+V bytes of the visible tokens of every distinct physical block, once."""
+    elt = 2 if w.dtype == "bf16" else 4
+    seen = {}
+    for s, seq in enumerate(w.seqs):
+        nb = -(-seq.ctx // 16)
+        for j in range(nb):
+            b = int(tables[s, j])
+            seen[b] = max(seen.get(b, 0), min(16, seq.ctx - 16 * j))
+    tokens = sum(seen.values())
+    return tokens * w.num_kv_heads * w.head_dim * elt * 2
+
+
+def logical_kv_bytes(w):
+    elt = 2 if w.dtype == "bf16" else 4
+    return sum(seq.ctx for seq in w.seqs) * w.num_kv_heads * w.head_dim * elt * 2
+
+
+def cpu_baseline(w, kv_bytes, rows, seconds):
+    """The oracle, as it stands, on the host cores: its own allocation and
+    scatter build the pools once; each timed call is gather + fp64 attention
+    over the whole batch of one layer."""
+    import oracle
+    a = oracle.Allocator(w.num_blocks, w.block_size, w.free_order)
+    kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    tables = []
+    for s, seq in enumerate(w.seqs):
+        row, _, _, slots = a.alloc(s, seq.tokens, w.max_blocks_per_seq)
+        oracle.scatter(kp, vp, seq.k, seq.v, slots)
+        tables.append(row)
+    tables = np.array(tables, dtype=np.int32)
+    threads = oracle.default_threads()
+    times = []
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or len(times) < 2:
+        t1 = time.perf_counter()
+        oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
+                               w.num_kv_heads, w.scale, w.sinks, w.dtype, threads)
+        times.append(time.perf_counter() - t1)
+        if len(times) >= 500:
+            break
+    med = float(np.median(times))
+    return {"value": round(kv_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} calls over one layer's batch ({rows} rows, {kv_bytes / 1e6:.1f} MB of "
+                      f"K/V), median {med * 1e3:.2f} ms per call (gather + fp64 attention); "
+                      f"seq-tokens/s {rows / med:.1f}"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mid_decode")
+    ap.add_argument("--layers", type=int, default=0, help="pool copies per step (0: reach 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import paged_kv_attention_block_amd as pk
+    from paged_kv_attention_block_amd.staging import stage
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.by_name(args.workload)
+    elt = 2 if w.dtype == "bf16" else 4
+
+    # host block allocation for the batch, timed on its own
+    t0 = time.perf_counter()
+    pool = pk.kv_pool_create(w.num_blocks, 16, w.free_order)
+    for s, seq in enumerate(w.seqs):
+        pk.kv_pool_alloc(pool, s, seq.tokens, w.max_blocks_per_seq)
+    alloc_us = (time.perf_counter() - t0) * 1e6
+    del pool
+
+    pool_bytes = w.num_blocks * w.num_kv_heads * w.head_dim * 16 * elt * 2
+    layers = args.layers or max(1, math.ceil(MIN_FOOTPRINT / pool_bytes))
+    st = stage(w, device=dev, copies=layers, poison=False)
+    kv_bytes = unique_kv_bytes(w, st.tables_np)
+    rows = w.total_rows
+    q_bytes = rows * w.num_q_heads * w.head_dim * elt
+    out_bytes = rows * w.num_q_heads * w.head_dim * 4
+    n_step_tok = int(st.step_slots_np.size)
+    scatter_bytes = n_step_tok * w.num_kv_heads * w.head_dim * elt * 2 * 2
+    stream = torch.cuda.current_stream()
+
+    def layer_call(l):
+        pk.kv_append_scatter(st.k_step, st.v_step, st.step_slots, st.k_pools[l], st.v_pools[l])
+        pk.paged_attention_forward(st.q, st.k_pools[l], st.v_pools[l], st.tables, st.context_lens, st.qsl,
+                                   st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
+                                   workspace=st.workspace)
+
+    def step():
+        for l in range(layers):
+            layer_call(l)
+
+    def attention_only():
+        for l in range(layers):
+            pk.paged_attention_forward(st.q, st.k_pools[l], st.v_pools[l], st.tables, st.context_lens, st.qsl,
+                                       st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
+                                       workspace=st.workspace)
+
+    # Both loops are captured once into HIP graphs and replayed, as a serving
+    # loop replays its decode step: host launch cost stays out of the timing.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(max(1, args.warmup)):
+            step()
+            attention_only()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g_step = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_step):
+        step()
+    g_att = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_att):
+        attention_only()
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        g_step.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # attention launches alone, back to back: average duration per call
+    e0.record(stream)
+    for _ in range(args.steps):
+        g_att.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    att_ms = e0.elapsed_time(e1) / (args.steps * layers)
+
+    # the same step launched eagerly (host launch cost included), for reference
+    e0.record(stream)
+    step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+
+    value = kv_bytes * layers / (ms_per_step * 1e-3) / 1e9
+    att_alg_bytes = kv_bytes + q_bytes + out_bytes
+    achieved = att_alg_bytes / (att_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, kv_bytes, rows, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/Q, seeded block placement)",
+        "config": {
+            "workload": w.name, "seqs": len(w.seqs), "context_lens": [int(s.ctx) for s in w.seqs],
+            "rows_per_layer": rows, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "block_size": 16, "layers_per_step": layers,
+            "kv_bytes_per_layer": kv_bytes, "logical_kv_bytes_per_layer": logical_kv_bytes(w),
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "seq_tokens_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "attention_call_us": round(att_ms * 1e3, 3),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "layer_us": round(ms_per_step * 1e3 / layers, 3),
+        "host_alloc_us_per_batch": round(alloc_us, 1),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "paged_attention_forward (split + fold launches)",
+            "alg_bytes_per_launch": att_alg_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

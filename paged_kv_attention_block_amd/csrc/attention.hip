@@ -433,20 +433,47 @@ __global__ __launch_bounds__(64) void attn_reduce(AttnParams P) {
     const int p = ctx - q_len + (i - P.qsl[s]);
     const int ns = min(num_splits(p + 1), P.max_splits);
     const size_t base = ((size_t)i * P.Hq + h) * P.max_splits;
+    // split maxima and sums, one split per lane (64 at a time), loaded together
     float M = -INFINITY;
-    for (int j = 0; j < ns; ++j) M = fmaxf(M, P.ws_ml[base + j].x);
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+        const float mj = j0 + lane < ns ? P.ws_ml[base + j0 + lane].x : -INFINITY;
+        M = fmaxf(M, mj);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     const float sk = P.sinks ? P.sinks[h] * kLog2e : -INFINITY;
     M = fmaxf(M, sk);
     float L = 0.f;
     float a[DU];
 #pragma unroll
     for (int u = 0; u < DU; ++u) a[u] = 0.f;
-    for (int j = 0; j < ns; ++j) {
-        const float2 ml = P.ws_ml[base + j];
-        const float w = fast_exp2(ml.x - M);
-        L = fmaf(ml.y, w, L);
+    for (int j0 = 0; j0 < ns; j0 += 64) {
+        const float2 mlj = j0 + lane < ns ? P.ws_ml[base + j0 + lane] : make_float2(-INFINITY, 0.f);
+        const float wj = fast_exp2(mlj.x - M);
+        const int nj = min(64, ns - j0);
+        int j = 0;
+        for (; j + 4 <= nj; j += 4) {
+            float x[4][DU];
 #pragma unroll
-        for (int u = 0; u < DU; ++u) a[u] = fmaf(w, P.ws_acc[(base + j) * D + lane + 64 * u], a[u]);
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int u = 0; u < DU; ++u) x[t][u] = P.ws_acc[(base + j0 + j + t) * D + lane + 64 * u];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j + t));
+                const float lj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlj.y), j + t));
+                L = fmaf(lj, w, L);
+#pragma unroll
+                for (int u = 0; u < DU; ++u) a[u] = fmaf(w, x[t][u], a[u]);
+            }
+        }
+        for (; j < nj; ++j) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+            const float lj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlj.y), j));
+            L = fmaf(lj, w, L);
+#pragma unroll
+            for (int u = 0; u < DU; ++u) a[u] = fmaf(w, P.ws_acc[(base + j0 + j) * D + lane + 64 * u], a[u]);
+        }
     }
     if (P.sinks) L += fast_exp2(sk - M);
 #pragma unroll
