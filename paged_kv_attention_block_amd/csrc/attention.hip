@@ -6,24 +6,28 @@
 // with a variant taking per-head sink logits; its "批量前向" paragraph pairs the
 // batched forward with a paged K/V scatter-write. Decode rows, chunked-prefill
 // rows (section "性能优化", chunked prefill) and speculative-verify windows
-// (section "MTP / NextN 推测解码") share one entry point. The speculative-
-// decoding pages (the TensorFold sections on the exactness rule and on
-// row-invariant wide-window kernels) require that a row computed alone and
-// the same row inside a window give identical bits; every design choice below
-// that fixes an order of floating-point operations exists for that.
+// (section "MTP / NextN 推测解码") share one entry point. The TensorFold pages
+// (sections on the exactness rule and on row-invariant wide-window kernels)
+// require that a row computed alone and the same row inside a window give
+// identical bits; every choice below that fixes an order of floating-point
+// operations exists for that.
 //
-// Arithmetic of one (query row, query head), identical for every row whatever
-// the batch, window or q_len around it:
-//  * keys are cut into splits by a fixed function of absolute key position
-//    (split_begin); one wave owns one split of one (sequence, KV head, rows);
-//  * inside a split, keys are consumed in 32-key chunks (two 16-token blocks)
-//    in ascending order with an online softmax in base 2;
-//  * bf16: S^T = K * Q^T and O^T = V^T * P^T on 16x16x32 bf16 MFMA tiles whose
-//    results were measured to be independent of the row's position in the
-//    tile; P enters the PV product as a hi + lo pair of bf16 values;
-//  * fp32: plain fp32 FMA chains, one wave per (row, head);
-//  * a separate pass folds the splits of each (row, head) left to right, adds
-//    the sink term and divides once.
+// Arithmetic of one (query row, query head), the same whatever batch, window,
+// q_len or launch shape surrounds the row:
+//  * absolute key positions are cut into splits (split_begin) and every split
+//    into four quarters; a quarter's keys are consumed in 32-key chunks (two
+//    16-token blocks) in ascending order by an online softmax in base 2;
+//  * bf16: S^T = K Q^T and O^T = V^T P^T on 16x16x32 bf16 MFMA tiles, whose
+//    per-element results do not depend on the row's position in the tile; P
+//    enters the PV product as a hi + lo pair of bf16 values;
+//  * the four quarter states fold left to right into a split state, the split
+//    states fold left to right into the row state (fold_state), and the sink
+//    and the one division come last (finalize);
+//  * fp32: one wave per (row, head), one online state over all keys in order.
+// Two bf16 launch shapes compute exactly that: "parallel" (one workgroup per
+// split, a wave per quarter, the last workgroup of a sequence folds the
+// splits) for decode and verify rows, and "sequential" (one workgroup per 64
+// rows walking every split, folds kept in registers) for prefill chunks.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -43,24 +47,21 @@ constexpr int kBlock = 16;
 constexpr int kChunk = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxHeadDim = 128;
+constexpr int kParRows = 32;   // rows per (sequence, KV head) the parallel shape takes
+constexpr int kSeqRows = 64;   // rows per workgroup in the sequential shape
 
 // ---------------------------------------------------------------------------
-// Fixed split partition of absolute key positions:
-//   [0, 1024)    64-key splits   (indices 0..15)
-//   [1024, 4096) 256-key splits  (indices 16..27)
-//   [4096, ...)  512-key splits  (indices 28..)
-// Small splits near the start give short contexts enough waves; long splits
-// further out keep the partial results small next to the K/V they summarise.
+// Fixed partition of absolute key positions: 256-key splits below 2048,
+// 1024-key splits from there on; each split has four equal quarters.
 // ---------------------------------------------------------------------------
+constexpr int kEdge = 2048, kSplitA = 256, kSplitB = 1024;
+constexpr int kSplitsA = kEdge / kSplitA;
+
 __host__ __device__ inline int split_index(int pos) {
-    if (pos < 1024) return pos >> 6;
-    if (pos < 4096) return 16 + ((pos - 1024) >> 8);
-    return 28 + ((pos - 4096) >> 9);
+    return pos < kEdge ? pos / kSplitA : kSplitsA + (pos - kEdge) / kSplitB;
 }
 __host__ __device__ inline int split_begin(int idx) {
-    if (idx < 16) return idx << 6;
-    if (idx < 28) return 1024 + ((idx - 16) << 8);
-    return 4096 + ((idx - 28) << 9);
+    return idx < kSplitsA ? idx * kSplitA : kEdge + (idx - kSplitsA) * kSplitB;
 }
 __host__ __device__ inline int num_splits(int len) { return len <= 0 ? 0 : split_index(len - 1) + 1; }
 
@@ -72,10 +73,12 @@ struct AttnParams {
     const int32_t *ctx_lens;
     const int32_t *qsl;
     const float *sinks;
-    float2 *ws_ml;   // [rows][Hq][max_splits] (running max in log2 units, sum)
-    float *ws_acc;   // [rows][Hq][max_splits][D]
-    float *out;      // [rows][Hq][D]
+    int32_t *counters;  // [num_seqs][Hkv], zero between calls
+    float2 *ws_ml;      // [rows][Hq][max_splits]: split max (log2 units), split sum
+    float *ws_acc;      // [rows][Hq][max_splits][D]
+    float *out;         // [rows][Hq][D]
     int32_t num_seqs, total_rows, Hq, Hkv, G, max_blocks_per_seq, num_blocks, max_splits;
+    int32_t decode_only;  // every sequence has q_len == 1 (rows packed in sequence order)
     float scale_log2;
 };
 
@@ -83,26 +86,134 @@ struct AttnParams {
 __device__ __attribute__((aligned(16))) uint16_t g_zero_tile[kBlock * kMaxHeadDim];
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ inline int seq_of_row(const int32_t *qsl, int num_seqs, int row) {
-    int lo = 0, hi = num_seqs;  // qsl[lo] <= row < qsl[hi]
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (qsl[mid] <= row) lo = mid; else hi = mid;
-    }
-    return lo;
+__device__ inline float bcast(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
 // ---------------------------------------------------------------------------
-// bf16 split kernel. One wave: (sequence s, KV head, rows row0..row0+16*NT-1
-// of the s-th [q_len * G] row space ordered as r * G + head_in_group, one split).
-// Lane l = 16 g + n: n is the MFMA column (query row of the tile), g the
-// k-slot group.
+// Online-softmax state of one 16-row MFMA tile held by one wave. Lane 16g+n
+// holds row n: its max m (log2 units), its sum l, and O^T[d][n] for
+// d = 16 dt + 4 g + i in acc[dt][i].
+// ---------------------------------------------------------------------------
+template <int DT>
+struct TileState {
+    float m, l;
+    f32x4_t acc[DT];
+};
+
+template <int DT>
+__device__ inline void state_clear(TileState<DT> &s) {
+    s.m = -INFINITY;
+    s.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) s.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// a := a (+) b, the online-softmax merge of two states over disjoint keys.
+// An empty state (m = -inf) is the identity, exactly.
+template <int DT>
+__device__ inline void fold_state(TileState<DT> &a, const TileState<DT> &b) {
+    if (b.m == -INFINITY) return;
+    if (a.m == -INFINITY) {
+        a = b;
+        return;
+    }
+    const float M = fmaxf(a.m, b.m);
+    const float al = fast_exp2(a.m - M);
+    const float be = fast_exp2(b.m - M);
+    a.l = fmaf(a.l, al, b.l * be);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.acc[dt][i] = fmaf(a.acc[dt][i], al, b.acc[dt][i] * be);
+    a.m = M;
+}
+
+// out = acc / (l + sink term); the sink logit (log2 units, -inf if none)
+// takes part in the max.
+template <int DT>
+__device__ inline void finalize(const TileState<DT> &s, float sink2, f32x4_t *o) {
+    float l = s.l;
+    float al = 1.f;
+    if (sink2 != -INFINITY) {
+        const float M = fmaxf(s.m, sink2);
+        al = fast_exp2(s.m - M);
+        l = fmaf(l, al, fast_exp2(sink2 - M));
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[dt][i] = (s.acc[dt][i] * al) / l;
+}
+
+// ---------------------------------------------------------------------------
+// One 32-key chunk for one tile: kop[tau][j] is the K operand of block tau and
+// k-step j (lane 16g+n holds token n, channels 32j+8g..+7), vop[dt] the V^T
+// operand (channels 16dt+n, tokens 4g..4g+3 of block 0 then of block 1),
+// qop[j] the Q operand (row n, channels 32j+8g..+7). Key kc+16tau+4g+i is
+// visible to the lane's row when it is <= prow.
 // ---------------------------------------------------------------------------
 template <int D>
+__device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[2][D / 32],
+                                    const u32x4_t (&vop)[D / 16], const u32x4_t (&qop)[D / 32], int kc, int prow,
+                                    int g, float scale_log2) {
+    constexpr int KJ = D / 32, DT = D / 16;
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, qop[j]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[0][j]), b, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[1][j]), b, s1, 0, 0, 0);
+    }
+    float sc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int key = kc + 4 * g + i;
+        sc[i] = key <= prow ? s0[i] * scale_log2 : -INFINITY;
+        sc[4 + i] = key + 16 <= prow ? s1[i] * scale_log2 : -INFINITY;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool has = kc <= prow;  // the row sees at least one key of the chunk
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    float pv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
+    float rs = pv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) rs += pv[e];
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    bf16x8_t phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const __bf16 h = (__bf16)pv[e];
+        phi[e] = h;
+        plo[e] = (__bf16)(pv[e] - (float)h);
+    }
+    const float l_new = fmaf(alpha, st.l, rs);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vop[dt]);
+        f32x4_t a = st.acc[dt] * alpha;
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a, 0, 0, 0);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a, 0, 0, 0);
+        st.acc[dt] = has ? a : st.acc[dt];
+    }
+    st.l = has ? l_new : st.l;
+    st.m = has ? m_new : st.m;
+}
+
+// K/V operands of one chunk in registers, read from global memory or LDS.
+template <int D>
 struct ChunkRegs {
-    u32x4_t k[2][D / 32];   // A operand of S^T = K Q^T, per block tau and k-step j
-    u32x2_t v[2][D / 16];   // half of the A operand of O^T = V^T P^T, per block and d-tile
+    u32x4_t k[2][D / 32];
+    u32x2_t v[2][D / 16];
 };
 
 template <int D>
@@ -120,217 +231,422 @@ __device__ inline void load_chunk(ChunkRegs<D> &c, const uint16_t *kb0, const ui
     }
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(64) void attn_bf16_split(AttnParams P, int one_item_per_seq) {
-    constexpr int R = 16 * NT;
-    constexpr int KJ = D / 32;
-    constexpr int DT = D / 16;
-    const int lane = threadIdx.x;
-    const int g = lane >> 4, n = lane & 15;
-    const int item = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
-
-    int s = 0, rb = 0;
-    if (one_item_per_seq) {
-        s = item;
-        if (s >= P.num_seqs) return;
-    } else {
-        int acc = 0;
-        bool found = false;
-        for (int t = 0; t < P.num_seqs; ++t) {
-            const int nb = ((P.qsl[t + 1] - P.qsl[t]) * P.G + R - 1) / R;
-            if (item < acc + nb) { s = t; rb = item - acc; found = true; break; }
-            acc += nb;
+// Zero V of keys at or past ctx, so that a zero weight never meets a NaN.
+template <int D>
+__device__ inline void mask_tail(ChunkRegs<D> &c, int kc, int ctx, int g) {
+    if (kc + kChunk <= ctx) return;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        const int k0 = kc + 16 * tau + 4 * g;
+        const uint32_t m0 = (k0 < ctx ? 0x0000FFFFu : 0u) | (k0 + 1 < ctx ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (k0 + 2 < ctx ? 0x0000FFFFu : 0u) | (k0 + 3 < ctx ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            c.v[tau][dt].x &= m0;
+            c.v[tau][dt].y &= m1;
         }
-        if (!found) return;
     }
-    const int q0 = P.qsl[s];
-    const int q_len = P.qsl[s + 1] - q0;
+}
+
+template <int D>
+__device__ inline void vop_of(const ChunkRegs<D> &c, u32x4_t (&vop)[D / 16]) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) vop[dt] = u32x4_t{c.v[0][dt].x, c.v[0][dt].y, c.v[1][dt].x, c.v[1][dt].y};
+}
+
+// Rows rho = row0 + 16 t + n of a sequence's [q_len * G] row space, ordered
+// r * G + head-in-group.
+struct RowInfo {
+    int prow;   // last visible key, -1 for padding rows
+    int r, hl;  // query row within the sequence, head within the group
+};
+
+__device__ inline RowInfo row_info(int rho, int rows_total, int G, int ctx, int q_len) {
+    RowInfo ri;
+    const bool valid = rho < rows_total;
+    ri.r = valid ? rho / G : 0;
+    ri.hl = valid ? rho - ri.r * G : 0;
+    ri.prow = valid ? ctx - q_len + ri.r : -1;
+    return ri;
+}
+
+template <int D>
+__device__ inline void load_q(u32x4_t (&qop)[D / 32], const AttnParams &P, int q0, const RowInfo &ri, int kvh, int g) {
+    const uint16_t *qrow =
+        reinterpret_cast<const uint16_t *>(P.q) + ((size_t)(q0 + ri.r) * P.Hq + kvh * P.G + ri.hl) * D;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+        qop[j] = ri.prow >= 0 ? *reinterpret_cast<const u32x4_t *>(qrow + 32 * j + 8 * g) : u32x4_t{0, 0, 0, 0};
+}
+
+__device__ inline float sink_log2(const AttnParams &P, int kvh, int hl) {
+    return P.sinks ? P.sinks[kvh * P.G + hl] * kLog2e : -INFINITY;
+}
+
+template <int DT>
+__device__ inline void store_out(const AttnParams &P, int q0, const RowInfo &ri, int kvh, int g, const f32x4_t *o) {
+    if (ri.prow < 0) return;
+    float *dst = P.out + ((size_t)(q0 + ri.r) * P.Hq + kvh * P.G + ri.hl) * (16 * DT) + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t *>(dst + 16 * dt) = o[dt];
+}
+
+// ---------------------------------------------------------------------------
+// Parallel shape: grid (sequence, KV head, split); 4 waves, wave w takes
+// quarter w of the split for all NT tiles (up to 16 NT rows per sequence and
+// KV head). Quarter states meet in LDS; a sequence with one split finishes
+// here, otherwise the split state goes to the workspace and the last
+// workgroup of the (sequence, KV head) folds all splits.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(256) void attn_parallel(AttnParams P) {
+    constexpr int DT = D / 16, KJ = D / 32;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int s = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
+
+    int q0, q_len;
+    if (P.decode_only) {
+        q0 = s;
+        q_len = 1;
+    } else {
+        q0 = P.qsl[s];
+        q_len = P.qsl[s + 1] - q0;
+    }
     const int ctx = P.ctx_lens[s];
-    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows) return;
     const int rows_total = q_len * P.G;
-    const int row0 = rb * R;
-    if (row0 >= rows_total) return;
-    const int row_last = min(row0 + R, rows_total) - 1;
-    const int p_max = ctx - q_len + row_last / P.G;
+    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT) return;
+    const int p_max = ctx - q_len + (rows_total - 1) / P.G;
     const int ks = split_begin(split);
     if (ks > p_max) return;
-    const int ke = min(split_begin(split + 1), p_max + 1);
+    const int qlen4 = (split_begin(split + 1) - ks) >> 2;
+    const int kq0 = ks + wave * qlen4;
+    const int kq1 = min(kq0 + qlen4, p_max + 1);
 
-    // Rows of this lane (column n of every tile) and the Q operand.
-    int prow[NT];
+    RowInfo ri[NT];
     u32x4_t qop[NT][KJ];
+    TileState<DT> st[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int rho = row0 + t * 16 + n;
-        const int r = rho / P.G;
-        const bool valid = rho < rows_total && q0 + r < P.total_rows;
-        const int rr = valid ? r : 0;                    // keep the address in bounds
-        const int hl = valid ? rho - r * P.G : 0;
-        prow[t] = valid ? ctx - q_len + r : -1;
-        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(P.q) +
-                               ((size_t)(q0 + rr) * P.Hq + kvh * P.G + hl) * D;
-#pragma unroll
-        for (int j = 0; j < KJ; ++j)
-            qop[t][j] = valid ? *reinterpret_cast<const u32x4_t *>(qrow + 32 * j + 8 * g)
-                              : u32x4_t{0, 0, 0, 0};
+        ri[t] = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
+        load_q<D>(qop[t], P, q0, ri[t], kvh, g);
+        state_clear(st[t]);
     }
 
-    // Physical block ids of the split, one per lane.
-    const int jb0 = ks / kBlock;
-    const int nblk_seq = (ctx + kBlock - 1) / kBlock;
-    const int nb_split = (ke - ks + kBlock - 1) / kBlock;
-    int bid = -1;
-    if (lane < nb_split) {
-        const int jb = jb0 + lane;
-        if (jb < nblk_seq && jb < P.max_blocks_per_seq) {
-            const int b = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
-            bid = (b >= 0 && b < P.num_blocks) ? b : -1;
-        }
-    }
-    const size_t tile = (size_t)kBlock * D;
-    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
-    const size_t bstride = (size_t)P.Hkv * tile;
-    auto kptr = [&](int b) { return b >= 0 ? kbase + (size_t)b * bstride : g_zero_tile; };
-    auto vptr = [&](int b) { return b >= 0 ? vbase + (size_t)b * bstride : g_zero_tile; };
-
-    float m[NT], l[NT];
-    f32x4_t acc[NT][DT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        m[t] = -INFINITY;
-        l[t] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    auto compute = [&](ChunkRegs<D> &c, int kc) {
-        if (kc + kChunk > ctx) {
-            // keys at or past ctx: zero V so that weight 0 never meets a NaN
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau) {
-                const int k0 = kc + 16 * tau + 4 * g;
-                const uint32_t m0 = (k0 < ctx ? 0x0000FFFFu : 0u) | (k0 + 1 < ctx ? 0xFFFF0000u : 0u);
-                const uint32_t m1 = (k0 + 2 < ctx ? 0x0000FFFFu : 0u) | (k0 + 3 < ctx ? 0xFFFF0000u : 0u);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    c.v[tau][dt].x &= m0;
-                    c.v[tau][dt].y &= m1;
-                }
+    if (kq0 < kq1) {
+        // physical block ids of the quarter, one per lane
+        const int jb0 = kq0 / kBlock;
+        const int nb_q = (kq1 - kq0 + kBlock - 1) / kBlock;
+        const int nblk_seq = (ctx + kBlock - 1) / kBlock;
+        int bid = -1;
+        if (lane < nb_q) {
+            const int jb = jb0 + lane;
+            if (jb < nblk_seq && jb < P.max_blocks_per_seq) {
+                const int b = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
+                bid = (b >= 0 && b < P.num_blocks) ? b : -1;
             }
         }
+        const size_t tile = (size_t)kBlock * D;
+        const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
+        const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
+        const size_t bstride = (size_t)P.Hkv * tile;
+        auto kptr = [&](int b) { return b >= 0 ? kbase + (size_t)b * bstride : g_zero_tile; };
+        auto vptr = [&](int b) { return b >= 0 ? vbase + (size_t)b * bstride : g_zero_tile; };
+        auto fetch = [&](ChunkRegs<D> &c, int kc) {
+            const int ci = (kc - kq0) / kBlock;
+            const int b0 = __builtin_amdgcn_readlane(bid, ci);
+            const int b1 = __builtin_amdgcn_readlane(bid, ci + 1);
+            load_chunk<D>(c, kptr(b0), vptr(b0), kptr(b1), vptr(b1), g, n);
+        };
+        auto compute = [&](ChunkRegs<D> &c, int kc) {
+            mask_tail<D>(c, kc, ctx, g);
+            u32x4_t vop[DT];
+            vop_of<D>(c, vop);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (16 * t < rows_total) chunk_update<D>(st[t], c.k, vop, qop[t], kc, ri[t].prow, g, P.scale_log2);
+        };
+        ChunkRegs<D> ca, cb;
+        fetch(ca, kq0);
+        for (int kc = kq0; kc < kq1; kc += 2 * kChunk) {
+            const bool more = kc + kChunk < kq1;
+            if (more) fetch(cb, kc + kChunk);
+            compute(ca, kc);
+            if (!more) break;
+            if (kc + 2 * kChunk < kq1) fetch(ca, kc + 2 * kChunk);
+            compute(cb, kc + kChunk);
+        }
+    }
+
+    // quarter states -> split state (left fold in quarter order), in wave 0
+    __shared__ f32x4_t lds_acc[3][NT][DT][64];
+    __shared__ float2 lds_ml[3][NT][64];
+    __shared__ int lds_last;
+    if (wave > 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (row0 + t * 16 >= rows_total) continue;
-            f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            lds_ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
 #pragma unroll
-            for (int j = 0; j < KJ; ++j) {
-                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, qop[t][j]);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, c.k[0][j]), b, s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, c.k[1][j]), b, s1, 0, 0, 0);
-            }
-            float sc[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kc + 4 * g + i;
-                sc[i] = key <= prow[t] ? s0[i] * P.scale_log2 : -INFINITY;
-                sc[4 + i] = key + 16 <= prow[t] ? s1[i] * P.scale_log2 : -INFINITY;
-            }
-            float mx = sc[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m[t], mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m[t] - m_use);
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
-            float rs = pv[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) rs += pv[e];
-            rs += __shfl_xor(rs, 16, 64);
-            rs += __shfl_xor(rs, 32, 64);
-            l[t] = alpha * l[t] + rs;
-            m[t] = m_new;
-            bf16x8_t phi, plo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 h = (__bf16)pv[e];
-                phi[e] = h;
-                plo[e] = (__bf16)(pv[e] - (float)h);
-            }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x4_t va4 = {c.v[0][dt].x, c.v[0][dt].y, c.v[1][dt].x, c.v[1][dt].y};
-                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, va4);
-                f32x4_t a = acc[t][dt] * alpha;
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a, 0, 0, 0);
-                acc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a, 0, 0, 0);
-            }
+            for (int dt = 0; dt < DT; ++dt) lds_acc[wave - 1][t][dt][lane] = st[t].acc[dt];
         }
-    };
-
-    // Two register sets: the next chunk's loads are in flight while the
-    // current chunk is computed.
-    ChunkRegs<D> ca, cb;
-    {
-        const int b0 = __builtin_amdgcn_readlane(bid, 0);
-        const int b1 = __builtin_amdgcn_readlane(bid, 1);
-        load_chunk<D>(ca, kptr(b0), vptr(b0), kptr(b1), vptr(b1), g, n);
     }
-    for (int kc = ks; kc < ke; kc += 2 * kChunk) {
-        const bool has_b = kc + kChunk < ke;
-        if (has_b) {
-            const int ci = (kc + kChunk - ks) / kBlock;
-            const int b0 = __builtin_amdgcn_readlane(bid, ci);
-            const int b1 = __builtin_amdgcn_readlane(bid, ci + 1);
-            load_chunk<D>(cb, kptr(b0), vptr(b0), kptr(b1), vptr(b1), g, n);
+    __syncthreads();
+    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
+    if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                TileState<DT> o;
+                const float2 ml = lds_ml[w][t][lane];
+                o.m = ml.x;
+                o.l = ml.y;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds_acc[w][t][dt][lane];
+                fold_state(st[t], o);
+            }
+        if (ns_item == 1) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                f32x4_t o[DT];
+                finalize(st[t], sink_log2(P, kvh, ri[t].hl), o);
+                store_out<DT>(P, q0, ri[t], kvh, g, o);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (ri[t].prow < 0) continue;
+                const size_t base =
+                    ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + split;
+                if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
+            }
         }
-        compute(ca, kc);
-        if (!has_b) break;
-        if (kc + 2 * kChunk < ke) {
-            const int ci = (kc + 2 * kChunk - ks) / kBlock;
-            const int b0 = __builtin_amdgcn_readlane(bid, ci);
-            const int b1 = __builtin_amdgcn_readlane(bid, ci + 1);
-            load_chunk<D>(ca, kptr(b0), vptr(b0), kptr(b1), vptr(b1), g, n);
-        }
-        compute(cb, kc + kChunk);
     }
+    if (ns_item == 1) return;
 
-    // Partial results of this split for rows that see at least one of its keys.
+    // arrival count of this (sequence, KV head); the last workgroup folds
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const int old = atomicAdd(&P.counters[(size_t)s * P.Hkv + kvh], 1);
+        lds_last = old == ns_item - 1;
+    }
+    __syncthreads();
+    if (!lds_last) return;
+    __threadfence();
+    if (tid == 0) atomicExch(&P.counters[(size_t)s * P.Hkv + kvh], 0);
+
+    // split states -> row state, left fold in split order; wave w owns the
+    // d-tiles w, w + 4, ... (the fold is elementwise in d)
+    constexpr int DW = DT / 4;
+    static_assert(DT % 4 == 0, "head_dim must be a multiple of 64");
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        if (prow[t] < ks) continue;
-        const int rho = row0 + t * 16 + n;
-        const int r = rho / P.G;
-        const int hl = rho - r * P.G;
-        const size_t base = ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * P.max_splits + split;
-        if (g == 0) P.ws_ml[base] = make_float2(m[t], l[t]);
+        if (16 * t >= rows_total) continue;
+        const RowInfo &r = ri[t];
+        const size_t base0 = ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * P.max_splits;
+        TileState<DW> acc;
+        state_clear(acc);
+        auto read = [&](TileState<DW> &x, int j) {
+            const float2 ml = P.ws_ml[base0 + j];
+            x.m = ml.x;
+            x.l = ml.y;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = acc[t][dt];
+            for (int e = 0; e < DW; ++e)
+                x.acc[e] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j) * D + 16 * (wave + 4 * e) + 4 * g);
+        };
+        int j = 0;
+        for (; j + 4 <= ns_item; j += 4) {
+            TileState<DW> x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) read(x[u], j + u);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) fold_state(acc, x[u]);
+        }
+        for (; j < ns_item; ++j) {
+            TileState<DW> x;
+            read(x, j);
+            fold_state(acc, x);
+        }
+        if (r.prow < 0) continue;
+        f32x4_t o[DW];
+        finalize(acc, sink_log2(P, kvh, r.hl), o);
+        float *dst = P.out + ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * D + 4 * g;
+#pragma unroll
+        for (int e = 0; e < DW; ++e) *reinterpret_cast<f32x4_t *>(dst + 16 * (wave + 4 * e)) = o[e];
     }
 }
 
 // ---------------------------------------------------------------------------
-// fp32 split kernel: one wave per (row, query head, split); lane t takes key
-// kc + t of each 64-key chunk for the scores and channel d = lane (+64) for
-// the value sum.
+// Sequential shape: one workgroup per 64 rows (4 tiles, wave w owns tile w)
+// of a sequence with more than kParRows rows per KV head. The workgroup walks
+// every chunk up to its last row's position; all 256 threads stage each
+// chunk's K/V in LDS, and each wave folds quarters and splits in registers.
 // ---------------------------------------------------------------------------
+__device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item, int lane, int &s_out, int &rb_out) {
+    int base = 0;
+    for (int t0 = 0; t0 < S; t0 += 64) {
+        const int t = t0 + lane;
+        int nb = 0;
+        if (t < S) {
+            const int rows = (qsl[t + 1] - qsl[t]) * G;
+            nb = rows > kParRows ? (rows + kSeqRows - 1) / kSeqRows : 0;
+        }
+        int incl = nb;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += v;
+        }
+        const int excl = incl - nb;
+        const bool hit = t < S && item >= base + excl && item < base + incl;
+        const unsigned long long mask = __ballot(hit);
+        if (mask) {
+            const int l = __ffsll((long long)mask) - 1;
+            s_out = t0 + l;
+            rb_out = item - base - __shfl(excl, l, 64);
+            return true;
+        }
+        base += __shfl(incl, 63, 64);
+    }
+    return false;
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void attn_f32_split(AttnParams P) {
+__global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
+    constexpr int DT = D / 16, KJ = D / 32;
+    constexpr int TILE = kBlock * D;          // elements of one (block, head) tile
+    constexpr int CHUNK = 4 * TILE;           // K0, V0, K1, V1
+    constexpr int PER_THREAD = CHUNK / 256;   // elements staged by each thread
+    constexpr int NV = PER_THREAD / 8;        // 16-byte pieces per thread
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 4, n = lane & 15;
+    const int kvh = blockIdx.y;
+
+    int s = 0, rb = 0;
+    if (!find_seq_item(P.qsl, P.num_seqs, P.G, blockIdx.x, lane, s, rb)) return;
+    const int q0 = P.qsl[s];
+    const int q_len = P.qsl[s + 1] - q0;
+    const int ctx = P.ctx_lens[s];
+    const int rows_total = q_len * P.G;
+    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows) return;
+    const int row0 = rb * kSeqRows;
+    const int row_last = min(row0 + kSeqRows, rows_total) - 1;
+    const int p_max = ctx - q_len + row_last / P.G;
+    if (p_max < 0) return;
+
+    const RowInfo ri = row_info(row0 + 16 * wave + n, rows_total, P.G, ctx, q_len);
+    u32x4_t qop[KJ];
+    load_q<D>(qop, P, q0, ri, kvh, g);
+    // last key any row of this wave's tile sees (wave-uniform, -1 if no rows)
+    const int wave_row0 = row0 + 16 * wave;
+    const int wave_pmax =
+        wave_row0 < rows_total ? ctx - q_len + min(wave_row0 + 15, rows_total - 1) / P.G : -1;
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][CHUNK];
+    const size_t bstride = (size_t)P.Hkv * TILE;
+    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * TILE;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * TILE;
+    const int nblk_seq = (ctx + kBlock - 1) / kBlock;
+    // this thread stages piece [part * TILE + off, + PER_THREAD) of every
+    // chunk; part = wave: 0 = K of block 0, 1 = V of block 0, 2 = K1, 3 = V1
+    const int part = wave;
+    const int off = lane * PER_THREAD;
+    const int tau = part >> 1;
+    const bool is_v = part & 1;
+
+    // block ids, 64 at a time, one per lane
+    int bid_base = -64, bid = -1;
+    auto block_id = [&](int jb) {
+        if (jb - bid_base >= 64) {
+            bid_base = jb & ~63;
+            const int x = bid_base + lane;
+            int b = -1;
+            if (x < nblk_seq && x < P.max_blocks_per_seq) {
+                const int y = P.bt[(size_t)s * P.max_blocks_per_seq + x];
+                b = (y >= 0 && y < P.num_blocks) ? y : -1;
+            }
+            bid = b;
+        }
+        return __builtin_amdgcn_readlane(bid, jb - bid_base);
+    };
+    u32x4_t pre[NV];
+    auto fetch = [&](int kc) {
+        const int b = block_id(kc / kBlock + tau);
+        const uint16_t *src = b >= 0 ? (is_v ? vbase : kbase) + (size_t)b * bstride + off : g_zero_tile + off;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) pre[v] = *reinterpret_cast<const u32x4_t *>(src + 8 * v);
+    };
+
+    TileState<DT> fin, spl, qtr;
+    state_clear(fin);
+    state_clear(spl);
+    state_clear(qtr);
+    const int nchunks = (p_max + kChunk) / kChunk;
+    fetch(0);
+    for (int c = 0; c < nchunks; ++c) {
+        const int kc = c * kChunk;
+        uint16_t *buf = lds[c & 1];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) *reinterpret_cast<u32x4_t *>(buf + part * TILE + off + 8 * v) = pre[v];
+        if (c + 1 < nchunks) fetch(kc + kChunk);
+        __syncthreads();
+        if (kc <= wave_pmax) {
+            ChunkRegs<D> cr;
+            load_chunk<D>(cr, buf, buf + TILE, buf + 2 * TILE, buf + 3 * TILE, g, n);
+            mask_tail<D>(cr, kc, ctx, g);
+            u32x4_t vop[DT];
+            vop_of<D>(cr, vop);
+            chunk_update<D>(qtr, cr.k, vop, qop, kc, ri.prow, g, P.scale_log2);
+        }
+        // quarter and split boundaries fall on chunk boundaries
+        const int next = kc + kChunk;
+        const int sj = split_index(kc);
+        const int sb = split_begin(sj), se = split_begin(sj + 1);
+        const bool last = c + 1 == nchunks;
+        if ((next - sb) % ((se - sb) >> 2) == 0 || last) {
+            fold_state(spl, qtr);
+            state_clear(qtr);
+        }
+        if (next == se || last) {
+            fold_state(fin, spl);
+            state_clear(spl);
+        }
+    }
+    f32x4_t o[DT];
+    finalize(fin, sink_log2(P, kvh, ri.hl), o);
+    store_out<DT>(P, q0, ri, kvh, g, o);
+}
+
+// ---------------------------------------------------------------------------
+// fp32: one wave per (row, query head) over all its keys. Lane t takes key
+// kc + t of each 64-key chunk for the score; lane d (and d + 64) owns channel
+// d of the value sum.
+// ---------------------------------------------------------------------------
+__device__ inline int seq_of_row(const int32_t *qsl, int num_seqs, int row) {
+    int lo = 0, hi = num_seqs;  // qsl[lo] <= row < qsl[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (qsl[mid] <= row) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
     constexpr int DU = D / 64;
     const int lane = threadIdx.x;
-    const int i = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+    const int i = blockIdx.x, h = blockIdx.y;
     const int s = seq_of_row(P.qsl, P.num_seqs, i);
     const int q_len = P.qsl[s + 1] - P.qsl[s];
     const int ctx = P.ctx_lens[s];
     const int p = ctx - q_len + (i - P.qsl[s]);
-    const int ks = split_begin(split);
-    if (ks > p) return;
-    const int ke = min(split_begin(split + 1), p + 1);
+    if (p < 0) return;
     const int kvh = h / P.G;
 
     __shared__ float qs[D];
@@ -347,9 +663,9 @@ __global__ __launch_bounds__(64) void attn_f32_split(AttnParams P) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) acc[u] = 0.f;
 
-    for (int kc = ks; kc < ke; kc += 64) {
+    for (int kc = 0; kc <= p; kc += 64) {
         const int key = kc + lane;
-        const bool vis = key < ke;
+        const bool vis = key <= p;
         int phys = -1;
         if (vis) {
             const int jb = key / kBlock;
@@ -376,19 +692,18 @@ __global__ __launch_bounds__(64) void attn_f32_split(AttnParams P) {
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        const float pv = fast_exp2(sc - m_use);
+        const float alpha = fast_exp2(m - m_new);
+        const float pv = fast_exp2(sc - m_new);
         float rs = pv;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, 64);
-        l = alpha * l + rs;
+        l = fmaf(alpha, l, rs);
         m = m_new;
 #pragma unroll
         for (int u = 0; u < DU; ++u) acc[u] *= alpha;
         for (int bb = 0; bb < 4; ++bb) {
             const int kb0 = kc + kBlock * bb;
-            if (kb0 >= ke) break;
+            if (kb0 > p) break;
             const int pb = __builtin_amdgcn_readlane(phys, kBlock * bb);
             if (pb < 0) continue;
 #pragma unroll
@@ -398,86 +713,28 @@ __global__ __launch_bounds__(64) void attn_f32_split(AttnParams P) {
 #pragma unroll
                 for (int q4 = 0; q4 < kBlock / 4; ++q4) {
                     const f32x4_t x = *reinterpret_cast<const f32x4_t *>(vrow + 4 * q4);
-                    vv[4 * q4 + 0] = x[0];
-                    vv[4 * q4 + 1] = x[1];
-                    vv[4 * q4 + 2] = x[2];
-                    vv[4 * q4 + 3] = x[3];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) vv[4 * q4 + e] = x[e];
                 }
 #pragma unroll
                 for (int tt = 0; tt < kBlock; ++tt) {
-                    const float w = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), kBlock * bb + tt));
-                    const float v = kb0 + tt < ke ? vv[tt] : 0.f;
+                    const float w = bcast(pv, kBlock * bb + tt);
+                    const float v = kb0 + tt <= p ? vv[tt] : 0.f;
                     acc[u] = fmaf(w, v, acc[u]);
                 }
             }
         }
     }
-    const size_t base = ((size_t)i * P.Hq + h) * P.max_splits + split;
-    if (lane == 0) P.ws_ml[base] = make_float2(m, l);
-#pragma unroll
-    for (int u = 0; u < DU; ++u) P.ws_acc[base * D + lane + 64 * u] = acc[u];
-}
-
-// ---------------------------------------------------------------------------
-// Split fold: one wave per (row, query head); lanes own channels.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(64) void attn_reduce(AttnParams P) {
-    constexpr int DU = D / 64;
-    const int lane = threadIdx.x;
-    const int i = blockIdx.x, h = blockIdx.y;
-    const int s = seq_of_row(P.qsl, P.num_seqs, i);
-    const int q_len = P.qsl[s + 1] - P.qsl[s];
-    const int ctx = P.ctx_lens[s];
-    const int p = ctx - q_len + (i - P.qsl[s]);
-    const int ns = min(num_splits(p + 1), P.max_splits);
-    const size_t base = ((size_t)i * P.Hq + h) * P.max_splits;
-    // split maxima and sums, one split per lane (64 at a time), loaded together
-    float M = -INFINITY;
-    for (int j0 = 0; j0 < ns; j0 += 64) {
-        const float mj = j0 + lane < ns ? P.ws_ml[base + j0 + lane].x : -INFINITY;
-        M = fmaxf(M, mj);
+    float lt = l;
+    float al = 1.f;
+    if (P.sinks) {
+        const float sk = P.sinks[h] * kLog2e;
+        const float M = fmaxf(m, sk);
+        al = fast_exp2(m - M);
+        lt = fmaf(l, al, fast_exp2(sk - M));
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float sk = P.sinks ? P.sinks[h] * kLog2e : -INFINITY;
-    M = fmaxf(M, sk);
-    float L = 0.f;
-    float a[DU];
-#pragma unroll
-    for (int u = 0; u < DU; ++u) a[u] = 0.f;
-    for (int j0 = 0; j0 < ns; j0 += 64) {
-        const float2 mlj = j0 + lane < ns ? P.ws_ml[base + j0 + lane] : make_float2(-INFINITY, 0.f);
-        const float wj = fast_exp2(mlj.x - M);
-        const int nj = min(64, ns - j0);
-        int j = 0;
-        for (; j + 4 <= nj; j += 4) {
-            float x[4][DU];
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int u = 0; u < DU; ++u) x[t][u] = P.ws_acc[(base + j0 + j + t) * D + lane + 64 * u];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j + t));
-                const float lj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlj.y), j + t));
-                L = fmaf(lj, w, L);
-#pragma unroll
-                for (int u = 0; u < DU; ++u) a[u] = fmaf(w, x[t][u], a[u]);
-            }
-        }
-        for (; j < nj; ++j) {
-            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
-            const float lj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mlj.y), j));
-            L = fmaf(lj, w, L);
-#pragma unroll
-            for (int u = 0; u < DU; ++u) a[u] = fmaf(w, P.ws_acc[(base + j0 + j) * D + lane + 64 * u], a[u]);
-        }
-    }
-    if (P.sinks) L += fast_exp2(sk - M);
-#pragma unroll
-    for (int u = 0; u < DU; ++u) P.out[((size_t)i * P.Hq + h) * D + lane + 64 * u] = a[u] / L;
+    for (int u = 0; u < DU; ++u) P.out[((size_t)i * P.Hq + h) * D + lane + 64 * u] = (acc[u] * al) / lt;
 }
 
 // ---------------------------------------------------------------------------
@@ -512,35 +769,35 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
 // host side
 // ---------------------------------------------------------------------------
 struct WsLayout {
-    size_t ml_bytes, acc_bytes;
+    size_t counter_bytes, ml_bytes, acc_bytes;
+    size_t total() const { return counter_bytes + ml_bytes + acc_bytes; }
 };
 
-static WsLayout ws_layout(int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Counters are sized for num_q_heads, an upper bound of num_kv_heads, so the
+// size depends only on the arguments of paged_attention_workspace_size.
+static WsLayout ws_layout(int64_t seqs, int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
     const int64_t cells = rows * Hq * splits;
     WsLayout w;
-    w.ml_bytes = (size_t)((cells * 8 + 255) / 256 * 256);
+    w.counter_bytes = round256((size_t)(seqs * Hq * 4));
+    w.ml_bytes = round256((size_t)(cells * 8));
     w.acc_bytes = (size_t)(cells * D * 4);
     return w;
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-template <int D, int NT>
-static void launch_bf16(const AttnParams &P, int items, int one, hipStream_t st) {
-    dim3 grid(items, P.Hkv, P.max_splits);
-    hipLaunchKernelGGL((attn_bf16_split<D, NT>), grid, dim3(64), 0, st, P, one);
-}
-
 template <int D>
-static void launch_bf16_nt(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
+static void launch_bf16(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
-    const int NT = rows_per_seq <= 16 ? 1 : (rows_per_seq <= 32 ? 2 : 4);
-    const int R = 16 * NT;
-    const int one = rows_per_seq <= R;
-    const int items = one ? P.num_seqs : (int)(((int64_t)total_rows * P.G + R - 1) / R + P.num_seqs);
-    if (NT == 1) launch_bf16<D, 1>(P, items, one, st);
-    else if (NT == 2) launch_bf16<D, 2>(P, items, one, st);
-    else launch_bf16<D, 4>(P, items, one, st);
+    const dim3 grid(P.num_seqs, P.Hkv, P.max_splits);
+    if (rows_per_seq <= 16) hipLaunchKernelGGL((attn_parallel<D, 1>), grid, dim3(256), 0, st, P);
+    else hipLaunchKernelGGL((attn_parallel<D, 2>), grid, dim3(256), 0, st, P);
+    if (rows_per_seq > kParRows) {
+        const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
+        hipLaunchKernelGGL((attn_sequential<D>), dim3((unsigned)items, P.Hkv), dim3(256), 0, st, P);
+    }
 }
 
 }  // namespace pkv
@@ -551,8 +808,8 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows, in
                                       int32_t head_dim, int32_t max_context_len) {
     if (num_seqs < 0 || total_q_rows < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0)
         return 0;
-    const pkv::WsLayout w = pkv::ws_layout(total_q_rows, num_q_heads, head_dim, pkv::num_splits(max_context_len));
-    return w.ml_bytes + w.acc_bytes;
+    return pkv::ws_layout(num_seqs, total_q_rows, num_q_heads, head_dim, pkv::num_splits(max_context_len))
+        .total();
 }
 
 int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
@@ -575,7 +832,7 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: num_q_heads %d is not a positive multiple of num_kv_heads %d",
                  num_q_heads, num_kv_heads);
-    if (num_q_heads > 65535 || num_kv_heads > 65535)
+    if (num_q_heads > 65535)
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: too many heads");
     if (!std::isfinite(scale)) PKV_FAIL(KV_EINVAL, "paged_attention_forward: scale is not finite");
     if (num_seqs == 0 || total_q_rows == 0) return KV_OK;
@@ -593,10 +850,10 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: q, pools, out and workspace must be 16-byte aligned");
     const int max_splits = num_splits(max_context_len);
     if (max_splits > 65535) PKV_FAIL(KV_EINVAL, "paged_attention_forward: max_context_len too large");
-    const WsLayout w = ws_layout(total_q_rows, num_q_heads, head_dim, max_splits);
-    if (workspace_bytes < w.ml_bytes + w.acc_bytes)
+    const WsLayout w = ws_layout(num_seqs, total_q_rows, num_q_heads, head_dim, max_splits);
+    if (workspace_bytes < w.total())
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: workspace of %zu bytes, need %zu", workspace_bytes,
-                 w.ml_bytes + w.acc_bytes);
+                 w.total());
 
     AttnParams P;
     P.q = q;
@@ -606,8 +863,9 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     P.ctx_lens = context_lens;
     P.qsl = query_start_loc;
     P.sinks = sinks;
-    P.ws_ml = reinterpret_cast<float2 *>(workspace);
-    P.ws_acc = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.ml_bytes);
+    P.counters = reinterpret_cast<int32_t *>(workspace);
+    P.ws_ml = reinterpret_cast<float2 *>(reinterpret_cast<char *>(workspace) + w.counter_bytes);
+    P.ws_acc = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.counter_bytes + w.ml_bytes);
     P.out = out;
     P.num_seqs = num_seqs;
     P.total_rows = total_q_rows;
@@ -617,21 +875,19 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     P.max_blocks_per_seq = max_blocks_per_seq;
     P.num_blocks = num_blocks;
     P.max_splits = max_splits;
+    P.decode_only = max_q_len == 1 && total_q_rows == num_seqs;
     P.scale_log2 = scale * kLog2e;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
 
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
-        if (head_dim == 64) launch_bf16_nt<64>(P, max_q_len, total_q_rows, st);
-        else launch_bf16_nt<128>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_bf16<64>(P, max_q_len, total_q_rows, st);
+        else launch_bf16<128>(P, max_q_len, total_q_rows, st);
     } else {
-        dim3 grid(total_q_rows, num_q_heads, max_splits);
-        if (head_dim == 64) hipLaunchKernelGGL((attn_f32_split<64>), grid, dim3(64), 0, st, P);
-        else hipLaunchKernelGGL((attn_f32_split<128>), grid, dim3(64), 0, st, P);
+        const dim3 grid(total_q_rows, num_q_heads);
+        if (head_dim == 64) hipLaunchKernelGGL((attn_f32<64>), grid, dim3(64), 0, st, P);
+        else hipLaunchKernelGGL((attn_f32<128>), grid, dim3(64), 0, st, P);
     }
-    dim3 rgrid(total_q_rows, num_q_heads);
-    if (head_dim == 64) hipLaunchKernelGGL((attn_reduce<64>), rgrid, dim3(64), 0, st, P);
-    else hipLaunchKernelGGL((attn_reduce<128>), rgrid, dim3(64), 0, st, P);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         PKV_FAIL(KV_EDEVICE, "paged_attention_forward: launch failed: %s", hipGetErrorString(e));

@@ -112,6 +112,6 @@ def stage(w, device="cuda", copies: int = 1, poison: bool = True, scatter_step: 
         k_step=k_step, v_step=v_step, step_slots=step_dev,
         sinks=None if w.sinks is None else torch.from_numpy(w.sinks).to(device),
         out=torch.empty((rows, w.num_q_heads, D), dtype=torch.float32, device=device),
-        workspace=torch.empty(max(ws, 1), dtype=torch.uint8, device=device),
+        workspace=torch.zeros(max(ws, 1), dtype=torch.uint8, device=device),
         max_q_len=int(max(seq.q_len for seq in w.seqs)), max_context_len=max_ctx, max_blocks=maxb,
         unique_blocks=unique)
