@@ -173,11 +173,9 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
 
 /*
  * Bytes of device workspace paged_attention_forward needs for these sizes
- * (0 on invalid sizes). The workspace holds per-sequence arrival counters
- * followed by per-split partial results. It must be zero-filled before its
- * first use; every call that completes leaves the counters at zero again, so
- * one workspace serves any number of calls. Calls that may run at the same
- * time (different streams) need different workspaces.
+ * (0 on invalid sizes). The workspace holds per-split partial results; its
+ * contents need no initialisation and are meaningless after a call. Calls that
+ * may run at the same time (different streams) need different workspaces.
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
                                       int32_t num_q_heads, int32_t head_dim,
@@ -206,8 +204,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
  *                   [num_seqs] = total_q_rows, q_len <= max_q_len
  *   sinks           device float [num_q_heads] or NULL
  *   out             device float [total_q_rows][num_q_heads][head_dim]
- *   workspace       device, >= paged_attention_workspace_size(...) bytes,
- *                   zero-filled before first use (see above)
+ *   workspace       device, >= paged_attention_workspace_size(...) bytes
  * max_q_len and max_context_len only size the launch and the workspace; they
  * never change a result. Every row's arithmetic depends only on its own query,
  * its visible keys and values, scale and sink: the same row gives the same bits

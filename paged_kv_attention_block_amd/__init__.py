@@ -240,8 +240,7 @@ def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query
         raise KVError(KV_EINVAL, "out has the wrong shape")
     need = paged_attention_workspace_size(S, total, hq, d, max_context_len)
     if workspace is None:
-        # zero-filled: the first bytes hold arrival counters that start at zero
-        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.paged_attention_forward(

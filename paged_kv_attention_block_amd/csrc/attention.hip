@@ -25,9 +25,9 @@
 //    and the one division come last (finalize);
 //  * fp32: one wave per (row, head), one online state over all keys in order.
 // Two bf16 launch shapes compute exactly that: "parallel" (one workgroup per
-// split, a wave per quarter, the last workgroup of a sequence folds the
-// splits) for decode and verify rows, and "sequential" (one workgroup per 64
-// rows walking every split, folds kept in registers) for prefill chunks.
+// split, a wave per quarter, then a fold launch over the split states) for
+// decode and verify rows, and "sequential" (one workgroup per 64 rows walking
+// every split, folds kept in registers) for prefill chunks.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -49,6 +49,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxHeadDim = 128;
 constexpr int kParRows = 32;   // rows per (sequence, KV head) the parallel shape takes
 constexpr int kSeqRows = 64;   // rows per workgroup in the sequential shape
+constexpr int kMaxGroupBlocks = 1024;  // block ids one parallel workgroup stages
 
 // ---------------------------------------------------------------------------
 // Fixed partition of absolute key positions: 256-key splits below 2048,
@@ -73,7 +74,6 @@ struct AttnParams {
     const int32_t *ctx_lens;
     const int32_t *qsl;
     const float *sinks;
-    int32_t *counters;  // [num_seqs][Hkv], zero between calls
     float2 *ws_ml;      // [rows][Hq][max_splits]: split max (log2 units), split sum
     float *ws_acc;      // [rows][Hq][max_splits][D]
     float *out;         // [rows][Hq][D]
@@ -147,12 +147,19 @@ __device__ inline void finalize(const TileState<DT> &s, float sink2, f32x4_t *o)
 }
 
 // ---------------------------------------------------------------------------
-// One 32-key chunk for one tile: kop[tau][j] is the K operand of block tau and
-// k-step j (lane 16g+n holds token n, channels 32j+8g..+7), vop[dt] the V^T
-// operand (channels 16dt+n, tokens 4g..4g+3 of block 0 then of block 1),
-// qop[j] the Q operand (row n, channels 32j+8g..+7). Key kc+16tau+4g+i is
+// One 32-key chunk (blocks b0, b1 = the chunk's two 16-token blocks) for one
+// tile. Lane 16g+n. Key slots: the S^T tile tau row m holds token
+// 8((m/4)%2) + 4tau + m%4 of block m/8, so that after the QK product lane
+// 16g+n holds, for its row n, the scores of tokens 8(g%2)..8(g%2)+7 of block
+// g/2 (tile 0 gives the first four, tile 1 the last four). Those eight keys
+// are the lane's k-slots of the PV product, whose V^T operand is then one
+// 16-byte run of the V block. kop[tau][j]: K of key slot (tau, n), channels
+// 32j+8g..+7; vop[dt]: V^T of channel 16dt+n at the lane's eight keys;
+// qop[j]: Q of row n, channels 32j+8g..+7. Key kc + key_off(g) + 4tau + i is
 // visible to the lane's row when it is <= prow.
 // ---------------------------------------------------------------------------
+__device__ inline int key_off(int g) { return 16 * (g >> 1) + 8 * (g & 1); }
+
 template <int D>
 __device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[2][D / 32],
                                     const u32x4_t (&vop)[D / 16], const u32x4_t (&qop)[D / 32], int kc, int prow,
@@ -168,9 +175,9 @@ __device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[
     float sc[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int key = kc + 4 * g + i;
+        const int key = kc + key_off(g) + i;
         sc[i] = key <= prow ? s0[i] * scale_log2 : -INFINITY;
-        sc[4 + i] = key + 16 <= prow ? s1[i] * scale_log2 : -INFINITY;
+        sc[4 + i] = key + 4 <= prow ? s1[i] * scale_log2 : -INFINITY;
     }
     float mx = sc[0];
 #pragma unroll
@@ -209,49 +216,46 @@ __device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[
     st.m = has ? m_new : st.m;
 }
 
-// K/V operands of one chunk in registers, read from global memory or LDS.
+// K/V operands of one chunk in registers, read from global memory or LDS, in
+// the key-slot order described at chunk_update.
 template <int D>
 struct ChunkRegs {
     u32x4_t k[2][D / 32];
-    u32x2_t v[2][D / 16];
+    u32x4_t v[D / 16];
 };
 
 template <int D>
 __device__ inline void load_chunk(ChunkRegs<D> &c, const uint16_t *kb0, const uint16_t *vb0,
                                   const uint16_t *kb1, const uint16_t *vb1, int g, int n) {
+    const uint16_t *kb = n >= 8 ? kb1 : kb0;                 // block of key slot n
+    const int tk = 8 * ((n >> 2) & 1) + (n & 3);            // its token, tile 0
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) {
-        c.k[0][j] = *reinterpret_cast<const u32x4_t *>(kb0 + ((4 * j + g) * kBlock + n) * 8);
-        c.k[1][j] = *reinterpret_cast<const u32x4_t *>(kb1 + ((4 * j + g) * kBlock + n) * 8);
+        c.k[0][j] = *reinterpret_cast<const u32x4_t *>(kb + ((4 * j + g) * kBlock + tk) * 8);
+        c.k[1][j] = *reinterpret_cast<const u32x4_t *>(kb + ((4 * j + g) * kBlock + tk + 4) * 8);
     }
+    const uint16_t *vb = (g >> 1) ? vb1 : vb0;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        c.v[0][dt] = *reinterpret_cast<const u32x2_t *>(vb0 + (16 * dt + n) * kBlock + 4 * g);
-        c.v[1][dt] = *reinterpret_cast<const u32x2_t *>(vb1 + (16 * dt + n) * kBlock + 4 * g);
-    }
+    for (int dt = 0; dt < D / 16; ++dt)
+        c.v[dt] = *reinterpret_cast<const u32x4_t *>(vb + (16 * dt + n) * kBlock + 8 * (g & 1));
 }
 
 // Zero V of keys at or past ctx, so that a zero weight never meets a NaN.
 template <int D>
 __device__ inline void mask_tail(ChunkRegs<D> &c, int kc, int ctx, int g) {
     if (kc + kChunk <= ctx) return;
+    const int k0 = kc + key_off(g);
+    uint32_t m[4];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-        const int k0 = kc + 16 * tau + 4 * g;
-        const uint32_t m0 = (k0 < ctx ? 0x0000FFFFu : 0u) | (k0 + 1 < ctx ? 0xFFFF0000u : 0u);
-        const uint32_t m1 = (k0 + 2 < ctx ? 0x0000FFFFu : 0u) | (k0 + 3 < ctx ? 0xFFFF0000u : 0u);
+    for (int w = 0; w < 4; ++w)
+        m[w] = (k0 + 2 * w < ctx ? 0x0000FFFFu : 0u) | (k0 + 2 * w + 1 < ctx ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            c.v[tau][dt].x &= m0;
-            c.v[tau][dt].y &= m1;
-        }
+    for (int dt = 0; dt < D / 16; ++dt) {
+        c.v[dt].x &= m[0];
+        c.v[dt].y &= m[1];
+        c.v[dt].z &= m[2];
+        c.v[dt].w &= m[3];
     }
-}
-
-template <int D>
-__device__ inline void vop_of(const ChunkRegs<D> &c, u32x4_t (&vop)[D / 16]) {
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) vop[dt] = u32x4_t{c.v[0][dt].x, c.v[0][dt].y, c.v[1][dt].x, c.v[1][dt].y};
 }
 
 // Rows rho = row0 + 16 t + n of a sequence's [q_len * G] row space, ordered
@@ -292,19 +296,22 @@ __device__ inline void store_out(const AttnParams &P, int q0, const RowInfo &ri,
 }
 
 // ---------------------------------------------------------------------------
-// Parallel shape: grid (sequence, KV head, split); 4 waves, wave w takes
-// quarter w of the split for all NT tiles (up to 16 NT rows per sequence and
-// KV head). Quarter states meet in LDS; a sequence with one split finishes
-// here, otherwise the split state goes to the workspace and the last
-// workgroup of the (sequence, KV head) folds all splits.
+// Parallel shape: grid (sequence, KV head, group of spw consecutive splits);
+// 4 waves, wave w streams quarter w of every split of the group, for all NT
+// tiles (up to 16 NT rows per sequence and KV head). At each split end the
+// quarter states meet in LDS and wave 0 folds them. A group that holds every
+// split of its sequence folds the split states itself and writes the output;
+// otherwise each split state goes to the workspace for attn_fold.
+// The wave's chunks form one stream across the group's splits with the next
+// chunk always in flight while the current one is computed.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(256) void attn_parallel(AttnParams P) {
+__global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_keys) {
     constexpr int DT = D / 16, KJ = D / 32;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int g = lane >> 4, n = lane & 15;
-    const int s = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
+    const int s = blockIdx.x, kvh = blockIdx.y;
 
     int q0, q_len;
     if (P.decode_only) {
@@ -318,11 +325,15 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P) {
     const int rows_total = q_len * P.G;
     if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT) return;
     const int p_max = ctx - q_len + (rows_total - 1) / P.G;
-    const int ks = split_begin(split);
-    if (ks > p_max) return;
-    const int qlen4 = (split_begin(split + 1) - ks) >> 2;
-    const int kq0 = ks + wave * qlen4;
-    const int kq1 = min(kq0 + qlen4, p_max + 1);
+    if (p_max < 0) return;
+    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
+    // this group: the splits that cover keys [z * group_keys, (z + 1) * group_keys)
+    const int g_lo = blockIdx.z * group_keys;
+    if (g_lo > p_max) return;
+    const int j0 = split_index(g_lo);
+    const int j1 = min(split_index(min(g_lo + group_keys, p_max + 1) - 1) + 1, ns_item);
+    if (j0 >= j1) return;
+    const bool whole = j0 == 0 && j1 == ns_item;
 
     RowInfo ri[NT];
     u32x4_t qop[NT][KJ];
@@ -334,151 +345,215 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P) {
         state_clear(st[t]);
     }
 
-    if (kq0 < kq1) {
-        // physical block ids of the quarter, one per lane
-        const int jb0 = kq0 / kBlock;
-        const int nb_q = (kq1 - kq0 + kBlock - 1) / kBlock;
+    // quarter w of split j: [kq0(j), kq1(j)); empty once kq0 > p_max
+    auto kq0_of = [&](int j) {
+        const int ks = split_begin(j);
+        return ks + wave * ((split_begin(j + 1) - ks) >> 2);
+    };
+    auto kq1_of = [&](int j) {
+        const int ks = split_begin(j);
+        return min(ks + (wave + 1) * ((split_begin(j + 1) - ks) >> 2), p_max + 1);
+    };
+
+    // physical ids of every block the group reads, staged once in LDS
+    __shared__ int lds_bid[kMaxGroupBlocks];
+    const int jb_first = split_begin(j0) / kBlock;
+    const int nb_group = min((min(split_begin(j1), p_max + 1) + kBlock - 1) / kBlock - jb_first, kMaxGroupBlocks);
+    {
         const int nblk_seq = (ctx + kBlock - 1) / kBlock;
-        int bid = -1;
-        if (lane < nb_q) {
-            const int jb = jb0 + lane;
+        const int32_t *bt_row = P.bt + (size_t)s * P.max_blocks_per_seq;
+        for (int i = tid; i < nb_group; i += 256) {
+            const int jb = jb_first + i;
+            int b = -1;
             if (jb < nblk_seq && jb < P.max_blocks_per_seq) {
-                const int b = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
-                bid = (b >= 0 && b < P.num_blocks) ? b : -1;
+                b = bt_row[jb];
+                b = (b >= 0 && b < P.num_blocks) ? b : -1;
             }
-        }
-        const size_t tile = (size_t)kBlock * D;
-        const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
-        const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
-        const size_t bstride = (size_t)P.Hkv * tile;
-        auto kptr = [&](int b) { return b >= 0 ? kbase + (size_t)b * bstride : g_zero_tile; };
-        auto vptr = [&](int b) { return b >= 0 ? vbase + (size_t)b * bstride : g_zero_tile; };
-        auto fetch = [&](ChunkRegs<D> &c, int kc) {
-            const int ci = (kc - kq0) / kBlock;
-            const int b0 = __builtin_amdgcn_readlane(bid, ci);
-            const int b1 = __builtin_amdgcn_readlane(bid, ci + 1);
-            load_chunk<D>(c, kptr(b0), vptr(b0), kptr(b1), vptr(b1), g, n);
-        };
-        auto compute = [&](ChunkRegs<D> &c, int kc) {
-            mask_tail<D>(c, kc, ctx, g);
-            u32x4_t vop[DT];
-            vop_of<D>(c, vop);
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                if (16 * t < rows_total) chunk_update<D>(st[t], c.k, vop, qop[t], kc, ri[t].prow, g, P.scale_log2);
-        };
-        ChunkRegs<D> ca, cb;
-        fetch(ca, kq0);
-        for (int kc = kq0; kc < kq1; kc += 2 * kChunk) {
-            const bool more = kc + kChunk < kq1;
-            if (more) fetch(cb, kc + kChunk);
-            compute(ca, kc);
-            if (!more) break;
-            if (kc + 2 * kChunk < kq1) fetch(ca, kc + 2 * kChunk);
-            compute(cb, kc + kChunk);
+            lds_bid[i] = b;
         }
     }
+    __syncthreads();
 
-    // quarter states -> split state (left fold in quarter order), in wave 0
-    __shared__ f32x4_t lds_acc[3][NT][DT][64];
-    __shared__ float2 lds_ml[3][NT][64];
-    __shared__ int lds_last;
-    if (wave > 0) {
+    const size_t tile = (size_t)kBlock * D;
+    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
+    const size_t bstride = (size_t)P.Hkv * tile;
+    auto block_at = [&](int jb) {
+        const int i = jb - jb_first;
+        return i < nb_group ? __builtin_amdgcn_readfirstlane(lds_bid[i]) : -1;
+    };
+    auto fetch = [&](ChunkRegs<D> &c, int kc) {
+        const int b0 = kc >= 0 ? block_at(kc / kBlock) : -1;
+        const int b1 = kc >= 0 ? block_at(kc / kBlock + 1) : -1;
+        load_chunk<D>(c, b0 >= 0 ? kbase + (size_t)b0 * bstride : g_zero_tile,
+                      b0 >= 0 ? vbase + (size_t)b0 * bstride : g_zero_tile,
+                      b1 >= 0 ? kbase + (size_t)b1 * bstride : g_zero_tile,
+                      b1 >= 0 ? vbase + (size_t)b1 * bstride : g_zero_tile, g, n);
+    };
+    auto compute = [&](ChunkRegs<D> &c, int kc) {
+        mask_tail<D>(c, kc, ctx, g);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            if (16 * t < rows_total) chunk_update<D>(st[t], c.k, c.v, qop[t], kc, ri[t].prow, g, P.scale_log2);
+    };
+
+    __shared__ f32x4_t lds_acc[2][3][NT][DT][64];
+    __shared__ float2 lds_ml[2][3][NT][64];
+    // row state of a whole group, kept by wave 0 in LDS between splits
+    __shared__ f32x4_t fin_acc[NT][DT][64];
+    __shared__ float2 fin_ml[NT][64];
+    if (whole && wave == 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) fin_ml[t][lane] = make_float2(-INFINITY, 0.f);
+    }
+    // end of split j: quarter states -> split state (wave 0), then either
+    // into the row state or out to the workspace
+    auto split_end = [&](int j) {
+        const int buf = j & 1;
+        if (wave > 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                lds_ml[buf][wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lds_acc[buf][wave - 1][t][dt][lane] = st[t].acc[dt];
+                state_clear(st[t]);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+#pragma unroll
+                for (int w = 0; w < 3; ++w) {
+                    TileState<DT> o;
+                    const float2 ml = lds_ml[buf][w][t][lane];
+                    o.m = ml.x;
+                    o.l = ml.y;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds_acc[buf][w][t][dt][lane];
+                    fold_state(st[t], o);
+                }
+                if (whole) {
+                    TileState<DT> f;
+                    const float2 ml = fin_ml[t][lane];
+                    f.m = ml.x;
+                    f.l = ml.y;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) f.acc[dt] = fin_acc[t][dt][lane];
+                    fold_state(f, st[t]);
+                    fin_ml[t][lane] = make_float2(f.m, f.l);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) fin_acc[t][dt][lane] = f.acc[dt];
+                } else if (ri[t].prow >= 0) {
+                    const size_t base =
+                        ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + j;
+                    if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
+                }
+                state_clear(st[t]);
+            }
+        }
+    };
+
+    // The wave streams its quarters' chunks in pairs (A, B); quarters hold an
+    // even number of chunks except a last one cut by p_max, whose missing
+    // partner would be fully masked and is simply skipped. The chunk after
+    // each pair, possibly the first of the next split, is fetched into A
+    // while B is computed.
+    // Every fetch is unconditional (a missing chunk reads the zero tile), so
+    // the loop-carried registers are always fresh loads and never need a copy
+    // that would wait for loads in flight.
+    ChunkRegs<D> ca, cb;
+    fetch(ca, kq0_of(j0) <= p_max ? kq0_of(j0) : -1);
+    for (int j = j0; j < j1; ++j) {
+        const int kq0 = kq0_of(j), kq1 = kq1_of(j);
+        for (int kc = kq0; kc < kq1; kc += 2 * kChunk) {
+            const bool has_b = kc + kChunk < kq1;
+            fetch(cb, has_b ? kc + kChunk : -1);
+            compute(ca, kc);
+            int nxt = kc + 2 * kChunk;
+            if (nxt >= kq1) nxt = j + 1 < j1 && kq0_of(j + 1) <= p_max ? kq0_of(j + 1) : -1;
+            fetch(ca, nxt);
+            if (has_b) compute(cb, kc + kChunk);
+        }
+        split_end(j);
+    }
+    if (whole && wave == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            lds_ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
+            TileState<DT> f;
+            const float2 ml = fin_ml[t][lane];
+            f.m = ml.x;
+            f.l = ml.y;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) lds_acc[wave - 1][t][dt][lane] = st[t].acc[dt];
+            for (int dt = 0; dt < DT; ++dt) f.acc[dt] = fin_acc[t][dt][lane];
+            f32x4_t o[DT];
+            finalize(f, sink_log2(P, kvh, ri[t].hl), o);
+            store_out<DT>(P, q0, ri[t], kvh, g, o);
         }
     }
-    __syncthreads();
-    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
-    if (wave == 0) {
-#pragma unroll
-        for (int w = 0; w < 3; ++w)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                TileState<DT> o;
-                const float2 ml = lds_ml[w][t][lane];
-                o.m = ml.x;
-                o.l = ml.y;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds_acc[w][t][dt][lane];
-                fold_state(st[t], o);
-            }
-        if (ns_item == 1) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                f32x4_t o[DT];
-                finalize(st[t], sink_log2(P, kvh, ri[t].hl), o);
-                store_out<DT>(P, q0, ri[t], kvh, g, o);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (ri[t].prow < 0) continue;
-                const size_t base =
-                    ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + split;
-                if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
-            }
-        }
-    }
-    if (ns_item == 1) return;
+}
 
-    // arrival count of this (sequence, KV head); the last workgroup folds
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const int old = atomicAdd(&P.counters[(size_t)s * P.Hkv + kvh], 1);
-        lds_last = old == ns_item - 1;
-    }
-    __syncthreads();
-    if (!lds_last) return;
-    __threadfence();
-    if (tid == 0) atomicExch(&P.counters[(size_t)s * P.Hkv + kvh], 0);
-
-    // split states -> row state, left fold in split order; wave w owns the
-    // d-tiles w, w + 4, ... (the fold is elementwise in d)
-    constexpr int DW = DT / 4;
+// ---------------------------------------------------------------------------
+// Split fold of the parallel shape: grid (sequence, KV head, tile); wave w
+// owns the d-tiles w, w + 4, ... of the tile's rows (the fold is elementwise
+// in d) and folds the split states left to right, then finalizes.
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+__global__ __launch_bounds__(256) void attn_fold(AttnParams P, int group_keys) {
+    constexpr int DT = D / 16, DW = DT / 4;
     static_assert(DT % 4 == 0, "head_dim must be a multiple of 64");
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        if (16 * t >= rows_total) continue;
-        const RowInfo &r = ri[t];
-        const size_t base0 = ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * P.max_splits;
-        TileState<DW> acc;
-        state_clear(acc);
-        auto read = [&](TileState<DW> &x, int j) {
-            const float2 ml = P.ws_ml[base0 + j];
-            x.m = ml.x;
-            x.l = ml.y;
-#pragma unroll
-            for (int e = 0; e < DW; ++e)
-                x.acc[e] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j) * D + 16 * (wave + 4 * e) + 4 * g);
-        };
-        int j = 0;
-        for (; j + 4 <= ns_item; j += 4) {
-            TileState<DW> x[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) read(x[u], j + u);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) fold_state(acc, x[u]);
-        }
-        for (; j < ns_item; ++j) {
-            TileState<DW> x;
-            read(x, j);
-            fold_state(acc, x);
-        }
-        if (r.prow < 0) continue;
-        f32x4_t o[DW];
-        finalize(acc, sink_log2(P, kvh, r.hl), o);
-        float *dst = P.out + ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * D + 4 * g;
-#pragma unroll
-        for (int e = 0; e < DW; ++e) *reinterpret_cast<f32x4_t *>(dst + 16 * (wave + 4 * e)) = o[e];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
+    const int g = lane >> 4, n = lane & 15;
+    const int s = blockIdx.x, kvh = blockIdx.y, t = blockIdx.z;
+    int q0, q_len;
+    if (P.decode_only) {
+        q0 = s;
+        q_len = 1;
+    } else {
+        q0 = P.qsl[s];
+        q_len = P.qsl[s + 1] - q0;
     }
+    const int ctx = P.ctx_lens[s];
+    const int rows_total = q_len * P.G;
+    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT || 16 * t >= rows_total) return;
+    const int p_max = ctx - q_len + (rows_total - 1) / P.G;
+    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
+    if (p_max + 1 <= group_keys) return;  // one workgroup held every split and finished it
+    const RowInfo r = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
+    const size_t base0 = ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * P.max_splits;
+    TileState<DW> acc;
+    state_clear(acc);
+    auto read = [&](TileState<DW> &x, int j) {
+        const float2 ml = P.ws_ml[base0 + j];
+        x.m = ml.x;
+        x.l = ml.y;
+#pragma unroll
+        for (int e = 0; e < DW; ++e)
+            x.acc[e] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j) * D + 16 * (wave + 4 * e) + 4 * g);
+    };
+    int j = 0;
+    for (; j + 4 <= ns_item; j += 4) {
+        TileState<DW> x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) read(x[u], j + u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fold_state(acc, x[u]);
+    }
+    for (; j < ns_item; ++j) {
+        TileState<DW> x;
+        read(x, j);
+        fold_state(acc, x);
+    }
+    if (r.prow < 0) return;
+    f32x4_t o[DW];
+    finalize(acc, sink_log2(P, kvh, r.hl), o);
+    float *dst = P.out + ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * D + 4 * g;
+#pragma unroll
+    for (int e = 0; e < DW; ++e) *reinterpret_cast<f32x4_t *>(dst + 16 * (wave + 4 * e)) = o[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -524,7 +599,7 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     constexpr int PER_THREAD = CHUNK / 256;   // elements staged by each thread
     constexpr int NV = PER_THREAD / 8;        // 16-byte pieces per thread
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int g = lane >> 4, n = lane & 15;
     const int kvh = blockIdx.y;
 
@@ -600,9 +675,7 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
             ChunkRegs<D> cr;
             load_chunk<D>(cr, buf, buf + TILE, buf + 2 * TILE, buf + 3 * TILE, g, n);
             mask_tail<D>(cr, kc, ctx, g);
-            u32x4_t vop[DT];
-            vop_of<D>(cr, vop);
-            chunk_update<D>(qtr, cr.k, vop, qop, kc, ri.prow, g, P.scale_log2);
+            chunk_update<D>(qtr, cr.k, cr.v, qop, kc, ri.prow, g, P.scale_log2);
         }
         // quarter and split boundaries fall on chunk boundaries
         const int next = kc + kChunk;
@@ -769,18 +842,15 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
 // host side
 // ---------------------------------------------------------------------------
 struct WsLayout {
-    size_t counter_bytes, ml_bytes, acc_bytes;
-    size_t total() const { return counter_bytes + ml_bytes + acc_bytes; }
+    size_t ml_bytes, acc_bytes;
+    size_t total() const { return ml_bytes + acc_bytes; }
 };
 
 static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Counters are sized for num_q_heads, an upper bound of num_kv_heads, so the
-// size depends only on the arguments of paged_attention_workspace_size.
-static WsLayout ws_layout(int64_t seqs, int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
+static WsLayout ws_layout(int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
     const int64_t cells = rows * Hq * splits;
     WsLayout w;
-    w.counter_bytes = round256((size_t)(seqs * Hq * 4));
     w.ml_bytes = round256((size_t)(cells * 8));
     w.acc_bytes = (size_t)(cells * D * 4);
     return w;
@@ -788,12 +858,34 @@ static WsLayout ws_layout(int64_t seqs, int64_t rows, int64_t Hq, int64_t D, int
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Keys per parallel workgroup: a power of two from 256 (1024 once contexts
+// pass 2048, so that groups never cut a 1024-key split), as small as gives
+// about kTargetGroups workgroups over the batch. Groups cover equal key
+// ranges, so workgroups carry equal loads. The choice only moves work between
+// workgroups; it never changes a result.
+constexpr int kTargetGroups = 1024;
+
+static int keys_per_group(const AttnParams &P, int max_context_len) {
+    const int64_t units = (int64_t)P.num_seqs * P.Hkv;
+    int kg = max_context_len > kEdge ? kSplitB : kSplitA;
+    while (kg < kMaxGroupBlocks * kBlock && units * ((max_context_len + kg - 1) / kg) > kTargetGroups) kg *= 2;
+    return kg;
+}
+
 template <int D>
-static void launch_bf16(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
+static void launch_bf16(const AttnParams &P, int max_q_len, int max_context_len, int total_rows,
+                        hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
-    const dim3 grid(P.num_seqs, P.Hkv, P.max_splits);
-    if (rows_per_seq <= 16) hipLaunchKernelGGL((attn_parallel<D, 1>), grid, dim3(256), 0, st, P);
-    else hipLaunchKernelGGL((attn_parallel<D, 2>), grid, dim3(256), 0, st, P);
+    const int kg = keys_per_group(P, max_context_len);
+    const dim3 grid(P.num_seqs, P.Hkv, (max_context_len + kg - 1) / kg);
+    const bool fold = max_context_len > kg;
+    if (rows_per_seq <= 16) {
+        hipLaunchKernelGGL((attn_parallel<D, 1>), grid, dim3(256), 0, st, P, kg);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P, kg);
+    } else {
+        hipLaunchKernelGGL((attn_parallel<D, 2>), grid, dim3(256), 0, st, P, kg);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P, kg);
+    }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
         hipLaunchKernelGGL((attn_sequential<D>), dim3((unsigned)items, P.Hkv), dim3(256), 0, st, P);
@@ -808,8 +900,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows, in
                                       int32_t head_dim, int32_t max_context_len) {
     if (num_seqs < 0 || total_q_rows < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0)
         return 0;
-    return pkv::ws_layout(num_seqs, total_q_rows, num_q_heads, head_dim, pkv::num_splits(max_context_len))
-        .total();
+    return pkv::ws_layout(total_q_rows, num_q_heads, head_dim, pkv::num_splits(max_context_len)).total();
 }
 
 int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
@@ -850,7 +941,7 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: q, pools, out and workspace must be 16-byte aligned");
     const int max_splits = num_splits(max_context_len);
     if (max_splits > 65535) PKV_FAIL(KV_EINVAL, "paged_attention_forward: max_context_len too large");
-    const WsLayout w = ws_layout(num_seqs, total_q_rows, num_q_heads, head_dim, max_splits);
+    const WsLayout w = ws_layout(total_q_rows, num_q_heads, head_dim, max_splits);
     if (workspace_bytes < w.total())
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: workspace of %zu bytes, need %zu", workspace_bytes,
                  w.total());
@@ -863,9 +954,8 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     P.ctx_lens = context_lens;
     P.qsl = query_start_loc;
     P.sinks = sinks;
-    P.counters = reinterpret_cast<int32_t *>(workspace);
-    P.ws_ml = reinterpret_cast<float2 *>(reinterpret_cast<char *>(workspace) + w.counter_bytes);
-    P.ws_acc = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.counter_bytes + w.ml_bytes);
+    P.ws_ml = reinterpret_cast<float2 *>(workspace);
+    P.ws_acc = reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + w.ml_bytes);
     P.out = out;
     P.num_seqs = num_seqs;
     P.total_rows = total_q_rows;
@@ -881,8 +971,8 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
 
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
-        if (head_dim == 64) launch_bf16<64>(P, max_q_len, total_q_rows, st);
-        else launch_bf16<128>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_bf16<64>(P, max_q_len, max_context_len, total_q_rows, st);
+        else launch_bf16<128>(P, max_q_len, max_context_len, total_q_rows, st);
     } else {
         const dim3 grid(total_q_rows, num_q_heads);
         if (head_dim == 64) hipLaunchKernelGGL((attn_f32<64>), grid, dim3(64), 0, st, P);
