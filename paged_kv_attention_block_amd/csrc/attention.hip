@@ -147,30 +147,72 @@ __device__ inline void finalize(const TileState<DT> &s, float sink2, f32x4_t *o)
 }
 
 // ---------------------------------------------------------------------------
-// One 32-key chunk (blocks b0, b1 = the chunk's two 16-token blocks) for one
-// tile. Lane 16g+n. Key slots: the S^T tile tau row m holds token
-// 8((m/4)%2) + 4tau + m%4 of block m/8, so that after the QK product lane
-// 16g+n holds, for its row n, the scores of tokens 8(g%2)..8(g%2)+7 of block
-// g/2 (tile 0 gives the first four, tile 1 the last four). Those eight keys
-// are the lane's k-slots of the PV product, whose V^T operand is then one
-// 16-byte run of the V block. kop[tau][j]: K of key slot (tau, n), channels
-// 32j+8g..+7; vop[dt]: V^T of channel 16dt+n at the lane's eight keys;
-// qop[j]: Q of row n, channels 32j+8g..+7. Key kc + key_off(g) + 4tau + i is
-// visible to the lane's row when it is <= prow.
+// One online-softmax step: a 32-key chunk, blocks b0 and b1. Lane 16g+n.
+// Key slots: the S^T tile tau row m holds token 8((m/4)%2) + 4tau + m%4 of
+// block m/8, so that after the QK product lane 16g+n holds, for its row n,
+// the scores of tokens 8(g%2)..8(g%2)+7 of block g/2 (tile 0 the first four,
+// tile 1 the last four). Those eight keys are the lane's k-slots of the PV
+// product, whose V^T operand is then one 16-byte run of the V block.
+//   k[tau][j]: K of key slot (tau, n), channels 32j+8g..+7
+//   v[dt]:     V^T of channel 16dt+n at the lane's eight keys
+//   qop[j]:    Q of row n, channels 32j+8g..+7
+// Key kc + key_off(g) + 4tau + i is visible to the lane's row when <= prow.
 // ---------------------------------------------------------------------------
+constexpr int kStep = 32;
 __device__ inline int key_off(int g) { return 16 * (g >> 1) + 8 * (g & 1); }
 
 template <int D>
-__device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[2][D / 32],
-                                    const u32x4_t (&vop)[D / 16], const u32x4_t (&qop)[D / 32], int kc, int prow,
-                                    int g, float scale_log2) {
+struct StepRegs {
+    u32x4_t k[2][D / 32];
+    u32x4_t v[D / 16];
+};
+
+// K/V operands of one chunk; kb0/vb0 and kb1/vb1 point at the K and V tiles
+// of its two blocks (global memory or LDS).
+template <int D>
+__device__ inline void load_step(StepRegs<D> &r, const uint16_t *kb0, const uint16_t *vb0, const uint16_t *kb1,
+                                 const uint16_t *vb1, int g, int n) {
+    const uint16_t *k = n >= 8 ? kb1 : kb0;
+    const int tk = 8 * ((n >> 2) & 1) + (n & 3);  // token of key slot n, tile 0
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+        r.k[0][j] = *reinterpret_cast<const u32x4_t *>(k + ((4 * j + g) * kBlock + tk) * 8);
+        r.k[1][j] = *reinterpret_cast<const u32x4_t *>(k + ((4 * j + g) * kBlock + tk + 4) * 8);
+    }
+    const uint16_t *v = (g >> 1) ? vb1 : vb0;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        r.v[dt] = *reinterpret_cast<const u32x4_t *>(v + (16 * dt + n) * kBlock + 8 * (g & 1));
+}
+
+// Zero V of keys at or past ctx, so that a zero weight never meets a NaN.
+template <int D>
+__device__ inline void mask_tail(StepRegs<D> &r, int kc, int ctx, int g) {
+    if (kc + kStep <= ctx) return;
+    const int k0 = kc + key_off(g);
+    uint32_t m[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        m[w] = (k0 + 2 * w < ctx ? 0x0000FFFFu : 0u) | (k0 + 2 * w + 1 < ctx ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        r.v[dt].x &= m[0];
+        r.v[dt].y &= m[1];
+        r.v[dt].z &= m[2];
+        r.v[dt].w &= m[3];
+    }
+}
+
+template <int D>
+__device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
+                                   int prow, int g, float scale_log2) {
     constexpr int KJ = D / 32, DT = D / 16;
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, qop[j]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[0][j]), b, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[1][j]), b, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[0][j]), b, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][j]), b, s1, 0, 0, 0);
     }
     float sc[8];
 #pragma unroll
@@ -179,9 +221,7 @@ __device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[
         sc[i] = key <= prow ? s0[i] * scale_log2 : -INFINITY;
         sc[4 + i] = key + 4 <= prow ? s1[i] * scale_log2 : -INFINITY;
     }
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const bool has = kc <= prow;  // the row sees at least one key of the chunk
@@ -191,71 +231,32 @@ __device__ inline void chunk_update(TileState<D / 16> &st, const u32x4_t (&kop)[
     float pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
-    float rs = pv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) rs += pv[e];
+    float rs = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
     rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
     bf16x8_t phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const __bf16 h = (__bf16)pv[e];
-        phi[e] = h;
-        plo[e] = (__bf16)(pv[e] - (float)h);
+        const __bf16 x = (__bf16)pv[e];
+        phi[e] = x;
+        plo[e] = (__bf16)(pv[e] - (float)x);
     }
-    const float l_new = fmaf(alpha, st.l, rs);
+    // Rows with no visible key in the chunk keep their state exactly; the
+    // rescale by alpha is skipped when it is 1 in every lane (x * 1 == x).
+    const bool rescale = __any(alpha != 1.f);
+    const bool all_has = __all(has);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, vop[dt]);
-        f32x4_t a = st.acc[dt] * alpha;
+        f32x4_t a = st.acc[dt];
+        if (rescale) a *= alpha;
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, r.v[dt]);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a, 0, 0, 0);
-        st.acc[dt] = has ? a : st.acc[dt];
+        st.acc[dt] = (all_has || has) ? a : st.acc[dt];
     }
+    const float l_new = fmaf(alpha, st.l, rs);
     st.l = has ? l_new : st.l;
     st.m = has ? m_new : st.m;
-}
-
-// K/V operands of one chunk in registers, read from global memory or LDS, in
-// the key-slot order described at chunk_update.
-template <int D>
-struct ChunkRegs {
-    u32x4_t k[2][D / 32];
-    u32x4_t v[D / 16];
-};
-
-template <int D>
-__device__ inline void load_chunk(ChunkRegs<D> &c, const uint16_t *kb0, const uint16_t *vb0,
-                                  const uint16_t *kb1, const uint16_t *vb1, int g, int n) {
-    const uint16_t *kb = n >= 8 ? kb1 : kb0;                 // block of key slot n
-    const int tk = 8 * ((n >> 2) & 1) + (n & 3);            // its token, tile 0
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-        c.k[0][j] = *reinterpret_cast<const u32x4_t *>(kb + ((4 * j + g) * kBlock + tk) * 8);
-        c.k[1][j] = *reinterpret_cast<const u32x4_t *>(kb + ((4 * j + g) * kBlock + tk + 4) * 8);
-    }
-    const uint16_t *vb = (g >> 1) ? vb1 : vb0;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-        c.v[dt] = *reinterpret_cast<const u32x4_t *>(vb + (16 * dt + n) * kBlock + 8 * (g & 1));
-}
-
-// Zero V of keys at or past ctx, so that a zero weight never meets a NaN.
-template <int D>
-__device__ inline void mask_tail(ChunkRegs<D> &c, int kc, int ctx, int g) {
-    if (kc + kChunk <= ctx) return;
-    const int k0 = kc + key_off(g);
-    uint32_t m[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-        m[w] = (k0 + 2 * w < ctx ? 0x0000FFFFu : 0u) | (k0 + 2 * w + 1 < ctx ? 0xFFFF0000u : 0u);
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        c.v[dt].x &= m[0];
-        c.v[dt].y &= m[1];
-        c.v[dt].z &= m[2];
-        c.v[dt].w &= m[3];
-    }
 }
 
 // Rows rho = row0 + 16 t + n of a sequence's [q_len * G] row space, ordered
@@ -296,14 +297,15 @@ __device__ inline void store_out(const AttnParams &P, int q0, const RowInfo &ri,
 }
 
 // ---------------------------------------------------------------------------
-// Parallel shape: grid (sequence, KV head, group of spw consecutive splits);
-// 4 waves, wave w streams quarter w of every split of the group, for all NT
+// Parallel shape: grid (sequence, KV head, key group); a group covers the
+// splits of keys [z * group_keys, (z + 1) * group_keys). 4 waves; wave w
+// streams quarter w of every split of the group, 64-key steps, for all NT
 // tiles (up to 16 NT rows per sequence and KV head). At each split end the
 // quarter states meet in LDS and wave 0 folds them. A group that holds every
 // split of its sequence folds the split states itself and writes the output;
 // otherwise each split state goes to the workspace for attn_fold.
-// The wave's chunks form one stream across the group's splits with the next
-// chunk always in flight while the current one is computed.
+// Each step is loaded and then computed; the 2-3 resident workgroups per CU
+// keep enough loads in flight while others compute.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_keys) {
@@ -327,7 +329,6 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
     const int p_max = ctx - q_len + (rows_total - 1) / P.G;
     if (p_max < 0) return;
     const int ns_item = min(num_splits(p_max + 1), P.max_splits);
-    // this group: the splits that cover keys [z * group_keys, (z + 1) * group_keys)
     const int g_lo = blockIdx.z * group_keys;
     if (g_lo > p_max) return;
     const int j0 = split_index(g_lo);
@@ -345,20 +346,11 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
         state_clear(st[t]);
     }
 
-    // quarter w of split j: [kq0(j), kq1(j)); empty once kq0 > p_max
-    auto kq0_of = [&](int j) {
-        const int ks = split_begin(j);
-        return ks + wave * ((split_begin(j + 1) - ks) >> 2);
-    };
-    auto kq1_of = [&](int j) {
-        const int ks = split_begin(j);
-        return min(ks + (wave + 1) * ((split_begin(j + 1) - ks) >> 2), p_max + 1);
-    };
-
     // physical ids of every block the group reads, staged once in LDS
     __shared__ int lds_bid[kMaxGroupBlocks];
     const int jb_first = split_begin(j0) / kBlock;
-    const int nb_group = min((min(split_begin(j1), p_max + 1) + kBlock - 1) / kBlock - jb_first, kMaxGroupBlocks);
+    const int nb_group =
+        min((min(split_begin(j1), p_max + 1) + kBlock - 1) / kBlock - jb_first, kMaxGroupBlocks);
     {
         const int nblk_seq = (ctx + kBlock - 1) / kBlock;
         const int32_t *bt_row = P.bt + (size_t)s * P.max_blocks_per_seq;
@@ -372,33 +364,8 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
             lds_bid[i] = b;
         }
     }
-    __syncthreads();
-
-    const size_t tile = (size_t)kBlock * D;
-    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
-    const size_t bstride = (size_t)P.Hkv * tile;
-    auto block_at = [&](int jb) {
-        const int i = jb - jb_first;
-        return i < nb_group ? __builtin_amdgcn_readfirstlane(lds_bid[i]) : -1;
-    };
-    auto fetch = [&](ChunkRegs<D> &c, int kc) {
-        const int b0 = kc >= 0 ? block_at(kc / kBlock) : -1;
-        const int b1 = kc >= 0 ? block_at(kc / kBlock + 1) : -1;
-        load_chunk<D>(c, b0 >= 0 ? kbase + (size_t)b0 * bstride : g_zero_tile,
-                      b0 >= 0 ? vbase + (size_t)b0 * bstride : g_zero_tile,
-                      b1 >= 0 ? kbase + (size_t)b1 * bstride : g_zero_tile,
-                      b1 >= 0 ? vbase + (size_t)b1 * bstride : g_zero_tile, g, n);
-    };
-    auto compute = [&](ChunkRegs<D> &c, int kc) {
-        mask_tail<D>(c, kc, ctx, g);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-            if (16 * t < rows_total) chunk_update<D>(st[t], c.k, c.v, qop[t], kc, ri[t].prow, g, P.scale_log2);
-    };
-
-    __shared__ f32x4_t lds_acc[2][3][NT][DT][64];
-    __shared__ float2 lds_ml[2][3][NT][64];
+    __shared__ f32x4_t lds_acc[3][NT][DT][64];
+    __shared__ float2 lds_ml[3][NT][64];
     // row state of a whole group, kept by wave 0 in LDS between splits
     __shared__ f32x4_t fin_acc[NT][DT][64];
     __shared__ float2 fin_ml[NT][64];
@@ -406,16 +373,39 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
 #pragma unroll
         for (int t = 0; t < NT; ++t) fin_ml[t][lane] = make_float2(-INFINITY, 0.f);
     }
-    // end of split j: quarter states -> split state (wave 0), then either
-    // into the row state or out to the workspace
-    auto split_end = [&](int j) {
-        const int buf = j & 1;
+    __syncthreads();
+
+    const size_t tile = (size_t)kBlock * D;
+    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
+    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
+    const size_t bstride = (size_t)P.Hkv * tile;
+
+    for (int j = j0; j < j1; ++j) {
+        const int ks = split_begin(j);
+        const int ql = (split_begin(j + 1) - ks) >> 2;
+        const int kq0 = ks + wave * ql;
+        const int kq1 = min(kq0 + ql, p_max + 1);
+        for (int kc = kq0; kc < kq1; kc += kStep) {
+            const int li = kc / kBlock - jb_first;
+            const int b0 = li < nb_group ? __builtin_amdgcn_readfirstlane(lds_bid[li]) : -1;
+            const int b1 = li + 1 < nb_group ? __builtin_amdgcn_readfirstlane(lds_bid[li + 1]) : -1;
+            StepRegs<D> r;
+            load_step<D>(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : g_zero_tile,
+                         b0 >= 0 ? vbase + (size_t)b0 * bstride : g_zero_tile,
+                         b1 >= 0 ? kbase + (size_t)b1 * bstride : g_zero_tile,
+                         b1 >= 0 ? vbase + (size_t)b1 * bstride : g_zero_tile, g, n);
+            mask_tail<D>(r, kc, ctx, g);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (16 * t < rows_total) step_update<D>(st[t], r, qop[t], kc, ri[t].prow, g, P.scale_log2);
+        }
+        // quarter states -> split state (wave 0, left fold in quarter order)
         if (wave > 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                lds_ml[buf][wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
+                lds_ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) lds_acc[buf][wave - 1][t][dt][lane] = st[t].acc[dt];
+                for (int dt = 0; dt < DT; ++dt) lds_acc[wave - 1][t][dt][lane] = st[t].acc[dt];
                 state_clear(st[t]);
             }
         }
@@ -426,11 +416,11 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
 #pragma unroll
                 for (int w = 0; w < 3; ++w) {
                     TileState<DT> o;
-                    const float2 ml = lds_ml[buf][w][t][lane];
+                    const float2 ml = lds_ml[w][t][lane];
                     o.m = ml.x;
                     o.l = ml.y;
 #pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds_acc[buf][w][t][dt][lane];
+                    for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds_acc[w][t][dt][lane];
                     fold_state(st[t], o);
                 }
                 if (whole) {
@@ -455,30 +445,7 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
                 state_clear(st[t]);
             }
         }
-    };
-
-    // The wave streams its quarters' chunks in pairs (A, B); quarters hold an
-    // even number of chunks except a last one cut by p_max, whose missing
-    // partner would be fully masked and is simply skipped. The chunk after
-    // each pair, possibly the first of the next split, is fetched into A
-    // while B is computed.
-    // Every fetch is unconditional (a missing chunk reads the zero tile), so
-    // the loop-carried registers are always fresh loads and never need a copy
-    // that would wait for loads in flight.
-    ChunkRegs<D> ca, cb;
-    fetch(ca, kq0_of(j0) <= p_max ? kq0_of(j0) : -1);
-    for (int j = j0; j < j1; ++j) {
-        const int kq0 = kq0_of(j), kq1 = kq1_of(j);
-        for (int kc = kq0; kc < kq1; kc += 2 * kChunk) {
-            const bool has_b = kc + kChunk < kq1;
-            fetch(cb, has_b ? kc + kChunk : -1);
-            compute(ca, kc);
-            int nxt = kc + 2 * kChunk;
-            if (nxt >= kq1) nxt = j + 1 < j1 && kq0_of(j + 1) <= p_max ? kq0_of(j + 1) : -1;
-            fetch(ca, nxt);
-            if (has_b) compute(cb, kc + kChunk);
-        }
-        split_end(j);
+        __syncthreads();  // the LDS slots are free again
     }
     if (whole && wave == 0) {
 #pragma unroll
@@ -595,8 +562,8 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     constexpr int DT = D / 16, KJ = D / 32;
     constexpr int TILE = kBlock * D;          // elements of one (block, head) tile
-    constexpr int CHUNK = 4 * TILE;           // K0, V0, K1, V1
-    constexpr int PER_THREAD = CHUNK / 256;   // elements staged by each thread
+    constexpr int STEP = 4 * TILE;            // K0, K1, V0, V1
+    constexpr int PER_THREAD = STEP / 256;    // elements staged by each thread
     constexpr int NV = PER_THREAD / 8;        // 16-byte pieces per thread
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
@@ -623,36 +590,26 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     const int wave_pmax =
         wave_row0 < rows_total ? ctx - q_len + min(wave_row0 + 15, rows_total - 1) / P.G : -1;
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][CHUNK];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][STEP];
     const size_t bstride = (size_t)P.Hkv * TILE;
     const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * TILE;
     const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * TILE;
     const int nblk_seq = (ctx + kBlock - 1) / kBlock;
     // this thread stages piece [part * TILE + off, + PER_THREAD) of every
-    // chunk; part = wave: 0 = K of block 0, 1 = V of block 0, 2 = K1, 3 = V1
-    const int part = wave;
-    const int off = lane * PER_THREAD;
-    const int tau = part >> 1;
-    const bool is_v = part & 1;
+    // chunk: parts 0, 1 are the K tiles of blocks 0, 1; parts 2, 3 their V
+    const int part = tid / (256 / 4);
+    const int off = (tid % (256 / 4)) * PER_THREAD;
+    const int blk = part & 1;
+    const bool is_v = part >= 2;
 
-    // block ids, 64 at a time, one per lane
-    int bid_base = -64, bid = -1;
-    auto block_id = [&](int jb) {
-        if (jb - bid_base >= 64) {
-            bid_base = jb & ~63;
-            const int x = bid_base + lane;
-            int b = -1;
-            if (x < nblk_seq && x < P.max_blocks_per_seq) {
-                const int y = P.bt[(size_t)s * P.max_blocks_per_seq + x];
-                b = (y >= 0 && y < P.num_blocks) ? y : -1;
-            }
-            bid = b;
-        }
-        return __builtin_amdgcn_readlane(bid, jb - bid_base);
-    };
     u32x4_t pre[NV];
     auto fetch = [&](int kc) {
-        const int b = block_id(kc / kBlock + tau);
+        const int jb = kc / kBlock + blk;
+        int b = -1;
+        if (jb < nblk_seq && jb < P.max_blocks_per_seq) {
+            const int x = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
+            b = (x >= 0 && x < P.num_blocks) ? x : -1;
+        }
         const uint16_t *src = b >= 0 ? (is_v ? vbase : kbase) + (size_t)b * bstride + off : g_zero_tile + off;
 #pragma unroll
         for (int v = 0; v < NV; ++v) pre[v] = *reinterpret_cast<const u32x4_t *>(src + 8 * v);
@@ -662,26 +619,26 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     state_clear(fin);
     state_clear(spl);
     state_clear(qtr);
-    const int nchunks = (p_max + kChunk) / kChunk;
+    const int nsteps = (p_max + kStep) / kStep;
     fetch(0);
-    for (int c = 0; c < nchunks; ++c) {
-        const int kc = c * kChunk;
+    for (int c = 0; c < nsteps; ++c) {
+        const int kc = c * kStep;
         uint16_t *buf = lds[c & 1];
 #pragma unroll
         for (int v = 0; v < NV; ++v) *reinterpret_cast<u32x4_t *>(buf + part * TILE + off + 8 * v) = pre[v];
-        if (c + 1 < nchunks) fetch(kc + kChunk);
+        if (c + 1 < nsteps) fetch(kc + kStep);
         __syncthreads();
         if (kc <= wave_pmax) {
-            ChunkRegs<D> cr;
-            load_chunk<D>(cr, buf, buf + TILE, buf + 2 * TILE, buf + 3 * TILE, g, n);
-            mask_tail<D>(cr, kc, ctx, g);
-            chunk_update<D>(qtr, cr.k, cr.v, qop, kc, ri.prow, g, P.scale_log2);
+            StepRegs<D> r;
+            load_step<D>(r, buf, buf + 2 * TILE, buf + TILE, buf + 3 * TILE, g, n);
+            mask_tail<D>(r, kc, ctx, g);
+            step_update<D>(qtr, r, qop, kc, ri.prow, g, P.scale_log2);
         }
-        // quarter and split boundaries fall on chunk boundaries
-        const int next = kc + kChunk;
+        // quarter and split boundaries fall on step boundaries
+        const int next = kc + kStep;
         const int sj = split_index(kc);
         const int sb = split_begin(sj), se = split_begin(sj + 1);
-        const bool last = c + 1 == nchunks;
+        const bool last = c + 1 == nsteps;
         if ((next - sb) % ((se - sb) >> 2) == 0 || last) {
             fold_state(spl, qtr);
             state_clear(qtr);
