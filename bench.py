@@ -79,6 +79,120 @@ def cpu_baseline(w, kv_bytes, rows, seconds):
                       f"seq-tokens/s {rows / med:.1f}"}
 
 
+def copy_calibrate(nbytes, reps):
+    """A plain device-to-device copy of nbytes, reps times: its HBM counters
+    per dispatch (read nbytes, write nbytes) scale the attention kernels'."""
+    import torch
+    n = (nbytes // 16) * 16
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0").view(torch.int32)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "reps": reps}), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries: kernel durations and HBM traffic per attention launch.
+# ---------------------------------------------------------------------------
+ATTN_SOURCE = os.path.join(ROOT, "paged_kv_attention_block_amd", "csrc", "attention.hip")
+ATTN_KERNELS = ("attn_parallel", "attn_fold", "attn_sequential", "attn_f32")
+
+
+def source_digest():
+    import hashlib
+    with open(ATTN_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").replace("pkv::", "").strip()
+
+
+def _counter_means(d, counter):
+    """Mean of `counter` per dispatch, per kernel, in the counter's unit."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        acc.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_profile(d, workload, commands):
+    """Write profiles/attention_<workload>.md from a directory holding the
+    rocprofv3 outputs: stats/ (--kernel-trace --stats), fetch/ and write/
+    (--pmc FETCH_SIZE, --pmc WRITE_SIZE over the bench), copy_fetch/ and
+    copy_write/ (the same counters over --copy-calibrate)."""
+    stats = _csv_rows(os.path.join(d, "stats"), "kernel_stats.csv")
+    copy = json.load(open(os.path.join(d, "copy.json")))
+    cbytes = copy["copy_bytes"]
+    cf = _counter_means(os.path.join(d, "copy_fetch"), "FETCH_SIZE")
+    cw = _counter_means(os.path.join(d, "copy_write"), "WRITE_SIZE")
+    ckey = max(cf, key=lambda k: cf[k][0])
+    f_scale = cbytes / (cf[ckey][0] * 1024.0)       # true bytes per counted byte
+    w_scale = cbytes / (cw[max(cw, key=lambda k: cw[k][0])][0] * 1024.0)
+    fetch = _counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(d, "write"), "WRITE_SIZE")
+    lines = [f"# Attention kernels, workload {workload}", "",
+             f"Source digest (sha256/16 of attention.hip): `{source_digest()}`", "",
+             "Commands (repository root, rocprofv3 output under gpurun_out/):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+        lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    lines += ["", "## HBM traffic per dispatch (rocprofv3 --pmc, one counter per run)", "",
+              f"Copy calibration: a {cbytes} B device copy (`{ckey}`) reads FETCH_SIZE "
+              f"{cf[ckey][0]:.0f} KiB and WRITE_SIZE {cw[max(cw, key=lambda k: cw[k][0])][0]:.0f} KiB per "
+              f"dispatch; scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write) turn counted KiB into bytes.",
+              "", "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled fetch MB | scaled write MB |",
+              "|---|---|---|---|---|---|"]
+    traffic = 0.0
+    for k in sorted(set(fetch) | set(write)):
+        if not k.startswith(ATTN_KERNELS) and "scatter" not in k:
+            continue
+        fk, fn = fetch.get(k, (0.0, 0))
+        wk, _ = write.get(k, (0.0, 0))
+        fb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
+        if k.startswith(ATTN_KERNELS):
+            traffic += fb + wb
+        lines.append(f"| {k} | {fn} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+    lines += ["", f"traffic_bytes_per_attention_call: {traffic:.0f}", ""]
+    out = os.path.join(ROOT, "profiles", f"attention_{workload}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(out)
+    return 0
+
+
+def committed_traffic(workload):
+    """HBM bytes per attention call from the committed summary, or None when
+    there is none or the kernels changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"attention_{workload}.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    if f"`{source_digest()}`" not in txt:
+        return None
+    for line in txt.splitlines():
+        if line.startswith("traffic_bytes_per_attention_call:"):
+            return float(line.split(":")[1])
+    return None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,7 +201,14 @@ def main(argv=None):
     ap.add_argument("--workload", default="mid_decode")
     ap.add_argument("--layers", type=int, default=0, help="pool copies per step (0: reach 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (for counter calibration) and exit")
+    ap.add_argument("--summarize", metavar="DIR", help="only write the profile summary from rocprofv3 output")
+    ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the summary")
     args = ap.parse_args(argv)
+
+    if args.summarize:
+        return summarize_profile(args.summarize, args.workload, args.commands)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
@@ -95,6 +216,9 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.copy_calibrate:
+        return copy_calibrate(args.copy_calibrate, max(1, args.steps))
 
     import synth
     import paged_kv_attention_block_amd as pk
@@ -219,7 +343,7 @@ def main(argv=None):
         "host_alloc_us_per_batch": round(alloc_us, 1),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name),
             "kernel": "paged_attention_forward (split + fold launches)",
             "alg_bytes_per_launch": att_alg_bytes,
         },

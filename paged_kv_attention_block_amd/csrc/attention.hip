@@ -30,6 +30,7 @@
 // every split, folds kept in registers) for prefill chunks.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -44,12 +45,10 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 16;
-constexpr int kChunk = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxHeadDim = 128;
 constexpr int kParRows = 32;   // rows per (sequence, KV head) the parallel shape takes
 constexpr int kSeqRows = 64;   // rows per workgroup in the sequential shape
-constexpr int kMaxGroupBlocks = 1024;  // block ids one parallel workgroup stages
 
 // ---------------------------------------------------------------------------
 // Fixed partition of absolute key positions: 256-key splits below 2048,
@@ -189,11 +188,10 @@ __device__ inline void load_step(StepRegs<D> &r, const uint16_t *kb0, const uint
 template <int D>
 __device__ inline void mask_tail(StepRegs<D> &r, int kc, int ctx, int g) {
     if (kc + kStep <= ctx) return;
-    const int k0 = kc + key_off(g);
+    const int nv = ctx - (kc + key_off(g));  // the lane's keys 0 .. nv-1 exist
     uint32_t m[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-        m[w] = (k0 + 2 * w < ctx ? 0x0000FFFFu : 0u) | (k0 + 2 * w + 1 < ctx ? 0xFFFF0000u : 0u);
+    for (int w = 0; w < 4; ++w) m[w] = (2 * w < nv ? 0x0000FFFFu : 0u) | (2 * w + 1 < nv ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
         r.v[dt].x &= m[0];
@@ -215,11 +213,11 @@ __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, 
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][j]), b, s1, 0, 0, 0);
     }
     float sc[8];
+    const int lim = prow - (kc + key_off(g));  // the row sees the lane's keys 0 .. lim
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int key = kc + key_off(g) + i;
-        sc[i] = key <= prow ? s0[i] * scale_log2 : -INFINITY;
-        sc[4 + i] = key + 4 <= prow ? s1[i] * scale_log2 : -INFINITY;
+        sc[i] = i <= lim ? s0[i] * scale_log2 : -INFINITY;
+        sc[4 + i] = i + 4 <= lim ? s1[i] * scale_log2 : -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -275,13 +273,15 @@ __device__ inline RowInfo row_info(int rho, int rows_total, int G, int ctx, int 
     return ri;
 }
 
+// Q of the lane's row; padding rows read the sequence's first row, which
+// they never use (no key is visible to them).
 template <int D>
 __device__ inline void load_q(u32x4_t (&qop)[D / 32], const AttnParams &P, int q0, const RowInfo &ri, int kvh, int g) {
     const uint16_t *qrow =
         reinterpret_cast<const uint16_t *>(P.q) + ((size_t)(q0 + ri.r) * P.Hq + kvh * P.G + ri.hl) * D;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j)
-        qop[j] = ri.prow >= 0 ? *reinterpret_cast<const u32x4_t *>(qrow + 32 * j + 8 * g) : u32x4_t{0, 0, 0, 0};
+        qop[j] = *reinterpret_cast<const u32x4_t *>(qrow + 32 * j + 8 * g);
 }
 
 __device__ inline float sink_log2(const AttnParams &P, int kvh, int hl) {
@@ -297,168 +297,158 @@ __device__ inline void store_out(const AttnParams &P, int q0, const RowInfo &ri,
 }
 
 // ---------------------------------------------------------------------------
-// Parallel shape: grid (sequence, KV head, key group); a group covers the
-// splits of keys [z * group_keys, (z + 1) * group_keys). 4 waves; wave w
-// streams quarter w of every split of the group, 64-key steps, for all NT
-// tiles (up to 16 NT rows per sequence and KV head). At each split end the
-// quarter states meet in LDS and wave 0 folds them. A group that holds every
-// split of its sequence folds the split states itself and writes the output;
-// otherwise each split state goes to the workspace for attn_fold.
-// Each step is loaded and then computed; the 2-3 resident workgroups per CU
-// keep enough loads in flight while others compute.
+// Parallel shape: one workgroup per (KV head, sequence, split), in a flat
+// grid whose fastest index is the KV head and whose split slots run the
+// 1024-key splits before the 256-key ones, so that short workgroups fill the
+// end. 4 waves; wave w streams quarter w of the split in 32-key steps for all
+// NT tiles (up to 16 NT rows per sequence and KV head). The quarter states
+// meet in LDS and wave 0 folds them in order. A sequence whose rows see one
+// split only is finished here; otherwise the split state goes to the
+// workspace and attn_fold folds the splits.
+// (A persistent grid claiming these items from counters, tried as a cure for
+// CUs the dispatcher leaves idle, ran slower on every workload measured.)
 // ---------------------------------------------------------------------------
+__device__ inline int split_of_slot(int z, int max_splits) {
+    if (max_splits <= kSplitsA) return z;
+    return z + kSplitsA < max_splits ? z + kSplitsA : z - (max_splits - kSplitsA);
+}
+
+// Waves per SIMD the parallel shape is built for: the register budget that
+// keeps enough workgroups resident to cover load latency. PF (prefetch of
+// the next step) doubles the step registers.
+constexpr int par_waves(int D, int NT, bool PF) {
+    return D == 64 ? (NT == 1 ? (PF ? 4 : 5) : 3) : (NT == 1 ? (PF ? 2 : 3) : 2);
+}
+
 template <int D, int NT>
-__global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_keys) {
+struct ParLds {
+    f32x4_t acc[3][NT][D / 16][64];
+    float2 ml[3][NT][64];
+};
+
+template <int D, int NT, bool PF>
+__global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnParams P) {
     constexpr int DT = D / 16, KJ = D / 32;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int g = lane >> 4, n = lane & 15;
-    const int s = blockIdx.x, kvh = blockIdx.y;
+    const int kvh = blockIdx.x % P.Hkv;
+    const int rest = blockIdx.x / P.Hkv;
+    const int s = rest % P.num_seqs;
+    const int j = split_of_slot(rest / P.num_seqs, P.max_splits);
 
-    int q0, q_len;
-    if (P.decode_only) {
-        q0 = s;
-        q_len = 1;
-    } else {
-        q0 = P.qsl[s];
-        q_len = P.qsl[s + 1] - q0;
-    }
+    // Loads that need nothing but the grid position go out together: the context
+    // length, the row offsets, and the block ids of the wave's quarter
+    // [kq0, kq0 + ql), lane i holding block kq0/16 + i.
+    // (no branches among them, so that none waits for another)
     const int ctx = P.ctx_lens[s];
-    const int rows_total = q_len * P.G;
-    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT) return;
-    const int p_max = ctx - q_len + (rows_total - 1) / P.G;
-    if (p_max < 0) return;
-    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
-    const int g_lo = blockIdx.z * group_keys;
-    if (g_lo > p_max) return;
-    const int j0 = split_index(g_lo);
-    const int j1 = min(split_index(min(g_lo + group_keys, p_max + 1) - 1) + 1, ns_item);
-    if (j0 >= j1) return;
-    const bool whole = j0 == 0 && j1 == ns_item;
+    const int qa = P.qsl[s], qb = P.qsl[s + 1];
+    const int ks = split_begin(j);
+    const int ql = (split_begin(j + 1) - ks) >> 2;
+    const int kq0 = ks + wave * ql;
+    const int jb = kq0 / kBlock + lane;
+    int bid = P.bt[(size_t)s * P.max_blocks_per_seq + min(jb, P.max_blocks_per_seq - 1)];
+    const int q0 = P.decode_only ? s : qa;
+    const int q_len = P.decode_only ? 1 : qb - qa;
 
+    const int rows_total = q_len * P.G;
+    const int p_max = ctx - q_len + (rows_total - 1) / P.G;
+    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
+    // (uniform over the workgroup)
+    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT && p_max >= 0 &&
+          j < ns_item))
+        return;
     RowInfo ri[NT];
     u32x4_t qop[NT][KJ];
     TileState<DT> st[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        ri[t] = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
-        load_q<D>(qop[t], P, q0, ri[t], kvh, g);
         state_clear(st[t]);
+        ri[t] = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
     }
-
-    // physical ids of every block the group reads, staged once in LDS
-    __shared__ int lds_bid[kMaxGroupBlocks];
-    const int jb_first = split_begin(j0) / kBlock;
-    const int nb_group =
-        min((min(split_begin(j1), p_max + 1) + kBlock - 1) / kBlock - jb_first, kMaxGroupBlocks);
     {
-        const int nblk_seq = (ctx + kBlock - 1) / kBlock;
-        const int32_t *bt_row = P.bt + (size_t)s * P.max_blocks_per_seq;
-        for (int i = tid; i < nb_group; i += 256) {
-            const int jb = jb_first + i;
-            int b = -1;
-            if (jb < nblk_seq && jb < P.max_blocks_per_seq) {
-                b = bt_row[jb];
-                b = (b >= 0 && b < P.num_blocks) ? b : -1;
-            }
-            lds_bid[i] = b;
-        }
-    }
-    __shared__ f32x4_t lds_acc[3][NT][DT][64];
-    __shared__ float2 lds_ml[3][NT][64];
-    // row state of a whole group, kept by wave 0 in LDS between splits
-    __shared__ f32x4_t fin_acc[NT][DT][64];
-    __shared__ float2 fin_ml[NT][64];
-    if (whole && wave == 0) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) fin_ml[t][lane] = make_float2(-INFINITY, 0.f);
-    }
-    __syncthreads();
-
-    const size_t tile = (size_t)kBlock * D;
-    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
-    const size_t bstride = (size_t)P.Hkv * tile;
-
-    for (int j = j0; j < j1; ++j) {
-        const int ks = split_begin(j);
-        const int ql = (split_begin(j + 1) - ks) >> 2;
-        const int kq0 = ks + wave * ql;
+        for (int t = 0; t < NT; ++t) load_q<D>(qop[t], P, q0, ri[t], kvh, g);
         const int kq1 = min(kq0 + ql, p_max + 1);
-        for (int kc = kq0; kc < kq1; kc += kStep) {
-            const int li = kc / kBlock - jb_first;
-            const int b0 = li < nb_group ? __builtin_amdgcn_readfirstlane(lds_bid[li]) : -1;
-            const int b1 = li + 1 < nb_group ? __builtin_amdgcn_readfirstlane(lds_bid[li + 1]) : -1;
-            StepRegs<D> r;
+        bid = (lane < ql / kBlock && jb < (ctx + kBlock - 1) / kBlock && jb < P.max_blocks_per_seq && bid >= 0 &&
+               bid < P.num_blocks)
+                  ? bid
+                  : -1;
+        const size_t tile = (size_t)kBlock * D;
+        const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
+        const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
+        const size_t bstride = (size_t)P.Hkv * tile;
+        // Step at key kc; lanes past the quarter's blocks hold -1, so a fetch
+        // one step past the end reads the zero tile.
+        auto fetch = [&](StepRegs<D> &r, int kc) {
+            const int li = (kc - kq0) / kBlock;
+            const int b0 = __builtin_amdgcn_readlane(bid, li);
+            const int b1 = __builtin_amdgcn_readlane(bid, li + 1);
             load_step<D>(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : g_zero_tile,
                          b0 >= 0 ? vbase + (size_t)b0 * bstride : g_zero_tile,
                          b1 >= 0 ? kbase + (size_t)b1 * bstride : g_zero_tile,
                          b1 >= 0 ? vbase + (size_t)b1 * bstride : g_zero_tile, g, n);
+        };
+        auto compute = [&](StepRegs<D> &r, int kc) {
             mask_tail<D>(r, kc, ctx, g);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 if (16 * t < rows_total) step_update<D>(st[t], r, qop[t], kc, ri[t].prow, g, P.scale_log2);
-        }
-        // quarter states -> split state (wave 0, left fold in quarter order)
-        if (wave > 0) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                lds_ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) lds_acc[wave - 1][t][dt][lane] = st[t].acc[dt];
-                state_clear(st[t]);
+        };
+        if constexpr (PF) {
+            // the next step's loads are in flight while this one is computed
+            StepRegs<D> cur;
+            fetch(cur, kq0);
+            for (int kc = kq0; kc < kq1; kc += kStep) {
+                StepRegs<D> nxt;
+                fetch(nxt, kc + kStep);
+                compute(cur, kc);
+                cur = nxt;
+            }
+        } else {
+            for (int kc = kq0; kc < kq1; kc += kStep) {
+                StepRegs<D> r;
+                fetch(r, kc);
+                compute(r, kc);
             }
         }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-#pragma unroll
-                for (int w = 0; w < 3; ++w) {
-                    TileState<DT> o;
-                    const float2 ml = lds_ml[w][t][lane];
-                    o.m = ml.x;
-                    o.l = ml.y;
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds_acc[w][t][dt][lane];
-                    fold_state(st[t], o);
-                }
-                if (whole) {
-                    TileState<DT> f;
-                    const float2 ml = fin_ml[t][lane];
-                    f.m = ml.x;
-                    f.l = ml.y;
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) f.acc[dt] = fin_acc[t][dt][lane];
-                    fold_state(f, st[t]);
-                    fin_ml[t][lane] = make_float2(f.m, f.l);
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) fin_acc[t][dt][lane] = f.acc[dt];
-                } else if (ri[t].prow >= 0) {
-                    const size_t base =
-                        ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + j;
-                    if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt)
-                        *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
-                }
-                state_clear(st[t]);
-            }
-        }
-        __syncthreads();  // the LDS slots are free again
     }
-    if (whole && wave == 0) {
+    __shared__ ParLds<D, NT> lds;
+    if (wave > 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            TileState<DT> f;
-            const float2 ml = fin_ml[t][lane];
-            f.m = ml.x;
-            f.l = ml.y;
+            lds.ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) f.acc[dt] = fin_acc[t][dt][lane];
+            for (int dt = 0; dt < DT; ++dt) lds.acc[wave - 1][t][dt][lane] = st[t].acc[dt];
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // quarter states -> split state (left fold in quarter order)
+    const bool whole = ns_item == 1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (ri[t].prow < 0) continue;
+#pragma unroll
+        for (int w = 0; w < 3; ++w) {
+            TileState<DT> o;
+            const float2 ml = lds.ml[w][t][lane];
+            o.m = ml.x;
+            o.l = ml.y;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds.acc[w][t][dt][lane];
+            fold_state(st[t], o);
+        }
+        if (whole) {
             f32x4_t o[DT];
-            finalize(f, sink_log2(P, kvh, ri[t].hl), o);
+            finalize(st[t], sink_log2(P, kvh, ri[t].hl), o);
             store_out<DT>(P, q0, ri[t], kvh, g, o);
+        } else {
+            const size_t base = ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + j;
+            if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
         }
     }
 }
@@ -469,7 +459,7 @@ __global__ __launch_bounds__(256) void attn_parallel(AttnParams P, int group_key
 // in d) and folds the split states left to right, then finalizes.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
-__global__ __launch_bounds__(256) void attn_fold(AttnParams P, int group_keys) {
+__global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
     constexpr int DT = D / 16, DW = DT / 4;
     static_assert(DT % 4 == 0, "head_dim must be a multiple of 64");
     const int tid = threadIdx.x;
@@ -489,31 +479,30 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P, int group_keys) {
     if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT || 16 * t >= rows_total) return;
     const int p_max = ctx - q_len + (rows_total - 1) / P.G;
     const int ns_item = min(num_splits(p_max + 1), P.max_splits);
-    if (p_max + 1 <= group_keys) return;  // one workgroup held every split and finished it
+    if (ns_item <= 1) return;  // attn_parallel finished the sequence
     const RowInfo r = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
     const size_t base0 = ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * P.max_splits;
     TileState<DW> acc;
     state_clear(acc);
-    auto read = [&](TileState<DW> &x, int j) {
-        const float2 ml = P.ws_ml[base0 + j];
-        x.m = ml.x;
-        x.l = ml.y;
+    // eight split states per round trip; slots past the last split stay empty
+    constexpr int U = 8;
+    for (int j = 0; j < ns_item; j += U) {
+        TileState<DW> x[U];
 #pragma unroll
-        for (int e = 0; e < DW; ++e)
-            x.acc[e] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j) * D + 16 * (wave + 4 * e) + 4 * g);
-    };
-    int j = 0;
-    for (; j + 4 <= ns_item; j += 4) {
-        TileState<DW> x[4];
+        for (int u = 0; u < U; ++u) {
+            state_clear(x[u]);
+            if (j + u < ns_item) {
+                const float2 ml = P.ws_ml[base0 + j + u];
+                x[u].m = ml.x;
+                x[u].l = ml.y;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) read(x[u], j + u);
+                for (int e = 0; e < DW; ++e)
+                    x[u].acc[e] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j + u) * D +
+                                                                      16 * (wave + 4 * e) + 4 * g);
+            }
+        }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) fold_state(acc, x[u]);
-    }
-    for (; j < ns_item; ++j) {
-        TileState<DW> x;
-        read(x, j);
-        fold_state(acc, x);
+        for (int u = 0; u < U; ++u) fold_state(acc, x[u]);
     }
     if (r.prow < 0) return;
     f32x4_t o[DW];
@@ -798,6 +787,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// Workspace: the split maxima and sums, then the split accumulators.
 struct WsLayout {
     size_t ml_bytes, acc_bytes;
     size_t total() const { return ml_bytes + acc_bytes; }
@@ -815,33 +805,25 @@ static WsLayout ws_layout(int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Keys per parallel workgroup: a power of two from 256 (1024 once contexts
-// pass 2048, so that groups never cut a 1024-key split), as small as gives
-// about kTargetGroups workgroups over the batch. Groups cover equal key
-// ranges, so workgroups carry equal loads. The choice only moves work between
-// workgroups; it never changes a result.
-constexpr int kTargetGroups = 1024;
+constexpr bool kPrefetch = false;
 
-static int keys_per_group(const AttnParams &P, int max_context_len) {
-    const int64_t units = (int64_t)P.num_seqs * P.Hkv;
-    int kg = max_context_len > kEdge ? kSplitB : kSplitA;
-    while (kg < kMaxGroupBlocks * kBlock && units * ((max_context_len + kg - 1) / kg) > kTargetGroups) kg *= 2;
-    return kg;
+template <int D, int NT, bool PF>
+static void launch_parallel(const AttnParams &P, hipStream_t st) {
+    const int64_t nwg = (int64_t)P.Hkv * P.num_seqs * P.max_splits;
+    hipLaunchKernelGGL((attn_parallel<D, NT, PF>), dim3((unsigned)nwg), dim3(256), 0, st, P);
 }
 
 template <int D>
 static void launch_bf16(const AttnParams &P, int max_q_len, int max_context_len, int total_rows,
                         hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
-    const int kg = keys_per_group(P, max_context_len);
-    const dim3 grid(P.num_seqs, P.Hkv, (max_context_len + kg - 1) / kg);
-    const bool fold = max_context_len > kg;
+    const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
-        hipLaunchKernelGGL((attn_parallel<D, 1>), grid, dim3(256), 0, st, P, kg);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P, kg);
+        launch_parallel<D, 1, kPrefetch>(P, st);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P);
     } else {
-        hipLaunchKernelGGL((attn_parallel<D, 2>), grid, dim3(256), 0, st, P, kg);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P, kg);
+        launch_parallel<D, 2, false>(P, st);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
@@ -898,6 +880,9 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: q, pools, out and workspace must be 16-byte aligned");
     const int max_splits = num_splits(max_context_len);
     if (max_splits > 65535) PKV_FAIL(KV_EINVAL, "paged_attention_forward: max_context_len too large");
+    if ((int64_t)num_kv_heads * num_seqs * max_splits * 256 > (int64_t)UINT32_MAX)
+        PKV_FAIL(KV_EINVAL, "paged_attention_forward: %d sequences x %d KV heads x %d splits exceed one launch",
+                 num_seqs, num_kv_heads, max_splits);
     const WsLayout w = ws_layout(total_q_rows, num_q_heads, head_dim, max_splits);
     if (workspace_bytes < w.total())
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: workspace of %zu bytes, need %zu", workspace_bytes,

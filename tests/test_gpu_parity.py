@@ -133,3 +133,28 @@ def test_empty_batch_is_noop(pk):
     out = pk.paged_attention_forward(q, kp, vp, bt, cl, qsl, 1, 64, 0.125)
     torch.cuda.synchronize()
     assert out.shape == (0, 4, 64)
+
+
+def test_workspace_reuse(pk):
+    """One workspace, left as the previous call wrote it, serves consecutive
+    calls of different shapes; each call matches the oracle (stale split
+    states must never leak into a later call)."""
+    import torch
+    from paged_kv_attention_block_amd.staging import stage
+    ws = None
+    for i, (S, lo, hi, q_len) in enumerate([(24, 3000, 9000, 1), (6, 200, 900, 1), (12, 2500, 7000, 8)]):
+        rng = np.random.default_rng(4242 + i)
+        ctxs = [int(x) for x in rng.integers(lo, hi, size=S)]
+        w = custom("bf16", 32, 8, 128, ctxs, [q_len] * S, seed=777 + i)
+        announce(f"workspace reuse call {i}: S={S} q_len={q_len} maxctx={max(ctxs)}")
+        st = stage(w)
+        need = pk.paged_attention_workspace_size(len(ctxs), w.total_rows, 32, 128, st.max_context_len)
+        if ws is None or ws.numel() < need:
+            ws = torch.full((max(need, 1 << 24),), 0x7F, dtype=torch.uint8, device="cuda")
+        out = pk.paged_attention_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens, st.qsl,
+                                         st.max_q_len, st.max_context_len, w.scale, out=st.out, workspace=ws)
+        torch.cuda.synchronize()
+        want = oracle_rows(w, list(range(w.total_rows)))
+        err = max_err(out.cpu().numpy(), want)
+        print(f"[case] workspace reuse call {i}: max abs err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
