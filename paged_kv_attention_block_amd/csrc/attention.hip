@@ -184,6 +184,33 @@ __device__ inline void load_step(StepRegs<D> &r, const uint16_t *kb0, const uint
         r.v[dt] = *reinterpret_cast<const u32x4_t *>(v + (16 * dt + n) * kBlock + 8 * (g & 1));
 }
 
+// The same operands from a step staged in LDS by attn_sequential, whose
+// layout permutes 16-byte pieces so that each group of 8 lanes reads 128
+// distinct bytes (no bank conflicts): in a K tile the 16 tokens of a channel
+// chunk sit in the order 0-3, 8-11, 4-7, 12-15 (lds_k_pos), and in a V tile
+// the two 16-byte halves of channel row r swap when bit 2 of r is set
+// (lds_v_half). K tiles of blocks 0, 1 at k0, k1; V tiles at v0, v1.
+__device__ inline int lds_k_pos(int token) { return (token & 3) + ((token >> 3) << 2) + (((token >> 2) & 1) << 3); }
+__device__ inline int lds_v_half(int row, int half) { return half ^ ((row >> 2) & 1); }
+
+template <int D>
+__device__ inline void load_step_lds(StepRegs<D> &r, const uint16_t *k0, const uint16_t *v0, const uint16_t *k1,
+                                     const uint16_t *v1, int g, int n) {
+    const uint16_t *k = n >= 8 ? k1 : k0;
+    const int pk = n & 7;  // lds_k_pos of the lane's tile-0 token; tile 1's follow 8 later
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+        r.k[0][j] = *reinterpret_cast<const u32x4_t *>(k + ((4 * j + g) * kBlock + pk) * 8);
+        r.k[1][j] = *reinterpret_cast<const u32x4_t *>(k + ((4 * j + g) * kBlock + pk + 8) * 8);
+    }
+    const uint16_t *v = (g >> 1) ? v1 : v0;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int row = 16 * dt + n;
+        r.v[dt] = *reinterpret_cast<const u32x4_t *>(v + row * kBlock + 8 * lds_v_half(row, g & 1));
+    }
+}
+
 // Zero V of keys at or past ctx, so that a zero weight never meets a NaN.
 template <int D>
 __device__ inline void mask_tail(StepRegs<D> &r, int kc, int ctx, int g) {
@@ -539,7 +566,9 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
         if (mask) {
             const int l = __ffsll((long long)mask) - 1;
             s_out = t0 + l;
-            rb_out = item - base - __shfl(excl, l, 64);
+            // row blocks in reverse: under the causal mask the last rows see
+            // the most keys, and the longest workgroups should start first
+            rb_out = __shfl(nb, l, 64) - 1 - (item - base - __shfl(excl, l, 64));
             return true;
         }
         base += __shfl(incl, 63, 64);
@@ -557,10 +586,10 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int g = lane >> 4, n = lane & 15;
-    const int kvh = blockIdx.y;
+    const int kvh = blockIdx.x % P.Hkv;  // heads fastest: each row block's heads start together
 
     int s = 0, rb = 0;
-    if (!find_seq_item(P.qsl, P.num_seqs, P.G, blockIdx.x, lane, s, rb)) return;
+    if (!find_seq_item(P.qsl, P.num_seqs, P.G, blockIdx.x / P.Hkv, lane, s, rb)) return;
     const int q0 = P.qsl[s];
     const int q_len = P.qsl[s + 1] - q0;
     const int ctx = P.ctx_lens[s];
@@ -580,46 +609,64 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
         wave_row0 < rows_total ? ctx - q_len + min(wave_row0 + 15, rows_total - 1) / P.G : -1;
 
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][STEP];
+    // the row state of each wave's tile, touched only at split ends
+    __shared__ f32x4_t fin_acc[4][DT][64];
+    __shared__ float2 fin_ml[4][64];
     const size_t bstride = (size_t)P.Hkv * TILE;
     const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * TILE;
     const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * TILE;
     const int nblk_seq = (ctx + kBlock - 1) / kBlock;
-    // this thread stages piece [part * TILE + off, + PER_THREAD) of every
-    // chunk: parts 0, 1 are the K tiles of blocks 0, 1; parts 2, 3 their V
-    const int part = tid / (256 / 4);
-    const int off = (tid % (256 / 4)) * PER_THREAD;
-    const int blk = part & 1;
-    const bool is_v = part >= 2;
+    // Wave w stages part w of every step: parts 0, 1 are the K tiles of the
+    // step's blocks 0, 1; parts 2, 3 their V. Thread piece: [off, off + PER_THREAD).
+    const int blk = wave & 1;
+    const bool is_v = wave >= 2;
+    const int off = lane * PER_THREAD;
 
-    u32x4_t pre[NV];
-    auto fetch = [&](int kc) {
-        const int jb = kc / kBlock + blk;
-        int b = -1;
-        if (jb < nblk_seq && jb < P.max_blocks_per_seq) {
-            const int x = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
-            b = (x >= 0 && x < P.num_blocks) ? x : -1;
-        }
+    // Block ids in register windows of 64 blocks (32 steps): lane i of bcur
+    // holds table entry 64 bw + i, bnxt the next window, loaded a window
+    // ahead. Entries are checked where they are used, so that no load waits.
+    const int32_t *bt_row = P.bt + (size_t)s * P.max_blocks_per_seq;
+    const int jb_max = min(nblk_seq, P.max_blocks_per_seq);  // blocks past it read the zero tile
+    auto load_bids = [&](int first) { return bt_row[min(first + lane, P.max_blocks_per_seq - 1)]; };
+    int bw = 0;  // window of the steps being computed
+    int bcur = load_bids(0), bnxt = load_bids(64);
+    // Step c's piece into dst; fetches run two steps ahead of the compute
+    // (so into the next window at a window's end) and past the last step
+    // they read the zero tile.
+    auto fetch = [&](u32x4_t (&dst)[NV], int c) {
+        const int jb = 2 * c + blk;
+        const int bc = __builtin_amdgcn_readlane(bcur, jb & 63);
+        const int bn = __builtin_amdgcn_readlane(bnxt, jb & 63);
+        int b = (c >> 5) == bw ? bc : bn;
+        b = (jb < jb_max && b >= 0 && b < P.num_blocks) ? b : -1;
         const uint16_t *src = b >= 0 ? (is_v ? vbase : kbase) + (size_t)b * bstride + off : g_zero_tile + off;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) pre[v] = *reinterpret_cast<const u32x4_t *>(src + 8 * v);
+        for (int v = 0; v < NV; ++v) dst[v] = *reinterpret_cast<const u32x4_t *>(src + 8 * v);
     };
 
-    TileState<DT> fin, spl, qtr;
-    state_clear(fin);
+    TileState<DT> spl, qtr;
     state_clear(spl);
     state_clear(qtr);
+    fin_ml[wave][lane] = make_float2(-INFINITY, 0.f);
     const int nsteps = (p_max + kStep) / kStep;
-    fetch(0);
-    for (int c = 0; c < nsteps; ++c) {
+    // One step: stage the piece fetched for step c, fetch step c + 2 into
+    // the same registers, then compute step c.
+    auto step = [&](int c, u32x4_t (&pre)[NV]) {
         const int kc = c * kStep;
         uint16_t *buf = lds[c & 1];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) *reinterpret_cast<u32x4_t *>(buf + part * TILE + off + 8 * v) = pre[v];
-        if (c + 1 < nsteps) fetch(kc + kStep);
+        for (int v = 0; v < NV; ++v) {
+            // piece (off + 8 v) / 8 of the tile: K chunk/token or V row/half
+            const int pc = (off >> 3) + v;
+            const int pos = is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
+                                 : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
+            *reinterpret_cast<u32x4_t *>(buf + wave * TILE + 8 * pos) = pre[v];
+        }
+        fetch(pre, c + 2);
         __syncthreads();
         if (kc <= wave_pmax) {
             StepRegs<D> r;
-            load_step<D>(r, buf, buf + 2 * TILE, buf + TILE, buf + 3 * TILE, g, n);
+            load_step_lds<D>(r, buf, buf + 2 * TILE, buf + TILE, buf + 3 * TILE, g, n);
             mask_tail<D>(r, kc, ctx, g);
             step_update<D>(qtr, r, qop, kc, ri.prow, g, P.scale_log2);
         }
@@ -633,10 +680,42 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
             state_clear(qtr);
         }
         if (next == se || last) {
+            TileState<DT> fin;
+            const float2 ml = fin_ml[wave][lane];
+            fin.m = ml.x;
+            fin.l = ml.y;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) fin.acc[dt] = fin_acc[wave][dt][lane];
             fold_state(fin, spl);
+            fin_ml[wave][lane] = make_float2(fin.m, fin.l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) fin_acc[wave][dt][lane] = fin.acc[dt];
             state_clear(spl);
         }
+    };
+    // two register stages, unrolled so that each stays in fixed registers
+    u32x4_t pre0[NV], pre1[NV];
+    fetch(pre0, 0);
+    fetch(pre1, 1);
+    // An even number of steps keeps the two stages in one order at the loop
+    // head; a step past the last computes nothing and folds empty states,
+    // which is exact.
+    const int nsteps2 = (nsteps + 1) & ~1;
+    for (int w0 = 0; w0 < nsteps2; w0 += 32, ++bw) {
+        const int wend = min(w0 + 32, nsteps2);
+        for (int c = w0; c < wend; c += 2) {
+            step(c, pre0);
+            step(c + 1, pre1);
+        }
+        bcur = bnxt;
+        bnxt = load_bids(64 * (bw + 2));
     }
+    TileState<DT> fin;
+    const float2 ml = fin_ml[wave][lane];
+    fin.m = ml.x;
+    fin.l = ml.y;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) fin.acc[dt] = fin_acc[wave][dt][lane];
     f32x4_t o[DT];
     finalize(fin, sink_log2(P, kvh, ri.hl), o);
     store_out<DT>(P, q0, ri, kvh, g, o);
@@ -827,7 +906,7 @@ static void launch_bf16(const AttnParams &P, int max_q_len, int max_context_len,
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
-        hipLaunchKernelGGL((attn_sequential<D>), dim3((unsigned)items, P.Hkv), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((attn_sequential<D>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
     }
 }
 

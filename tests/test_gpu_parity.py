@@ -99,6 +99,14 @@ def test_prefill_from_zero_full_causal(pk):
     check_workload(pk, w)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_chunk_on_long_context(pk, D):
+    """Prefill chunks whose rows see thousands of keys: the prefill shape walks
+    many 32-step windows of block ids, across both split sizes."""
+    w = custom("bf16", 16, 4, D, [5000, 2300, 700], [200, 33, 9], seed=80 + D, sinks=True)
+    check_workload(pk, w)
+
+
 def test_long_context(pk):
     w = custom("bf16", 16, 2, 128, [20000, 9000], [1, 4], seed=79, sinks=True)
     check_workload(pk, w)
