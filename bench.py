@@ -2,8 +2,10 @@
 on one MI355X.
 
 One step = one decode step through L attention layers: for every layer, the
-step's new K/V rows are scatter-written into that layer's paged pool
-(kv_append_scatter) and one batched paged_attention_forward runs over it.
+step's new K/V rows are scatter-written into that layer's paged pool and one
+batched attention runs over it, both through paged_attention_append_forward
+(equal to kv_append_scatter followed by paged_attention_forward; decode batches
+take the new tokens inside the attention launches).
 Layers are distinct pool copies sharing one set of block tables, so a step
 touches more memory than the 256 MB last-level cache holds and the reported
 bandwidth is HBM bandwidth. Block allocation (kv_pool_alloc) happens once per
@@ -249,10 +251,10 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     def layer_call(l):
-        pk.kv_append_scatter(st.k_step, st.v_step, st.step_slots, st.k_pools[l], st.v_pools[l])
-        pk.paged_attention_forward(st.q, st.k_pools[l], st.v_pools[l], st.tables, st.context_lens, st.qsl,
-                                   st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
-                                   workspace=st.workspace)
+        pk.paged_attention_append_forward(st.q, st.k_step, st.v_step, st.step_slots, st.k_pools[l],
+                                          st.v_pools[l], st.tables, st.context_lens, st.qsl, st.max_q_len,
+                                          st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
+                                          workspace=st.workspace)
 
     def step():
         for l in range(layers):

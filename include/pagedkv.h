@@ -222,6 +222,31 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
                             const float *sinks, float *out, void *workspace,
                             size_t workspace_bytes, void *hip_stream);
 
+/*
+ * One decode step's append and attention in one call ("原生分页注意力", its
+ * batched-forward paragraph: the batched forward paired with a paged K/V
+ * scatter-write). Row i's own token is the new token of its sequence: it sits
+ * at position context_lens[s] - q_len + r (so context_lens already counts it),
+ * its K/V are k_new[i], v_new[i] ([total_q_rows][num_kv_heads][head_dim],
+ * type `dtype`) and its pool slot is slot_mapping[i] (-1: the token is already
+ * resident, write nothing). The call equals kv_append_scatter(k_new, v_new,
+ * slot_mapping, total_q_rows, ...) followed by paged_attention_forward(...) on
+ * the same stream, bit for bit in `out` and in the pools. Other arguments,
+ * ownership and errors are those of paged_attention_forward; k_pool and v_pool
+ * are written. A bf16 batch of single-row sequences (decode) writes and uses
+ * the new tokens inside the attention launch; any other batch is scattered
+ * first.
+ */
+int paged_attention_append_forward(const void *q, const void *k_new, const void *v_new,
+                                   const int32_t *slot_mapping, void *k_pool, void *v_pool, int32_t dtype,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                   int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                   const float *sinks, float *out, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

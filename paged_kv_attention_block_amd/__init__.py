@@ -22,7 +22,7 @@ __all__ = [
     "KV_F32", "KV_BF16", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
     "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_workspace_size",
-    "paged_attention_forward", "empty_pools", "BLOCK_SIZE",
+    "paged_attention_forward", "paged_attention_append_forward", "empty_pools", "BLOCK_SIZE",
 ]
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
@@ -55,8 +55,12 @@ _lib.paged_attention_workspace_size.restype = _sz
 _lib.paged_attention_forward.argtypes = [
     _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
     _f32, _p, _p, _p, _sz, _p]
+_lib.paged_attention_append_forward.argtypes = [
+    _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    _f32, _p, _p, _p, _sz, _p]
 for _name in ("kv_pool_create", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
-              "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_forward"):
+              "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_forward",
+              "paged_attention_append_forward"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -213,10 +217,8 @@ def paged_attention_workspace_size(num_seqs: int, total_q_rows: int, num_q_heads
                                                    max_context_len))
 
 
-def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
-                            max_context_len: int, scale: float, sinks=None, out=None, workspace=None,
-                            stream=None):
-    """out [total_rows, Hq, D] float32 = attention of q over the paged cache (see pagedkv.h)."""
+def _forward_args(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out,
+                  workspace):
     torch = _torch()
     _need(q, "q", ndim=3)
     _need(k_pool, "k_pool", dtype=q.dtype, ndim=5)
@@ -243,10 +245,42 @@ def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
+    return S, total, hq, hkv, d, nb, out, workspace, ws_bytes
+
+
+def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
+                            max_context_len: int, scale: float, sinks=None, out=None, workspace=None,
+                            stream=None):
+    """out [total_rows, Hq, D] float32 = attention of q over the paged cache (see pagedkv.h)."""
+    S, total, hq, hkv, d, nb, out, workspace, ws_bytes = _forward_args(
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
     _check(_lib.paged_attention_forward(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), _dtype_code(q), block_tables.data_ptr(),
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len,
         max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
+        _stream_ptr(stream)))
+    return out
+
+
+def paged_attention_append_forward(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_tables, context_lens,
+                                   query_start_loc, max_q_len: int, max_context_len: int, scale: float,
+                                   sinks=None, out=None, workspace=None, stream=None):
+    """kv_append_scatter of each row's own token (k_new, v_new [total_rows, Hkv, D], slot_mapping
+    [total_rows]) and paged_attention_forward in one call (see pagedkv.h); returns out."""
+    torch = _torch()
+    S, total, hq, hkv, d, nb, out, workspace, ws_bytes = _forward_args(
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
+    _need(k_new, "k_new", dtype=q.dtype, ndim=3)
+    _need(v_new, "v_new", dtype=q.dtype, ndim=3)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    if tuple(k_new.shape) != (total, hkv, d) or tuple(v_new.shape) != (total, hkv, d) or \
+            slot_mapping.shape[0] != total:
+        raise KVError(KV_EINVAL, "k_new, v_new and slot_mapping must hold one row per query row")
+    _check(_lib.paged_attention_append_forward(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_pool.data_ptr(),
+        v_pool.data_ptr(), _dtype_code(q), block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        query_start_loc.data_ptr(), S, total, max_q_len, max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
         _stream_ptr(stream)))
     return out

@@ -79,6 +79,12 @@ struct AttnParams {
     int32_t num_seqs, total_rows, Hq, Hkv, G, max_blocks_per_seq, num_blocks, max_splits;
     int32_t decode_only;  // every sequence has q_len == 1 (rows packed in sequence order)
     float scale_log2;
+    // Appending decode step (paged_attention_append_forward), else all null:
+    // row s's own token sits at position ctx - 1; its K/V rows, and the pool
+    // slot the split holding that position writes them to.
+    const uint16_t *k_new, *v_new;
+    const int32_t *slots;
+    uint16_t *kp_w, *vp_w;
 };
 
 // A zero (block, head) tile: loads of blocks past the end of a sequence read it.
@@ -228,6 +234,40 @@ __device__ inline void mask_tail(StepRegs<D> &r, int kc, int ctx, int g) {
     }
 }
 
+// Put the new token's K/V (held in registers: knew[j] = channels
+// 32j+8g..+7, vnew[dt] = channel 16dt+n) into the operands of the step at kc
+// that holds its position pn, in place of what the pool held there. Only
+// fixed register indices and per-lane selects: a register array indexed by a
+// run-time value would live in scratch memory.
+template <int D>
+__device__ inline void patch_new_key(StepRegs<D> &r, const u32x4_t (&knew)[D / 32], const uint32_t (&vnew)[D / 16],
+                                     int kc, int pn, int g, int n) {
+    const int hb = (pn - kc) >> 4, t = pn & (kBlock - 1);
+    const int tk = 8 * ((n >> 2) & 1) + (n & 3);
+    const bool kblk = (n >= 8) == (hb == 1);
+    const bool k0 = kblk && tk == t, k1 = kblk && tk + 4 == t;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+        r.k[0][j] = k0 ? knew[j] : r.k[0][j];
+        r.k[1][j] = k1 ? knew[j] : r.k[1][j];
+    }
+    // V^T: the lane's eight keys are tokens 8(g&1)..+7 of block g>>1; the new
+    // key is element e of them, the low or high half of 32-bit word e / 2
+    const bool vm = (g >> 1) == hb && (t >> 3) == (g & 1);
+    const int e = t & 7;
+    const bool w0 = vm && (e >> 1) == 0, w1 = vm && (e >> 1) == 1, w2 = vm && (e >> 1) == 2, w3 = vm && (e >> 1) == 3;
+    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    const int sh = (e & 1) ? 16 : 0;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const uint32_t ins = vnew[dt] << sh;
+        r.v[dt].x = w0 ? ((r.v[dt].x & keep) | ins) : r.v[dt].x;
+        r.v[dt].y = w1 ? ((r.v[dt].y & keep) | ins) : r.v[dt].y;
+        r.v[dt].z = w2 ? ((r.v[dt].z & keep) | ins) : r.v[dt].z;
+        r.v[dt].w = w3 ? ((r.v[dt].w & keep) | ins) : r.v[dt].w;
+    }
+}
+
 template <int D>
 __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
                                    int prow, int g, float scale_log2) {
@@ -341,10 +381,11 @@ __device__ inline int split_of_slot(int z, int max_splits) {
 }
 
 // Waves per SIMD the parallel shape is built for: the register budget that
-// keeps enough workgroups resident to cover load latency. PF (prefetch of
-// the next step) doubles the step registers.
+// keeps enough workgroups resident to cover load latency. The two-stage
+// variant (PF) serves grids that leave CUs free, where occupancy does not
+// matter, and takes the whole register file.
 constexpr int par_waves(int D, int NT, bool PF) {
-    return D == 64 ? (NT == 1 ? (PF ? 4 : 5) : 3) : (NT == 1 ? (PF ? 2 : 3) : 2);
+    return PF ? 2 : D == 64 ? (NT == 1 ? 5 : 3) : (NT == 1 ? 3 : 2);
 }
 
 template <int D, int NT>
@@ -353,7 +394,7 @@ struct ParLds {
     float2 ml[3][NT][64];
 };
 
-template <int D, int NT, bool PF>
+template <int D, int NT, bool PF, bool APPEND>
 __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnParams P) {
     constexpr int DT = D / 16, KJ = D / 32;
     const int tid = threadIdx.x;
@@ -382,9 +423,21 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     const int p_max = ctx - q_len + (rows_total - 1) / P.G;
     const int ns_item = min(num_splits(p_max + 1), P.max_splits);
     // (uniform over the workgroup)
-    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT && p_max >= 0 &&
-          j < ns_item))
+    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT && p_max >= 0)) return;
+    if (j >= ns_item) {
+        // No row sees this split: its slot holds an empty state, so that the
+        // fold reads every slot without first learning the context length.
+        if (wave == 0) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int rho = 16 * t + n;
+                if (g != 0 || rho >= rows_total) continue;
+                const int r = rho / P.G, hl = rho - r * P.G;
+                P.ws_ml[((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * P.max_splits + j] = make_float2(-INFINITY, 0.f);
+            }
+        }
         return;
+    }
     RowInfo ri[NT];
     u32x4_t qop[NT][KJ];
     TileState<DT> st[NT];
@@ -401,6 +454,30 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                bid < P.num_blocks)
                   ? bid
                   : -1;
+        // appending decode step: the wave whose quarter holds the new key
+        const int pn = ctx - 1;
+        const bool fused = APPEND && kq0 <= pn && pn < kq1;
+        u32x4_t knew[KJ];
+        uint32_t vnew[DT];
+        if (APPEND && fused) {
+            const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
+#pragma unroll
+            for (int jj = 0; jj < KJ; ++jj)
+                knew[jj] = *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + (4 * jj + g) * 8);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) vnew[dt] = P.v_new[rowoff + 16 * dt + n];
+            // and writes it to its pool slot, as the scatter-write would
+            const int slot = P.slots[s];
+            if (slot >= 0 && slot < P.num_blocks * kBlock) {
+                const int b = slot / kBlock, o = slot % kBlock;
+                const size_t tb = ((size_t)b * P.Hkv + kvh) * D;  // element offset of the (block, head) tile
+                if (lane < D / 8)
+                    *reinterpret_cast<u32x4_t *>(P.kp_w + tb * kBlock + ((size_t)lane * kBlock + o) * 8) =
+                        *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + lane * 8);
+#pragma unroll
+                for (int c = lane; c < D; c += 64) P.vp_w[tb * kBlock + (size_t)c * kBlock + o] = P.v_new[rowoff + c];
+            }
+        }
         const size_t tile = (size_t)kBlock * D;
         const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
         const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
@@ -417,20 +494,28 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                          b1 >= 0 ? vbase + (size_t)b1 * bstride : g_zero_tile, g, n);
         };
         auto compute = [&](StepRegs<D> &r, int kc) {
+            if constexpr (APPEND)
+                if (fused && kc <= pn && pn < kc + kStep) patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
             mask_tail<D>(r, kc, ctx, g);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
                 if (16 * t < rows_total) step_update<D>(st[t], r, qop[t], kc, ri[t].prow, g, P.scale_log2);
         };
         if constexpr (PF) {
-            // the next step's loads are in flight while this one is computed
-            StepRegs<D> cur;
-            fetch(cur, kq0);
-            for (int kc = kq0; kc < kq1; kc += kStep) {
-                StepRegs<D> nxt;
-                fetch(nxt, kc + kStep);
-                compute(cur, kc);
-                cur = nxt;
+            // Two register stages, each refilled as soon as it is consumed,
+            // so that two steps are in flight; unrolled so that each stage
+            // keeps fixed registers (a copy between stages would wait for the
+            // loads it copies).
+            StepRegs<D> r0, r1;
+            fetch(r0, kq0);
+            if (kq0 + kStep < kq1) fetch(r1, kq0 + kStep);
+            for (int kc = kq0; kc < kq1; kc += 2 * kStep) {
+                compute(r0, kc);
+                if (kc + 2 * kStep < kq1) fetch(r0, kc + 2 * kStep);
+                if (kc + kStep < kq1) {
+                    compute(r1, kc + kStep);
+                    if (kc + 3 * kStep < kq1) fetch(r1, kc + 3 * kStep);
+                }
             }
         } else {
             for (int kc = kq0; kc < kq1; kc += kStep) {
@@ -451,8 +536,9 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     }
     __syncthreads();
     if (wave != 0) return;
-    // quarter states -> split state (left fold in quarter order)
-    const bool whole = ns_item == 1;
+    // quarter states -> split state (left fold in quarter order); with one
+    // split slot there is no fold launch and the rows are finished here
+    const bool whole = P.max_splits == 1;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         if (ri[t].prow < 0) continue;
@@ -501,24 +587,22 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
         q0 = P.qsl[s];
         q_len = P.qsl[s + 1] - q0;
     }
-    const int ctx = P.ctx_lens[s];
     const int rows_total = q_len * P.G;
     if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT || 16 * t >= rows_total) return;
-    const int p_max = ctx - q_len + (rows_total - 1) / P.G;
-    const int ns_item = min(num_splits(p_max + 1), P.max_splits);
-    if (ns_item <= 1) return;  // attn_parallel finished the sequence
-    const RowInfo r = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
-    const size_t base0 = ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * P.max_splits;
+    // every slot holds a state (empty past the row's keys): no context length needed
+    const int rho = min(16 * t + n, rows_total - 1);  // padding lanes repeat a real row and store nothing
+    const int r = rho / P.G, hl = rho - r * P.G;
+    const size_t base0 = ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * P.max_splits;
     TileState<DW> acc;
     state_clear(acc);
-    // eight split states per round trip; slots past the last split stay empty
+    // eight split states per round trip
     constexpr int U = 8;
-    for (int j = 0; j < ns_item; j += U) {
+    for (int j = 0; j < P.max_splits; j += U) {
         TileState<DW> x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             state_clear(x[u]);
-            if (j + u < ns_item) {
+            if (j + u < P.max_splits) {
                 const float2 ml = P.ws_ml[base0 + j + u];
                 x[u].m = ml.x;
                 x[u].l = ml.y;
@@ -531,10 +615,10 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
 #pragma unroll
         for (int u = 0; u < U; ++u) fold_state(acc, x[u]);
     }
-    if (r.prow < 0) return;
+    if (16 * t + n >= rows_total) return;
     f32x4_t o[DW];
-    finalize(acc, sink_log2(P, kvh, r.hl), o);
-    float *dst = P.out + ((size_t)(q0 + r.r) * P.Hq + kvh * P.G + r.hl) * D + 4 * g;
+    finalize(acc, sink_log2(P, kvh, hl), o);
+    float *dst = P.out + ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * D + 4 * g;
 #pragma unroll
     for (int e = 0; e < DW; ++e) *reinterpret_cast<f32x4_t *>(dst + 16 * (wave + 4 * e)) = o[e];
 }
@@ -884,12 +968,38 @@ static WsLayout ws_layout(int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr bool kPrefetch = false;
+// A grid that leaves CUs free takes the two-stage variant: per-workgroup
+// latency then decides the time, and occupancy does not matter.
+template <int D, int NT>
+static void launch_parallel(const AttnParams &P, hipStream_t st);
 
-template <int D, int NT, bool PF>
-static void launch_parallel(const AttnParams &P, hipStream_t st) {
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64 && cache[dev] > 0) return cache[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    if (dev < 64) cache[dev] = cus;
+    return cus;
+}
+
+template <int D, int NT, bool APPEND>
+static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
     const int64_t nwg = (int64_t)P.Hkv * P.num_seqs * P.max_splits;
-    hipLaunchKernelGGL((attn_parallel<D, NT, PF>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+    if constexpr (NT == 1) {
+        if (nwg <= device_cus()) {
+            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+}
+
+template <int D, int NT>
+static void launch_parallel(const AttnParams &P, hipStream_t st) {
+    if (P.k_new) launch_parallel_as<D, NT, true>(P, st);
+    else launch_parallel_as<D, NT, false>(P, st);
 }
 
 template <int D>
@@ -898,10 +1008,10 @@ static void launch_bf16(const AttnParams &P, int max_q_len, int max_context_len,
     const int rows_per_seq = max_q_len * P.G;
     const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
-        launch_parallel<D, 1, kPrefetch>(P, st);
+        launch_parallel<D, 1>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P);
     } else {
-        launch_parallel<D, 2, false>(P, st);
+        launch_parallel<D, 2>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
@@ -921,15 +1031,22 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows, in
     return pkv::ws_layout(total_q_rows, num_q_heads, head_dim, pkv::num_splits(max_context_len)).total();
 }
 
-int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
-                            const int32_t *block_tables, int32_t max_blocks_per_seq,
-                            const int32_t *context_lens, const int32_t *query_start_loc,
-                            int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
-                            int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                            const float *sinks, float *out, void *workspace, size_t workspace_bytes,
-                            void *hip_stream) {
-    using namespace pkv;
+}  // extern "C"
+
+namespace pkv {
+
+struct AppendArgs {
+    const void *k_new, *v_new;
+    const int32_t *slots;
+};
+
+static int forward_impl(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                        const int32_t *block_tables, int32_t max_blocks_per_seq,
+                        const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
+                        int32_t total_q_rows, int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                        float scale, const float *sinks, float *out, void *workspace, size_t workspace_bytes,
+                        void *hip_stream, const AppendArgs *app) {
     if (dtype != KV_BF16 && dtype != KV_F32)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: dtype %d not supported", dtype);
     if (head_dim != 64 && head_dim != 128)
@@ -988,7 +1105,29 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     P.max_splits = max_splits;
     P.decode_only = max_q_len == 1 && total_q_rows == num_seqs;
     P.scale_log2 = scale * kLog2e;
+    P.k_new = P.v_new = nullptr;
+    P.slots = nullptr;
+    P.kp_w = P.vp_w = nullptr;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+
+    if (app) {
+        // One new token per row, at the row's own position. A decode batch in
+        // the parallel shape takes them inside the attention launch; any other
+        // batch is scattered first, as two calls would.
+        const bool fused = dtype == KV_BF16 && P.decode_only && max_q_len * P.G <= kParRows;
+        if (fused) {
+            P.k_new = static_cast<const uint16_t *>(app->k_new);
+            P.v_new = static_cast<const uint16_t *>(app->v_new);
+            P.slots = app->slots;
+            P.kp_w = static_cast<uint16_t *>(const_cast<void *>(k_pool));
+            P.vp_w = static_cast<uint16_t *>(const_cast<void *>(v_pool));
+        } else {
+            const int rc = kv_append_scatter(app->k_new, app->v_new, app->slots, total_q_rows,
+                                             const_cast<void *>(k_pool), const_cast<void *>(v_pool), num_blocks,
+                                             num_kv_heads, head_dim, block_size, dtype, hip_stream);
+            if (rc != KV_OK) return rc;
+        }
+    }
 
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
@@ -1003,6 +1142,48 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     if (e != hipSuccess)
         PKV_FAIL(KV_EDEVICE, "paged_attention_forward: launch failed: %s", hipGetErrorString(e));
     return KV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                            const int32_t *block_tables, int32_t max_blocks_per_seq,
+                            const int32_t *context_lens, const int32_t *query_start_loc,
+                            int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                            int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                            const float *sinks, float *out, void *workspace, size_t workspace_bytes,
+                            void *hip_stream) {
+    return pkv::forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens,
+                             query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, workspace,
+                             workspace_bytes, hip_stream, nullptr);
+}
+
+int paged_attention_append_forward(const void *q, const void *k_new, const void *v_new,
+                                   const int32_t *slot_mapping, void *k_pool, void *v_pool, int32_t dtype,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                   int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                   const float *sinks, float *out, void *workspace, size_t workspace_bytes,
+                                   void *hip_stream) {
+    using namespace pkv;
+    if (num_seqs > 0 && total_q_rows > 0) {
+        if (!k_new || !v_new || !slot_mapping)
+            PKV_FAIL(KV_EINVAL, "paged_attention_append_forward: k_new, v_new and slot_mapping are required");
+        if (!aligned16(k_new) || !aligned16(v_new))
+            PKV_FAIL(KV_EINVAL, "paged_attention_append_forward: k_new and v_new must be 16-byte aligned");
+        if ((int64_t)num_blocks * kBlock > INT32_MAX)
+            PKV_FAIL(KV_EINVAL, "paged_attention_append_forward: pool too large");
+    }
+    const AppendArgs app{k_new, v_new, slot_mapping};
+    return forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens, query_start_loc,
+                        num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                        block_size, num_blocks, scale, sinks, out, workspace, workspace_bytes, hip_stream, &app);
 }
 
 int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_mapping, int32_t n,

@@ -74,6 +74,30 @@ def test_forward_rejects_bad_host_arguments(pk):
     assert call(rows=0) == pk.KV_OK
 
 
+def test_append_forward_rejects_bad_host_arguments(pk):
+    lib = _lib(pk)
+    f = ctypes.c_void_p(256)
+    ws = pk.paged_attention_workspace_size(4, 4, 32, 128, 800)
+
+    def call(**kw):
+        a = dict(q=f, kn=f, vn=f, slots=f, k=f, v=f, dtype=pk.KV_BF16, bt=f, mb=64, ctx=f, qsl=f, S=4, rows=4,
+                 mq=1, mctx=800, hq=32, hkv=8, d=128, bs=16, nb=1000, scale=0.088, sinks=None, out=f, ws=f,
+                 wsb=ws, st=None)
+        a.update(kw)
+        return lib.paged_attention_append_forward(
+            a["q"], a["kn"], a["vn"], a["slots"], a["k"], a["v"], a["dtype"], a["bt"], a["mb"], a["ctx"],
+            a["qsl"], a["S"], a["rows"], a["mq"], a["mctx"], a["hq"], a["hkv"], a["d"], a["bs"], a["nb"],
+            a["scale"], a["sinks"], a["out"], a["ws"], a["wsb"], a["st"])
+
+    assert call(kn=None) == pk.KV_EINVAL
+    assert "k_new" in pk.kv_last_error()
+    assert call(slots=None) == pk.KV_EINVAL
+    assert call(vn=ctypes.c_void_p(260)) == pk.KV_EINVAL   # misaligned
+    assert call(hq=30) == pk.KV_EINVAL                      # the forward's own checks still apply
+    assert call(wsb=16) == pk.KV_EINVAL
+    assert call(S=0) == pk.KV_OK
+
+
 def test_scatter_rejects_bad_host_arguments(pk):
     lib = _lib(pk)
     f = ctypes.c_void_p(256)
