@@ -78,6 +78,7 @@ struct AttnParams {
     float *out;         // [rows][Hq][D]
     int32_t num_seqs, total_rows, Hq, Hkv, G, max_blocks_per_seq, num_blocks, max_splits;
     int32_t decode_only;  // every sequence has q_len == 1 (rows packed in sequence order)
+    int32_t seq_stride;   // sequence slots per split slot in the parallel grid (>= num_seqs)
     float scale_log2;
     // Appending decode step (paged_attention_append_forward), else all null:
     // row s's own token sits at position ctx - 1; its K/V rows, and the pool
@@ -402,8 +403,9 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     const int g = lane >> 4, n = lane & 15;
     const int kvh = blockIdx.x % P.Hkv;
     const int rest = blockIdx.x / P.Hkv;
-    const int s = rest % P.num_seqs;
-    const int j = split_of_slot(rest / P.num_seqs, P.max_splits);
+    const int s = rest % P.seq_stride;
+    const int j = split_of_slot(rest / P.seq_stride, P.max_splits);
+    if (s >= P.num_seqs) return;  // padding slot
 
     // Loads that need nothing but the grid position go out together: the context
     // length, the row offsets, and the block ids of the wave's quarter
@@ -986,7 +988,7 @@ static int device_cus() {
 
 template <int D, int NT, bool APPEND>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
-    const int64_t nwg = (int64_t)P.Hkv * P.num_seqs * P.max_splits;
+    const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.max_splits;
     if constexpr (NT == 1) {
         if (nwg <= device_cus()) {
             hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND>), dim3((unsigned)nwg), dim3(256), 0, st, P);
@@ -1076,7 +1078,7 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: q, pools, out and workspace must be 16-byte aligned");
     const int max_splits = num_splits(max_context_len);
     if (max_splits > 65535) PKV_FAIL(KV_EINVAL, "paged_attention_forward: max_context_len too large");
-    if ((int64_t)num_kv_heads * num_seqs * max_splits * 256 > (int64_t)UINT32_MAX)
+    if ((int64_t)num_kv_heads * (num_seqs + 3) * max_splits * 256 > (int64_t)UINT32_MAX)
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: %d sequences x %d KV heads x %d splits exceed one launch",
                  num_seqs, num_kv_heads, max_splits);
     const WsLayout w = ws_layout(total_q_rows, num_q_heads, head_dim, max_splits);
@@ -1104,6 +1106,12 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     P.num_blocks = num_blocks;
     P.max_splits = max_splits;
     P.decode_only = max_q_len == 1 && total_q_rows == num_seqs;
+    // The dispatcher deals workgroups to the shader engines of a die in turn,
+    // by count, not by work. A sequence stride of 1 mod 4 (padding slots exit
+    // at once) moves each sequence to the next engine at every split slot,
+    // so that no engine gets all the splits of the same long sequences.
+    P.seq_stride = num_seqs;
+    if ((int64_t)num_kv_heads * num_seqs * max_splits > device_cus()) P.seq_stride += (5 - num_seqs % 4) % 4;
     P.scale_log2 = scale * kLog2e;
     P.k_new = P.v_new = nullptr;
     P.slots = nullptr;
