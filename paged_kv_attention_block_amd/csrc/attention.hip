@@ -922,31 +922,80 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// Scatter-write: one thread per (token, KV head, 16-byte piece of the head dim).
+// Scatter-write: one workgroup per 16 consecutive new tokens and one KV head.
+// Where the 16 tokens fill one block in order (a prefill chunk, a verify
+// window), the K tile and the transposed V tile are written as whole 16-byte
+// pieces, the V rows gathered through LDS; otherwise each token's K chunks are
+// 16-byte stores and its V values single-element stores.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, const T *__restrict__ vn,
                                                      const int32_t *__restrict__ slots, int n, T *kp, T *vp,
                                                      int num_blocks, int Hkv, int D) {
-    constexpr int X = 16 / sizeof(T);
-    const int cpt = D / X;
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= (long)n * Hkv * cpt) return;
-    const int c = (int)(idx % cpt);
-    const int h = (int)((idx / cpt) % Hkv);
-    const int i = (int)(idx / ((long)cpt * Hkv));
-    const int slot = slots[i];
-    if (slot < 0 || slot >= num_blocks * kBlock) return;
-    const int b = slot / kBlock, o = slot % kBlock;
-    const size_t src = ((size_t)i * Hkv + h) * D + (size_t)c * X;
-    const u32x4_t kv = *reinterpret_cast<const u32x4_t *>(kn + src);
-    *reinterpret_cast<u32x4_t *>(kp + ((((size_t)b * Hkv + h) * cpt + c) * kBlock + o) * X) = kv;
-    const u32x4_t vv = *reinterpret_cast<const u32x4_t *>(vn + src);
-    T e[X];
-    __builtin_memcpy(e, &vv, 16);
-    T *vd = vp + (((size_t)b * Hkv + h) * D + (size_t)c * X) * kBlock + o;
+    constexpr int X = 16 / sizeof(T);  // elements per 16-byte piece
+    const int tid = threadIdx.x;
+    const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
+    const int cpt = D / X;              // 16-byte pieces per token row
+    __shared__ int s_slot[kBlock];
+    __shared__ int s_full;
+    __shared__ __attribute__((aligned(16))) T sv[kBlock * 256];
+    if (tid < kBlock) {
+        const int i = i0 + tid;
+        int sl = i < n ? slots[i] : -1;
+        s_slot[tid] = (sl >= 0 && sl < num_blocks * kBlock) ? sl : -1;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const int sl0 = s_slot[0];
+        const bool ok = tid >= kBlock || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlock == 0);
+        const bool full = __all(ok);
+        if (tid == 0) s_full = full;
+    }
+    __syncthreads();
+    const bool full = s_full;
+    const int ntok = min(kBlock, n - i0);
+    if (full) {
+        const size_t tile = ((size_t)(s_slot[0] / kBlock) * Hkv + h) * D * kBlock;  // element offset
+        // K: piece (c, token t) of the tile is token t's chunk c
+        for (int p = tid; p < cpt * kBlock; p += 256) {
+            const int c = p / kBlock, t = p % kBlock;
+            *reinterpret_cast<u32x4_t *>(kp + tile + (size_t)p * X) =
+                *reinterpret_cast<const u32x4_t *>(kn + ((size_t)(i0 + t) * Hkv + h) * D + (size_t)c * X);
+        }
+        // V: rows through LDS, then each 16-byte piece of a channel row holds X tokens
+        for (int p = tid; p < cpt * kBlock; p += 256) {
+            const int t = p / cpt, c = p % cpt;
+            *reinterpret_cast<u32x4_t *>(sv + (size_t)t * D + (size_t)c * X) =
+                *reinterpret_cast<const u32x4_t *>(vn + ((size_t)(i0 + t) * Hkv + h) * D + (size_t)c * X);
+        }
+        __syncthreads();
+        constexpr int PPR = kBlock / X;  // pieces per channel row
+        for (int p = tid; p < D * PPR; p += 256) {
+            const int ch = p / PPR, q = p % PPR;
+            T e[X];
 #pragma unroll
-    for (int x = 0; x < X; ++x) vd[(size_t)x * kBlock] = e[x];
+            for (int x = 0; x < X; ++x) e[x] = sv[(size_t)(q * X + x) * D + ch];
+            u32x4_t w;
+            __builtin_memcpy(&w, e, 16);
+            *reinterpret_cast<u32x4_t *>(vp + tile + (size_t)ch * kBlock + q * X) = w;
+        }
+        return;
+    }
+    for (int p = tid; p < ntok * cpt; p += 256) {
+        const int t = p / cpt, c = p % cpt;
+        const int sl = s_slot[t];
+        if (sl < 0) continue;
+        const int b = sl / kBlock, o = sl % kBlock;
+        const size_t tile = ((size_t)b * Hkv + h) * D * kBlock;
+        const size_t src = ((size_t)(i0 + t) * Hkv + h) * D + (size_t)c * X;
+        *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)c * kBlock + o) * X) =
+            *reinterpret_cast<const u32x4_t *>(kn + src);
+        const u32x4_t vv = *reinterpret_cast<const u32x4_t *>(vn + src);
+        T e[X];
+        __builtin_memcpy(e, &vv, 16);
+#pragma unroll
+        for (int x = 0; x < X; ++x) vp[tile + ((size_t)c * X + x) * kBlock + o] = e[x];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1212,22 +1261,19 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
         PKV_FAIL(KV_EINVAL, "kv_append_scatter: K/V and pools must be 16-byte aligned");
     if ((int64_t)num_blocks * kBlock > INT32_MAX) PKV_FAIL(KV_EINVAL, "kv_append_scatter: pool too large");
-    const int X = dtype == KV_BF16 ? 8 : 4;
-    const int64_t threads = (int64_t)n * num_kv_heads * (head_dim / X);
-    const int64_t blocks = (threads + 255) / 256;
-    if (blocks > INT32_MAX) PKV_FAIL(KV_EINVAL, "kv_append_scatter: too many tokens");
+    const int64_t groups = ((int64_t)n + kBlock - 1) / kBlock;
+    if (groups > INT32_MAX || num_kv_heads > 65535) PKV_FAIL(KV_EINVAL, "kv_append_scatter: too many tokens or heads");
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
+    const dim3 grid((unsigned)groups, (unsigned)num_kv_heads);
     if (dtype == KV_BF16)
-        hipLaunchKernelGGL(scatter_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new), slot_mapping,
-                           n, static_cast<uint16_t *>(k_pool), static_cast<uint16_t *>(v_pool), num_blocks,
-                           num_kv_heads, head_dim);
+        hipLaunchKernelGGL(scatter_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(k_new),
+                           static_cast<const uint16_t *>(v_new), slot_mapping, n, static_cast<uint16_t *>(k_pool),
+                           static_cast<uint16_t *>(v_pool), num_blocks, num_kv_heads, head_dim);
     else
-        hipLaunchKernelGGL(scatter_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
-                           static_cast<const float *>(k_new), static_cast<const float *>(v_new), slot_mapping, n,
-                           static_cast<float *>(k_pool), static_cast<float *>(v_pool), num_blocks, num_kv_heads,
-                           head_dim);
+        hipLaunchKernelGGL(scatter_kernel<float>, grid, dim3(256), 0, st, static_cast<const float *>(k_new),
+                           static_cast<const float *>(v_new), slot_mapping, n, static_cast<float *>(k_pool),
+                           static_cast<float *>(v_pool), num_blocks, num_kv_heads, head_dim);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) PKV_FAIL(KV_EDEVICE, "kv_append_scatter: launch failed: %s", hipGetErrorString(e));
     return KV_OK;

@@ -166,3 +166,46 @@ def test_workspace_reuse(pk):
         err = max_err(out.cpu().numpy(), want)
         print(f"[case] workspace reuse call {i}: max abs err {err:.3e}", flush=True)
         assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_scatter_patterns_bit_exact(pk, dtype, D):
+    """kv_append_scatter against the oracle scatter on slot patterns that mix
+    whole blocks written in order (the 16-byte-piece path), runs shifted
+    inside blocks, reversed runs, skipped slots (-1) and a ragged last group."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(31 + D + (dtype == "bf16"))
+    nb, hkv = 96, 3
+    perm = rng.permutation(nb)
+    slots = []
+    slots += list(range(perm[0] * 16, perm[0] * 16 + 16))            # group 0: whole block, in order
+    slots += list(range(perm[2] * 16, perm[2] * 16 + 16))[::-1]       # group 1: whole block, reversed
+    slots += list(range(perm[4] * 16, perm[4] * 16 + 16))             # group 2: whole block, in order
+    slots += list(range(perm[1] * 16 + 5, perm[1] * 16 + 16))         # shifted run
+    slots += [-1] * 3 + list(range(perm[3] * 16, perm[3] * 16 + 13))  # skipped slots
+    slots += list(range(perm[5] * 16, perm[5] * 16 + 7))              # ragged end
+    slots = np.array(slots, dtype=np.int32)
+    n = slots.size
+    announce(f"scatter patterns dtype={dtype} D={D} n={n}")
+    if dtype == "bf16":
+        kn = synth.f32_to_bf16_bits(rng.standard_normal((n, hkv, D), dtype=np.float32))
+        vn = synth.f32_to_bf16_bits(rng.standard_normal((n, hkv, D), dtype=np.float32))
+        tk = torch.from_numpy(kn.view(np.int16)).cuda().view(torch.bfloat16)
+        tv = torch.from_numpy(vn.view(np.int16)).cuda().view(torch.bfloat16)
+        nan = np.uint16(0x7FC0)
+    else:
+        kn = rng.standard_normal((n, hkv, D), dtype=np.float32)
+        vn = rng.standard_normal((n, hkv, D), dtype=np.float32)
+        tk, tv = torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda()
+        nan = np.float32(np.nan)
+    kp, vp = pk.empty_pools(nb, hkv, D, tk.dtype, "cuda")
+    kp.fill_(float("nan"))
+    vp.fill_(float("nan"))
+    pk.kv_append_scatter(tk, tv, torch.from_numpy(slots).cuda(), kp, vp)
+    torch.cuda.synchronize()
+    ko, vo = oracle.empty_pools(nb, hkv, D, 16, dtype, fill=nan)
+    oracle.scatter(ko, vo, kn, vn, slots)
+    np.testing.assert_array_equal(_bits(kp), ko.view(np.uint16 if dtype == "bf16" else np.uint32))
+    np.testing.assert_array_equal(_bits(vp), vo.view(np.uint16 if dtype == "bf16" else np.uint32))
