@@ -77,10 +77,12 @@ def _lib():
             build()
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_attention.restype = ctypes.c_int
-        lib.oracle_attention.argtypes = [
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
-            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+        for fn in (lib.oracle_attention, lib.oracle_attention_kv64):
+            fn.restype = ctypes.c_int
+            fn.argtypes = [
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
         _LIB = lib
     return _LIB
 
@@ -175,21 +177,24 @@ def attention(q, k_seqs, v_seqs, qsl, num_q_heads, num_kv_heads, scale, sinks=No
     q: [total_rows, Hq, D] storage dtype; k_seqs/v_seqs: lists of [ctx_s, Hkv, D];
     qsl: [S+1]; sinks: [Hq] float32 or None. Returns float64 [total_rows, Hq, D].
     """
-    q32 = np.ascontiguousarray(to_f32(q, dtype))
+    kv64 = dtype == "fp8"   # K/V come as float64 dequantized values; q is bf16
+    q32 = np.ascontiguousarray(to_f32(q, "bf16" if kv64 else dtype))
     D = q32.shape[-1]
     ctxs = [int(k.shape[0]) for k in k_seqs]
     key_start = np.zeros(len(ctxs) + 1, dtype=np.int64)
     key_start[1:] = np.cumsum(ctxs)
+    conv = (lambda a: np.asarray(a, dtype=np.float64)) if kv64 else (lambda a: to_f32(a, dtype))
     if len(k_seqs):
-        k32 = np.ascontiguousarray(np.concatenate([to_f32(k, dtype).reshape(-1, num_kv_heads, D) for k in k_seqs]))
-        v32 = np.ascontiguousarray(np.concatenate([to_f32(v, dtype).reshape(-1, num_kv_heads, D) for v in v_seqs]))
+        k32 = np.ascontiguousarray(np.concatenate([conv(k).reshape(-1, num_kv_heads, D) for k in k_seqs]))
+        v32 = np.ascontiguousarray(np.concatenate([conv(v).reshape(-1, num_kv_heads, D) for v in v_seqs]))
     else:
-        k32 = np.zeros((0, num_kv_heads, D), np.float32)
+        k32 = np.zeros((0, num_kv_heads, D), np.float64 if kv64 else np.float32)
         v32 = k32
     qsl = np.ascontiguousarray(np.asarray(qsl, dtype=np.int32))
     out = np.zeros((int(qsl[-1]), num_q_heads, D), dtype=np.float64)
     sk = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
-    rc = _lib().oracle_attention(
+    fn = _lib().oracle_attention_kv64 if kv64 else _lib().oracle_attention
+    rc = fn(
         q32.ctypes.data, k32.ctypes.data, v32.ctypes.data, key_start.ctypes.data, qsl.ctypes.data,
         len(ctxs), num_q_heads, num_kv_heads, D, float(scale),
         None if sk is None else sk.ctypes.data, out.ctypes.data,
@@ -204,10 +209,155 @@ def paged_attention(q, k_pool, v_pool, block_tables, context_lens, qsl, num_q_he
     """Gather every sequence through its block table, then attention()."""
     ks, vs = [], []
     for s, ctx in enumerate(context_lens):
-        k, v = gather(k_pool, v_pool, block_tables[s], int(ctx))
+        if dtype == "fp8":
+            k, v = fp8_gather(k_pool, v_pool, block_tables[s], int(ctx))
+        else:
+            k, v = gather(k_pool, v_pool, block_tables[s], int(ctx))
         ks.append(k)
         vs.append(v)
     return attention(q, ks, vs, qsl, num_q_heads, num_kv_heads, scale, sinks, dtype, threads)
+
+
+# ----------------------------------------------------------------------------
+# 8-bit pools: FP8 E4M3 codes with one float32 scale per (token, KV head)
+# ----------------------------------------------------------------------------
+#
+# The pages name 8-bit KV codecs but define none (TensorSharp "高级功能",
+# section "内存优化": quantized paged KV blocks). The reading used here:
+#
+# * each (token, KV head) row x of D values (bf16) gets a scale
+#   s = amax / 448 in float32 (amax = max |x|, 448 the largest E4M3 value), and
+#   codes c = E4M3(round to nearest even, x / s clamped to [-448, 448]), the
+#   division in float32; a row of zeros has s = 0 and all codes 0;
+# * the stored value is decode(c) * s;
+# * E4M3 is the OCP 8-bit floating-point format E4M3FN: 1 sign bit, 4 exponent
+#   bits with bias 7, 3 mantissa bits, subnormals at exponent 0, no infinities,
+#   NaN only at S.1111.111, largest finite value 448.
+#
+# Layout of a (block, KV head) tile: 16*D code bytes then 16 float32 scales
+# (one per token slot), 16*D + 64 bytes in all; pools are
+# uint8 [num_blocks][Hkv][16*D + 64]. Within the codes:
+#   K: token t, channel c = 64 p + 32 jj + 8 g + e  ->  byte ((p*4 + g)*16 + t)*16 + jj*8 + e
+#   V: token t = 8 h + e, channel c = 16 (2 d + dd) + n  ->  byte (((d*16 + n)*2 + h)*2 + dd)*8 + e
+
+FP8_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 value of every E4M3FN code (NaN for S.1111.111)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * (m / 8.0) * 2.0 ** -6
+    val = np.where(e == 0, sub, normal)
+    return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))   # codes 0x00 .. 0x7E, ascending values
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Codes of float values |x| <= 448 by round to nearest, ties to the even
+    code (even mantissa); the sign bit follows x (negative zero keeps it)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > FP8_MAX):
+        raise ValueError("e4m3_encode needs finite |x| <= 448")
+    a = np.abs(x)
+    hi = np.searchsorted(_E4M3_POS, a, side="left").clip(0, 0x7E)   # first code with value >= a
+    lo = (hi - 1).clip(0, 0x7E)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == _E4M3_POS[hi], hi, np.where(pick_hi, hi, lo))
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize_rows(x_bf16):
+    """Rows [..., D] of bf16 bits -> (codes uint8 [..., D], scales float32 [...])."""
+    x = to_f32(x_bf16, "bf16")
+    amax = np.max(np.abs(x), axis=-1)
+    s = (amax.astype(np.float32) / np.float32(FP8_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = (x / safe[..., None]).astype(np.float32)
+    r = np.clip(r, np.float32(-FP8_MAX), np.float32(FP8_MAX))
+    codes = e4m3_encode(r)
+    codes = np.where((s > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, s
+
+
+def fp8_dequantize(codes, scales) -> np.ndarray:
+    """float64 values decode(c) * s."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def _fp8_k_offsets(D):
+    """Byte offset of (token t, channel c) in the code area of a K tile: [16, D]."""
+    t = np.arange(16)[:, None]
+    c = np.arange(D)[None, :]
+    p, jj, g, e = c // 64, (c // 32) % 2, (c // 8) % 4, c % 8
+    return ((p * 4 + g) * 16 + t) * 16 + jj * 8 + e
+
+
+def _fp8_v_offsets(D):
+    """Byte offset of (token t, channel c) in the code area of a V tile: [16, D]."""
+    t = np.arange(16)[:, None]
+    c = np.arange(D)[None, :]
+    dt, n = c // 16, c % 16
+    d, dd = dt // 2, dt % 2
+    h, e = t // 8, t % 8
+    return (((d * 16 + n) * 2 + h) * 2 + dd) * 8 + e
+
+
+def fp8_empty_pools(num_blocks, num_kv_heads, head_dim, fill=None):
+    if head_dim % 64:
+        raise ValueError("8-bit pools need head_dim a multiple of 64")
+    tile = 16 * head_dim + 64
+    kp = np.zeros((num_blocks, num_kv_heads, tile), dtype=np.uint8)
+    vp = np.zeros((num_blocks, num_kv_heads, tile), dtype=np.uint8)
+    if fill is not None:
+        kp[...] = fill
+        vp[...] = fill
+    return kp, vp
+
+
+def fp8_scatter(k_pool, v_pool, k_new_bf16, v_new_bf16, slots):
+    """Quantize new tokens ([n, Hkv, D] bf16 bits) and write codes and scales
+    at their slots (-1 = skip)."""
+    nb, hkv, tile = k_pool.shape
+    D = (tile - 64) // 16
+    offk, offv = _fp8_k_offsets(D), _fp8_v_offsets(D)
+    kc, ks = fp8_quantize_rows(k_new_bf16)
+    vc, vs = fp8_quantize_rows(v_new_bf16)
+    for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
+        if slot < 0:
+            continue
+        b, o = int(slot // 16), int(slot % 16)
+        for h in range(hkv):
+            k_pool[b, h, offk[o]] = kc[i, h]
+            v_pool[b, h, offv[o]] = vc[i, h]
+            k_pool[b, h, 16 * D + 4 * o:16 * D + 4 * o + 4] = np.frombuffer(ks[i, h].tobytes(), np.uint8)
+            v_pool[b, h, 16 * D + 4 * o:16 * D + 4 * o + 4] = np.frombuffer(vs[i, h].tobytes(), np.uint8)
+
+
+def fp8_gather(k_pool, v_pool, block_table_row, ctx):
+    """Dequantized float64 K, V [ctx, Hkv, D] of one sequence."""
+    nb, hkv, tile = k_pool.shape
+    D = (tile - 64) // 16
+    offk, offv = _fp8_k_offsets(D), _fp8_v_offsets(D)
+    bt = np.asarray(block_table_row, dtype=np.int64)
+    k = np.zeros((ctx, hkv, D))
+    v = np.zeros((ctx, hkv, D))
+    for t in range(ctx):
+        b, o = int(bt[t // 16]), t % 16
+        if b < 0 or b >= nb:
+            raise ValueError("block table points outside the pool")
+        sk = k_pool[b, :, 16 * D + 4 * o:16 * D + 4 * o + 4].copy().view(np.float32)[:, 0]
+        sv = v_pool[b, :, 16 * D + 4 * o:16 * D + 4 * o + 4].copy().view(np.float32)[:, 0]
+        k[t] = fp8_dequantize(k_pool[b][:, offk[o]], sk)
+        v[t] = fp8_dequantize(v_pool[b][:, offv[o]], sv)
+    return k, v
 
 
 # ----------------------------------------------------------------------------

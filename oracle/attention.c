@@ -25,7 +25,8 @@
  * of the DSpark drafter) is one logit per query head that enters the softmax
  * denominator only: it carries no value vector and is not multiplied by scale.
  *
- * Inputs arrive as float (every bf16 and fp32 value is exact in float) and are
+ * Inputs arrive as float (every bf16 and fp32 value is exact in float), or K/V
+ * as double (dequantized 8-bit values: code times per-token scale), and are
  * widened to double before any arithmetic; all sums are in double, in index
  * order. Output is double.
  */
@@ -33,19 +34,17 @@
 #include <stdint.h>
 #include <stddef.h>
 
-/*
- * q      [total_rows][Hq][D]          query rows, packed per sequence
- * k, v   [key_start[S]][Hkv][D]       gathered keys/values; sequence s owns
- *                                      positions key_start[s] .. key_start[s+1]
- * qsl    [S+1]                         query-row offsets
- * sinks  [Hq] or NULL
- * out    [total_rows][Hq][D]
- * Returns 0, or -1 on inconsistent sizes (q_len > ctx, Hq % Hkv != 0).
- */
-int oracle_attention(const float *q, const float *k, const float *v,
-                     const int64_t *key_start, const int32_t *qsl, int32_t num_seqs,
-                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                     double scale, const float *sinks, double *out, int32_t num_threads)
+/* One key/value element as double: from float storage, or from double
+ * storage (dequantized 8-bit pools, whose values a float may not hold). */
+static inline double kv_at(const void *base, int64_t idx, int kv64)
+{
+    return kv64 ? ((const double *)base)[idx] : (double)((const float *)base)[idx];
+}
+
+static int attend(const float *q, const void *k, const void *v, int kv64,
+                  const int64_t *key_start, const int32_t *qsl, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  double scale, const float *sinks, double *out, int32_t num_threads)
 {
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0)
         return -1;
@@ -78,10 +77,10 @@ int oracle_attention(const float *q, const float *k, const float *v,
         /* scores and their maximum */
         double M = -INFINITY;
         for (int64_t t = 0; t <= p; ++t) {
-            const float *kt = k + ((key_start[s] + t) * num_kv_heads + g) * D;
+            const int64_t kt = ((key_start[s] + t) * num_kv_heads + g) * D;
             double dot = 0.0;
             for (int64_t d = 0; d < D; ++d)
-                dot += (double)qi[d] * (double)kt[d];
+                dot += (double)qi[d] * kv_at(k, kt + d, kv64);
             double x = scale * dot;
             if (x > M)
                 M = x;
@@ -93,15 +92,14 @@ int oracle_attention(const float *q, const float *k, const float *v,
             o[d] = 0.0;
         double Z = 0.0;
         for (int64_t t = 0; t <= p; ++t) {
-            const float *kt = k + ((key_start[s] + t) * num_kv_heads + g) * D;
-            const float *vt = v + ((key_start[s] + t) * num_kv_heads + g) * D;
+            const int64_t kt = ((key_start[s] + t) * num_kv_heads + g) * D;
             double dot = 0.0;
             for (int64_t d = 0; d < D; ++d)
-                dot += (double)qi[d] * (double)kt[d];
+                dot += (double)qi[d] * kv_at(k, kt + d, kv64);
             double w = exp(scale * dot - M);
             Z += w;
             for (int64_t d = 0; d < D; ++d)
-                o[d] += w * (double)vt[d];
+                o[d] += w * kv_at(v, kt + d, kv64);
         }
         if (sinks)
             Z += exp((double)sinks[h] - M);
@@ -109,4 +107,32 @@ int oracle_attention(const float *q, const float *k, const float *v,
             o[d] /= Z;
     }
     return 0;
+}
+
+/*
+ * q      [total_rows][Hq][D]          query rows, packed per sequence
+ * k, v   [key_start[S]][Hkv][D]       gathered keys/values; sequence s owns
+ *                                      positions key_start[s] .. key_start[s+1]
+ * qsl    [S+1]                         query-row offsets
+ * sinks  [Hq] or NULL
+ * out    [total_rows][Hq][D]
+ * Returns 0, or -1 on inconsistent sizes (q_len > ctx, Hq % Hkv != 0).
+ */
+int oracle_attention(const float *q, const float *k, const float *v,
+                     const int64_t *key_start, const int32_t *qsl, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     double scale, const float *sinks, double *out, int32_t num_threads)
+{
+    return attend(q, k, v, 0, key_start, qsl, num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                  sinks, out, num_threads);
+}
+
+/* The same with double keys and values. */
+int oracle_attention_kv64(const float *q, const double *k, const double *v,
+                          const int64_t *key_start, const int32_t *qsl, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          double scale, const float *sinks, double *out, int32_t num_threads)
+{
+    return attend(q, k, v, 1, key_start, qsl, num_seqs, num_q_heads, num_kv_heads, head_dim, scale,
+                  sinks, out, num_threads);
 }

@@ -89,8 +89,10 @@ class Workload:
 
 
 def _normal(rng, shape, dtype):
+    """N(0, 1) values; bf16 bits for bf16 workloads and for 8-bit-pool ("fp8")
+    workloads, whose queries and new K/V rows arrive in bf16."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    return f32_to_bf16_bits(x) if dtype in ("bf16", "fp8") else x
 
 
 def _pool_size(unique_blocks: int, exact: Optional[int] = None) -> int:
