@@ -33,9 +33,19 @@ METRIC = "paged-attn decode KV GB/s (% of HBM peak) + seq-tokens/s, 1 GPU"
 MIN_FOOTPRINT = 1 << 30        # bytes of pool touched per step
 
 
+def row_bytes(w):
+    """Bytes one token's K (or V) row of one KV head occupies in the pool:
+    head_dim elements, or for 8-bit pools head_dim codes and a float32 scale."""
+    return {"bf16": 2 * w.head_dim, "f32": 4 * w.head_dim, "fp8": w.head_dim + 4}[w.dtype]
+
+
+def elem_bytes(w):
+    """Bytes of one element of the queries and the new K/V rows."""
+    return 4 if w.dtype == "f32" else 2
+
+
 def unique_kv_bytes(w, tables):
     """K+V bytes of the visible tokens of every distinct physical block, once."""
-    elt = 2 if w.dtype == "bf16" else 4
     seen = {}
     for s, seq in enumerate(w.seqs):
         nb = -(-seq.ctx // 16)
@@ -43,12 +53,11 @@ def unique_kv_bytes(w, tables):
             b = int(tables[s, j])
             seen[b] = max(seen.get(b, 0), min(16, seq.ctx - 16 * j))
     tokens = sum(seen.values())
-    return tokens * w.num_kv_heads * w.head_dim * elt * 2
+    return tokens * w.num_kv_heads * row_bytes(w) * 2
 
 
 def logical_kv_bytes(w):
-    elt = 2 if w.dtype == "bf16" else 4
-    return sum(seq.ctx for seq in w.seqs) * w.num_kv_heads * w.head_dim * elt * 2
+    return sum(seq.ctx for seq in w.seqs) * w.num_kv_heads * row_bytes(w) * 2
 
 
 def cpu_baseline(w, kv_bytes, rows, seconds):
@@ -57,11 +66,16 @@ def cpu_baseline(w, kv_bytes, rows, seconds):
     over the whole batch of one layer."""
     import oracle
     a = oracle.Allocator(w.num_blocks, w.block_size, w.free_order)
-    kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+    if w.dtype == "fp8":
+        kp, vp = oracle.fp8_empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim)
+        put = oracle.fp8_scatter
+    else:
+        kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
+        put = oracle.scatter
     tables = []
     for s, seq in enumerate(w.seqs):
         row, _, _, slots = a.alloc(s, seq.tokens, w.max_blocks_per_seq)
-        oracle.scatter(kp, vp, seq.k, seq.v, slots)
+        put(kp, vp, seq.k, seq.v, slots)
         tables.append(row)
     tables = np.array(tables, dtype=np.int32)
     threads = oracle.default_threads()
@@ -233,7 +247,7 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = synth.by_name(args.workload)
-    elt = 2 if w.dtype == "bf16" else 4
+    elt = elem_bytes(w)
 
     # host block allocation for the batch, timed on its own
     t0 = time.perf_counter()
@@ -243,7 +257,7 @@ def main(argv=None):
     alloc_us = (time.perf_counter() - t0) * 1e6
     del pool
 
-    pool_bytes = w.num_blocks * w.num_kv_heads * w.head_dim * 16 * elt * 2
+    pool_bytes = w.num_blocks * w.num_kv_heads * 16 * row_bytes(w) * 2
     layers = args.layers or max(1, math.ceil(MIN_FOOTPRINT / pool_bytes))
     st = stage(w, device=dev, copies=layers, poison=False)
     kv_bytes = unique_kv_bytes(w, st.tables_np)
@@ -251,7 +265,7 @@ def main(argv=None):
     q_bytes = rows * w.num_q_heads * w.head_dim * elt
     out_bytes = rows * w.num_q_heads * w.head_dim * 4
     n_step_tok = int(st.step_slots_np.size)
-    scatter_bytes = n_step_tok * w.num_kv_heads * w.head_dim * elt * 2 * 2
+    scatter_bytes = n_step_tok * w.num_kv_heads * (w.head_dim * elt + row_bytes(w)) * 2
     stream = torch.cuda.current_stream()
 
     def layer_call(l):

@@ -41,6 +41,21 @@
  * pieces of the head dimension side by side across the 16 tokens of a block;
  * V is stored transposed within a block (one row of 16 tokens per channel).
  * Both make every (block, KV head) tile a contiguous 16 * head_dim element run.
+ *
+ * 8-bit pools (KV_FP8; "内存优化" names quantized KV blocks but fixes no codec):
+ * each (token, KV head) row x of head_dim values is stored as OCP FP8 E4M3FN
+ * codes c with one float32 scale s = max|x| / 448 (float32 division), the codes
+ * being x / s (float32 division) clamped to [-448, 448] and rounded to the
+ * nearest code, ties to the even code; a row of zeros stores s = 0 and zero
+ * codes. The value the attention uses is c * s. A (block, KV head) tile is
+ * 16 * head_dim code bytes followed by the 16 tokens' float32 scales
+ * (16 * head_dim + 64 bytes); the pools are
+ *   K_pool, V_pool [num_blocks][num_kv_heads][16 * head_dim + 64] bytes,
+ * codes placed, for token t and channel c,
+ *   K: c = 64 p + 32 jj + 8 g + e  at byte ((p * 4 + g) * 16 + t) * 16 + jj * 8 + e
+ *   V: t = 8 h + e, c = 16 (2 d + dd) + n  at byte (((d * 16 + n) * 2 + h) * 2 + dd) * 8 + e
+ * (head_dim a multiple of 64). Queries and the new K/V rows handed to
+ * kv_append_scatter are bf16.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -61,7 +76,7 @@ enum kv_status {
     KV_EINTERNAL = -5      /* unexpected internal failure */
 };
 
-enum kv_dtype { KV_F32 = 0, KV_BF16 = 1 };
+enum kv_dtype { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
 
 #define PAGEDKV_ABI_VERSION 1
 
@@ -160,11 +175,15 @@ int kv_pool_set_hash_mask(kv_pool *pool, uint64_t mask);
  *   V_pool[slot / 16][h][d][slot % 16]            = v_new[i][h][d]
  * for all h < num_kv_heads, d < head_dim: a bit copy. Slots of -1 are skipped;
  * slots outside the pool are skipped. Slots must be distinct within a call.
+ * With dtype KV_FP8, k_new and v_new are bf16 and each (token, head) row is
+ * quantized as described under "8-bit pools" and written with its scale.
  *   k_new, v_new  device [n][num_kv_heads][head_dim], element type `dtype`
+ *                 (bf16 for KV_FP8)
  *   slot_mapping  device int32 [n]
  *   k_pool, v_pool device pools in the layout above, num_blocks blocks
- * Supported: dtype KV_BF16 or KV_F32, head_dim a multiple of 16 up to 256,
- * block_size 16. Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
+ * Supported: dtype KV_BF16 or KV_F32 with head_dim a multiple of 16 up to 256;
+ * KV_FP8 with head_dim 64 or 128; block_size 16.
+ * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
  */
 int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_mapping,
                       int32_t n, void *k_pool, void *v_pool, int32_t num_blocks,
@@ -210,7 +229,9 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
  * its visible keys and values, scale and sink: the same row gives the same bits
  * alone, in any batch, and inside any window (a verify window row equals the
  * same query run as a single decode row over the keys up to it).
- * Supported: head_dim 64 or 128, block_size 16, dtype KV_BF16 or KV_F32.
+ * Supported: head_dim 64 or 128, block_size 16, dtype KV_BF16, KV_F32 or
+ * KV_FP8 (q in bf16, pools of 8-bit tiles: the keys and values are the
+ * stored codes times their scales).
  * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
  */
 int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
@@ -234,8 +255,8 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
  * the same stream, bit for bit in `out` and in the pools. Other arguments,
  * ownership and errors are those of paged_attention_forward; k_pool and v_pool
  * are written. A bf16 batch of single-row sequences (decode) writes and uses
- * the new tokens inside the attention launch; any other batch is scattered
- * first.
+ * the new tokens inside the attention launch; any other batch, and every
+ * KV_FP8 batch (k_new, v_new in bf16), is scattered first.
  */
 int paged_attention_append_forward(const void *q, const void *k_new, const void *v_new,
                                    const int32_t *slot_mapping, void *k_pool, void *v_pool, int32_t dtype,

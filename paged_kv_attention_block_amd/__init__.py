@@ -8,7 +8,10 @@ memory and streams. If the library is missing the import fails: there is no
 fallback path.
 
 Pool layout (see the header): with X = 16 bytes / element size,
-``K_pool [num_blocks, Hkv, D // X, 16, X]`` and ``V_pool [num_blocks, Hkv, D, 16]``.
+``K_pool [num_blocks, Hkv, D // X, 16, X]`` and ``V_pool [num_blocks, Hkv, D, 16]``
+for float32 and bf16 pools; 8-bit pools (E4M3 codes with a float32 scale per
+token and KV head) are ``torch.uint8 [num_blocks, Hkv, 16 * D + 64]`` each,
+with bf16 queries and bf16 new K/V rows.
 """
 from __future__ import annotations
 
@@ -19,14 +22,14 @@ import numpy as np
 
 __all__ = [
     "KV_OK", "KV_EINVAL", "KV_ENOMEM", "KV_EUNSUPPORTED", "KV_EDEVICE", "KV_EINTERNAL",
-    "KV_F32", "KV_BF16", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
+    "KV_F32", "KV_BF16", "KV_FP8", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
     "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_workspace_size",
     "paged_attention_forward", "paged_attention_append_forward", "empty_pools", "BLOCK_SIZE",
 ]
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
-KV_F32, KV_BF16 = 0, 1
+KV_F32, KV_BF16, KV_FP8 = 0, 1, 2
 BLOCK_SIZE = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -183,32 +186,57 @@ def _need(t, name, dtype=None, ndim=None):
 
 
 def empty_pools(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):
-    """Allocate (K_pool, V_pool) device tensors in the library's layout."""
+    """Allocate (K_pool, V_pool) device tensors in the library's layout;
+    dtype torch.uint8 gives 8-bit pools."""
     torch = _torch()
+    if dtype == torch.uint8:
+        tile = 16 * head_dim + 64
+        return (torch.empty((num_blocks, num_kv_heads, tile), dtype=dtype, device=device),
+                torch.empty((num_blocks, num_kv_heads, tile), dtype=dtype, device=device))
     X = 16 // torch.empty((), dtype=dtype).element_size()
     k = torch.empty((num_blocks, num_kv_heads, head_dim // X, BLOCK_SIZE, X), dtype=dtype, device=device)
     v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=dtype, device=device)
     return k, v
 
 
+def _pools(k_pool, v_pool, elem_dtype, hkv, d):
+    """Check the pools against the element type of the rows that go with them
+    (queries or new K/V) and return (dtype code, num_blocks)."""
+    torch = _torch()
+    if k_pool.dtype == torch.uint8:
+        if elem_dtype != torch.bfloat16:
+            raise KVError(KV_EINVAL, "8-bit pools take bf16 queries and bf16 new K/V rows")
+        _need(k_pool, "k_pool", dtype=torch.uint8, ndim=3)
+        _need(v_pool, "v_pool", dtype=torch.uint8, ndim=3)
+        nb = k_pool.shape[0]
+        want = (nb, hkv if hkv is not None else k_pool.shape[1], 16 * d + 64)
+        if tuple(k_pool.shape) != want or tuple(v_pool.shape) != want:
+            raise KVError(KV_EINVAL, f"8-bit pools must be [num_blocks, Hkv, {16 * d + 64}]")
+        return KV_FP8, nb
+    _need(k_pool, "k_pool", dtype=elem_dtype, ndim=5)
+    _need(v_pool, "v_pool", dtype=elem_dtype, ndim=4)
+    nb = k_pool.shape[0]
+    h = hkv if hkv is not None else k_pool.shape[1]
+    if tuple(v_pool.shape) != (nb, h, d, BLOCK_SIZE) or k_pool.shape[1] != h or \
+            k_pool.shape[2] * k_pool.shape[4] != d or k_pool.shape[3] != BLOCK_SIZE:
+        raise KVError(KV_EINVAL, "pool shapes do not match the rows")
+    return _dtype_code(k_pool), nb
+
+
 def kv_append_scatter(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None) -> None:
-    """Scatter-write k_new/v_new [n, Hkv, D] into the pools at slot_mapping [n] (int32, -1 = skip)."""
+    """Scatter-write k_new/v_new [n, Hkv, D] into the pools at slot_mapping [n] (int32, -1 = skip);
+    8-bit pools quantize each (token, KV head) row."""
     torch = _torch()
     _need(k_new, "k_new", ndim=3)
     _need(v_new, "v_new", dtype=k_new.dtype, ndim=3)
     _need(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
-    _need(k_pool, "k_pool", dtype=k_new.dtype, ndim=5)
-    _need(v_pool, "v_pool", dtype=k_new.dtype, ndim=4)
     n, hkv, d = k_new.shape
     if v_new.shape != k_new.shape or slot_mapping.shape[0] != n:
         raise KVError(KV_EINVAL, "k_new, v_new and slot_mapping sizes disagree")
-    nb = k_pool.shape[0]
-    if tuple(v_pool.shape) != (nb, hkv, d, BLOCK_SIZE) or k_pool.shape[1] != hkv or \
-            k_pool.shape[2] * k_pool.shape[4] != d or k_pool.shape[3] != BLOCK_SIZE:
-        raise KVError(KV_EINVAL, "pool shapes do not match k_new")
+    code, nb = _pools(k_pool, v_pool, k_new.dtype, hkv, d)
     _check(_lib.kv_append_scatter(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), n,
                                   k_pool.data_ptr(), v_pool.data_ptr(), nb, hkv, d, BLOCK_SIZE,
-                                  _dtype_code(k_new), _stream_ptr(stream)))
+                                  code, _stream_ptr(stream)))
 
 
 def paged_attention_workspace_size(num_seqs: int, total_q_rows: int, num_q_heads: int, head_dim: int,
@@ -221,13 +249,12 @@ def _forward_args(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
                   workspace):
     torch = _torch()
     _need(q, "q", ndim=3)
-    _need(k_pool, "k_pool", dtype=q.dtype, ndim=5)
-    _need(v_pool, "v_pool", dtype=q.dtype, ndim=4)
     _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
     _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
     _need(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
     total, hq, d = q.shape
-    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    code, nb = _pools(k_pool, v_pool, q.dtype, None, d)
+    hkv = k_pool.shape[1]
     S = context_lens.shape[0]
     if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S:
         raise KVError(KV_EINVAL, "context_lens, query_start_loc and block_tables disagree on num_seqs")
@@ -245,17 +272,17 @@ def _forward_args(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
-    return S, total, hq, hkv, d, nb, out, workspace, ws_bytes
+    return S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes
 
 
 def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
                             max_context_len: int, scale: float, sinks=None, out=None, workspace=None,
                             stream=None):
     """out [total_rows, Hq, D] float32 = attention of q over the paged cache (see pagedkv.h)."""
-    S, total, hq, hkv, d, nb, out, workspace, ws_bytes = _forward_args(
+    S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
         q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
     _check(_lib.paged_attention_forward(
-        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), _dtype_code(q), block_tables.data_ptr(),
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), code, block_tables.data_ptr(),
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len,
         max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
@@ -269,7 +296,7 @@ def paged_attention_append_forward(q, k_new, v_new, slot_mapping, k_pool, v_pool
     """kv_append_scatter of each row's own token (k_new, v_new [total_rows, Hkv, D], slot_mapping
     [total_rows]) and paged_attention_forward in one call (see pagedkv.h); returns out."""
     torch = _torch()
-    S, total, hq, hkv, d, nb, out, workspace, ws_bytes = _forward_args(
+    S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
         q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
     _need(k_new, "k_new", dtype=q.dtype, ndim=3)
     _need(v_new, "v_new", dtype=q.dtype, ndim=3)
@@ -279,7 +306,7 @@ def paged_attention_append_forward(q, k_new, v_new, slot_mapping, k_pool, v_pool
         raise KVError(KV_EINVAL, "k_new, v_new and slot_mapping must hold one row per query row")
     _check(_lib.paged_attention_append_forward(
         q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_pool.data_ptr(),
-        v_pool.data_ptr(), _dtype_code(q), block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+        v_pool.data_ptr(), code, block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
         query_start_loc.data_ptr(), S, total, max_q_len, max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
         _stream_ptr(stream)))

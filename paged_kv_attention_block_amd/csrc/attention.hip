@@ -269,23 +269,34 @@ __device__ inline void patch_new_key(StepRegs<D> &r, const u32x4_t (&knew)[D / 3
     }
 }
 
-template <int D>
-__device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
-                                   int prow, int g, float scale_log2) {
+// One online-softmax step over the MFMA operands kop(tau, j) (K, tile tau,
+// k-step j) and vop(dt) (V^T, d-tile dt). SCALED: 8-bit pools, whose scores
+// take the keys' K scales (ksc, the lane's 8 keys) and whose probabilities
+// take the keys' V scales (vsc) before the PV product; the sum l takes the
+// unscaled probabilities.
+template <int D, bool SCALED, class KOp, class VOp>
+__device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const float (&ksc)[8],
+                                 const float (&vsc)[8], const u32x4_t (&qop)[D / 32], int kc, int prow, int g,
+                                 float scale_log2) {
     constexpr int KJ = D / 32, DT = D / 16;
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
         const bf16x8_t b = __builtin_bit_cast(bf16x8_t, qop[j]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[0][j]), b, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[1][j]), b, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(0, j), b, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop(1, j), b, s1, 0, 0, 0);
     }
     float sc[8];
     const int lim = prow - (kc + key_off(g));  // the row sees the lane's keys 0 .. lim
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        sc[i] = i <= lim ? s0[i] * scale_log2 : -INFINITY;
-        sc[4 + i] = i + 4 <= lim ? s1[i] * scale_log2 : -INFINITY;
+        if constexpr (SCALED) {
+            sc[i] = i <= lim ? (s0[i] * ksc[i]) * scale_log2 : -INFINITY;
+            sc[4 + i] = i + 4 <= lim ? (s1[i] * ksc[4 + i]) * scale_log2 : -INFINITY;
+        } else {
+            sc[i] = i <= lim ? s0[i] * scale_log2 : -INFINITY;
+            sc[4 + i] = i + 4 <= lim ? s1[i] * scale_log2 : -INFINITY;
+        }
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -303,9 +314,11 @@ __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, 
     bf16x8_t phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const __bf16 x = (__bf16)pv[e];
+        float w = pv[e];
+        if constexpr (SCALED) w = w * vsc[e];
+        const __bf16 x = (__bf16)w;
         phi[e] = x;
-        plo[e] = (__bf16)(pv[e] - (float)x);
+        plo[e] = (__bf16)(w - (float)x);
     }
     // Rows with no visible key in the chunk keep their state exactly; the
     // rescale by alpha is skipped when it is 1 in every lane (x * 1 == x).
@@ -315,7 +328,7 @@ __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, 
     for (int dt = 0; dt < DT; ++dt) {
         f32x4_t a = st.acc[dt];
         if (rescale) a *= alpha;
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, r.v[dt]);
+        const bf16x8_t va = vop(dt);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a, 0, 0, 0);
         a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a, 0, 0, 0);
         st.acc[dt] = (all_has || has) ? a : st.acc[dt];
@@ -324,6 +337,161 @@ __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, 
     st.l = has ? l_new : st.l;
     st.m = has ? m_new : st.m;
 }
+
+template <int D>
+__device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
+                                   int prow, int g, float scale_log2) {
+    const float none[8] = {};
+    step_core<D, false>(
+        st, [&](int tau, int j) { return __builtin_bit_cast(bf16x8_t, r.k[tau][j]); },
+        [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, prow, g, scale_log2);
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit pools: FP8 E4M3 codes (OCP E4M3FN) with one float32 scale per
+// (token, KV head); the stored value is code * scale. Tile of a (block, KV
+// head): 16 * D code bytes, then the 16 tokens' scales. Within the codes
+//   K: token t, channel c = 64 p + 32 jj + 8 g + e  at byte ((p*4 + g)*16 + t)*16 + jj*8 + e
+//   V: token t = 8 h + e, channel c = 16 (2 d + dd) + n  at byte (((d*16 + n)*2 + h)*2 + dd)*8 + e
+// so that one 16-byte load gives a lane its K operands of two MFMA k-steps,
+// or its V^T operands of two d-tiles. Codes become bf16 exactly; scales act
+// in float32 on the scores (K) and on the probabilities (V).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int D>
+constexpr int q8_tile_bytes() { return 16 * D + 64; }
+
+template <int D>
+struct StepRegs8 {
+    u32x4_t k[2][D / 64];  // tile tau, channel pair p
+    u32x4_t v[D / 32];     // d-tile pair
+    f32x4_t ks[2], vs[2];  // scales of the lane's keys 0-3 and 4-7
+};
+
+// eight codes (two dwords, low byte first) -> eight bf16 values, exact
+__device__ inline bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Operands of one chunk from 8-bit tiles kt0/vt0 and kt1/vt1 (blocks 0, 1).
+// kpos(t): position of token t's K pieces, vhalf(row, h): position of V half
+// h of channel row `row` (identity in the pools; swizzled in LDS staging).
+template <int D, class KPos, class VHalf>
+__device__ inline void load_step8(StepRegs8<D> &r, const uint8_t *kt0, const uint8_t *vt0, const uint8_t *kt1,
+                                  const uint8_t *vt1, int g, int n, KPos kpos, VHalf vhalf) {
+    const uint8_t *k = n >= 8 ? kt1 : kt0;
+    const int tk = 8 * ((n >> 2) & 1) + (n & 3);
+#pragma unroll
+    for (int p = 0; p < D / 64; ++p) {
+        r.k[0][p] = *reinterpret_cast<const u32x4_t *>(k + ((p * 4 + g) * kBlock + kpos(tk)) * 16);
+        r.k[1][p] = *reinterpret_cast<const u32x4_t *>(k + ((p * 4 + g) * kBlock + kpos(tk + 4)) * 16);
+    }
+    const uint8_t *v = (g >> 1) ? vt1 : vt0;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+        r.v[d] = *reinterpret_cast<const u32x4_t *>(v + ((d * 16 + n) * 2 + vhalf(d * 16 + n, g & 1)) * 16);
+    const uint8_t *kss = ((g >> 1) ? kt1 : kt0) + 16 * D + 32 * (g & 1);
+    const uint8_t *vss = v + 16 * D + 32 * (g & 1);
+    r.ks[0] = *reinterpret_cast<const f32x4_t *>(kss);
+    r.ks[1] = *reinterpret_cast<const f32x4_t *>(kss + 16);
+    r.vs[0] = *reinterpret_cast<const f32x4_t *>(vss);
+    r.vs[1] = *reinterpret_cast<const f32x4_t *>(vss + 16);
+}
+
+template <int D>
+__device__ inline void load_step8(StepRegs8<D> &r, const uint8_t *kt0, const uint8_t *vt0, const uint8_t *kt1,
+                                  const uint8_t *vt1, int g, int n) {
+    load_step8<D>(r, kt0, vt0, kt1, vt1, g, n, [](int t) { return t; }, [](int, int h) { return h; });
+}
+
+// Zero V codes and V scales of keys at or past ctx, so that a zero weight
+// never meets a NaN (the scores of those keys are masked by select).
+template <int D>
+__device__ inline void mask_tail8(StepRegs8<D> &r, int kc, int ctx, int g) {
+    if (kc + kStep <= ctx) return;
+    const int nv = ctx - (kc + key_off(g));  // the lane's keys 0 .. nv-1 exist
+    auto bytes = [](int k) {                 // low k bytes of a dword set, 0 <= k <= 4
+        return k <= 0 ? 0u : k >= 4 ? 0xFFFFFFFFu : (1u << (8 * k)) - 1u;
+    };
+    const uint32_t m0 = bytes(nv), m1 = bytes(nv - 4);
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d) {
+        r.v[d].x &= m0;
+        r.v[d].y &= m1;
+        r.v[d].z &= m0;
+        r.v[d].w &= m1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.vs[0][i] = i < nv ? r.vs[0][i] : 0.f;
+        r.vs[1][i] = i + 4 < nv ? r.vs[1][i] : 0.f;
+    }
+}
+
+template <int D>
+__device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r, const u32x4_t (&qop)[D / 32],
+                                    int kc, int prow, int g, float scale_log2) {
+    float ksc[8], vsc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ksc[i] = r.ks[0][i];
+        ksc[4 + i] = r.ks[1][i];
+        vsc[i] = r.vs[0][i];
+        vsc[4 + i] = r.vs[1][i];
+    }
+    step_core<D, true>(
+        st,
+        [&](int tau, int j) {
+            const u32x4_t w = r.k[tau][j >> 1];
+            return (j & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+        },
+        [&](int dt) {
+            const u32x4_t w = r.v[dt >> 1];
+            return (dt & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+        },
+        ksc, vsc, qop, kc, prow, g, scale_log2);
+}
+
+// Pool access of the parallel and sequential shapes for bf16 (Q8 = false)
+// and 8-bit (Q8 = true) tiles; pointers are byte addresses of tiles.
+template <int D, bool Q8>
+struct Pool;
+
+template <int D>
+struct Pool<D, false> {
+    using Regs = StepRegs<D>;
+    static constexpr size_t tile_bytes = (size_t)kBlock * D * 2;
+    __device__ static void load(Regs &r, const uint8_t *k0, const uint8_t *v0, const uint8_t *k1, const uint8_t *v1,
+                                int g, int n) {
+        load_step<D>(r, reinterpret_cast<const uint16_t *>(k0), reinterpret_cast<const uint16_t *>(v0),
+                     reinterpret_cast<const uint16_t *>(k1), reinterpret_cast<const uint16_t *>(v1), g, n);
+    }
+    __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail<D>(r, kc, ctx, g); }
+    __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
+                                  int prow, int g, float sl2) {
+        step_update<D>(st, r, qop, kc, prow, g, sl2);
+    }
+};
+
+template <int D>
+struct Pool<D, true> {
+    using Regs = StepRegs8<D>;
+    static constexpr size_t tile_bytes = (size_t)q8_tile_bytes<D>();
+    __device__ static void load(Regs &r, const uint8_t *k0, const uint8_t *v0, const uint8_t *k1, const uint8_t *v1,
+                                int g, int n) {
+        load_step8<D>(r, k0, v0, k1, v1, g, n);
+    }
+    __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail8<D>(r, kc, ctx, g); }
+    __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
+                                  int prow, int g, float sl2) {
+        step_update8<D>(st, r, qop, kc, prow, g, sl2);
+    }
+};
 
 // Rows rho = row0 + 16 t + n of a sequence's [q_len * G] row space, ordered
 // r * G + head-in-group.
@@ -395,8 +563,10 @@ struct ParLds {
     float2 ml[3][NT][64];
 };
 
-template <int D, int NT, bool PF, bool APPEND>
+template <int D, int NT, bool PF, bool APPEND, bool Q8>
 __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnParams P) {
+    using PoolT = Pool<D, Q8>;
+    using Regs = typename PoolT::Regs;
     constexpr int DT = D / 16, KJ = D / 32;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
@@ -458,10 +628,10 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                   : -1;
         // appending decode step: the wave whose quarter holds the new key
         const int pn = ctx - 1;
-        const bool fused = APPEND && kq0 <= pn && pn < kq1;
+        const bool fused = APPEND && !Q8 && kq0 <= pn && pn < kq1;
         u32x4_t knew[KJ];
         uint32_t vnew[DT];
-        if (APPEND && fused) {
+        if (APPEND && !Q8 && fused) {
             const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
 #pragma unroll
             for (int jj = 0; jj < KJ; ++jj)
@@ -480,35 +650,35 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                 for (int c = lane; c < D; c += 64) P.vp_w[tb * kBlock + (size_t)c * kBlock + o] = P.v_new[rowoff + c];
             }
         }
-        const size_t tile = (size_t)kBlock * D;
-        const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * tile;
-        const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * tile;
+        const size_t tile = PoolT::tile_bytes;
+        const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * tile;
+        const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * tile;
+        const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_zero_tile);
         const size_t bstride = (size_t)P.Hkv * tile;
         // Step at key kc; lanes past the quarter's blocks hold -1, so a fetch
         // one step past the end reads the zero tile.
-        auto fetch = [&](StepRegs<D> &r, int kc) {
+        auto fetch = [&](Regs &r, int kc) {
             const int li = (kc - kq0) / kBlock;
             const int b0 = __builtin_amdgcn_readlane(bid, li);
             const int b1 = __builtin_amdgcn_readlane(bid, li + 1);
-            load_step<D>(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : g_zero_tile,
-                         b0 >= 0 ? vbase + (size_t)b0 * bstride : g_zero_tile,
-                         b1 >= 0 ? kbase + (size_t)b1 * bstride : g_zero_tile,
-                         b1 >= 0 ? vbase + (size_t)b1 * bstride : g_zero_tile, g, n);
+            PoolT::load(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : zero, b0 >= 0 ? vbase + (size_t)b0 * bstride : zero,
+                        b1 >= 0 ? kbase + (size_t)b1 * bstride : zero, b1 >= 0 ? vbase + (size_t)b1 * bstride : zero,
+                        g, n);
         };
-        auto compute = [&](StepRegs<D> &r, int kc) {
-            if constexpr (APPEND)
+        auto compute = [&](Regs &r, int kc) {
+            if constexpr (APPEND && !Q8)
                 if (fused && kc <= pn && pn < kc + kStep) patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
-            mask_tail<D>(r, kc, ctx, g);
+            PoolT::mask(r, kc, ctx, g);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                if (16 * t < rows_total) step_update<D>(st[t], r, qop[t], kc, ri[t].prow, g, P.scale_log2);
+                if (16 * t < rows_total) PoolT::update(st[t], r, qop[t], kc, ri[t].prow, g, P.scale_log2);
         };
         if constexpr (PF) {
             // Two register stages, each refilled as soon as it is consumed,
             // so that two steps are in flight; unrolled so that each stage
             // keeps fixed registers (a copy between stages would wait for the
             // loads it copies).
-            StepRegs<D> r0, r1;
+            Regs r0, r1;
             fetch(r0, kq0);
             if (kq0 + kStep < kq1) fetch(r1, kq0 + kStep);
             for (int kc = kq0; kc < kq1; kc += 2 * kStep) {
@@ -521,7 +691,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
             }
         } else {
             for (int kc = kq0; kc < kq1; kc += kStep) {
-                StepRegs<D> r;
+                Regs r;
                 fetch(r, kc);
                 compute(r, kc);
             }
@@ -662,13 +832,14 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
     return false;
 }
 
-template <int D>
+template <int D, bool Q8>
 __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
+    using PoolT = Pool<D, Q8>;
+    using Regs = typename PoolT::Regs;
     constexpr int DT = D / 16, KJ = D / 32;
-    constexpr int TILE = kBlock * D;          // elements of one (block, head) tile
-    constexpr int STEP = 4 * TILE;            // K0, K1, V0, V1
-    constexpr int PER_THREAD = STEP / 256;    // elements staged by each thread
-    constexpr int NV = PER_THREAD / 8;        // 16-byte pieces per thread
+    constexpr int TB = (int)PoolT::tile_bytes;  // bytes of one (block, head) tile
+    constexpr int NP = TB / 16;                 // its 16-byte pieces
+    constexpr int NV = (NP + 63) / 64;          // pieces each lane stages (lane + 64 v)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int g = lane >> 4, n = lane & 15;
@@ -694,19 +865,32 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     const int wave_pmax =
         wave_row0 < rows_total ? ctx - q_len + min(wave_row0 + 15, rows_total - 1) / P.G : -1;
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][STEP];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * TB];
     // the row state of each wave's tile, touched only at split ends
     __shared__ f32x4_t fin_acc[4][DT][64];
     __shared__ float2 fin_ml[4][64];
-    const size_t bstride = (size_t)P.Hkv * TILE;
-    const uint16_t *kbase = reinterpret_cast<const uint16_t *>(P.kp) + (size_t)kvh * TILE;
-    const uint16_t *vbase = reinterpret_cast<const uint16_t *>(P.vp) + (size_t)kvh * TILE;
+    const size_t bstride = (size_t)P.Hkv * TB;
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * TB;
+    const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * TB;
+    const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_zero_tile);
     const int nblk_seq = (ctx + kBlock - 1) / kBlock;
     // Wave w stages part w of every step: parts 0, 1 are the K tiles of the
-    // step's blocks 0, 1; parts 2, 3 their V. Thread piece: [off, off + PER_THREAD).
+    // step's blocks 0, 1; parts 2, 3 their V. Lane l stages pieces l + 64 v.
     const int blk = wave & 1;
     const bool is_v = wave >= 2;
-    const int off = lane * PER_THREAD;
+    // LDS position of piece pc of the wave's part (see load_step_lds and
+    // load_step8: K token order 0-3, 8-11, 4-7, 12-15; V halves swapped on
+    // rows with bit 2 set; 8-bit tiles keep their scales in place)
+    auto lds_pos = [&](int pc) {
+        if constexpr (Q8) {
+            if (pc >= D) return pc;                                   // scales
+            return is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
+                        : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
+        } else {
+            return is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
+                        : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
+        }
+    };
 
     // Block ids in register windows of 64 blocks (32 steps): lane i of bcur
     // holds table entry 64 bw + i, bnxt the next window, loaded a window
@@ -725,9 +909,11 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
         const int bn = __builtin_amdgcn_readlane(bnxt, jb & 63);
         int b = (c >> 5) == bw ? bc : bn;
         b = (jb < jb_max && b >= 0 && b < P.num_blocks) ? b : -1;
-        const uint16_t *src = b >= 0 ? (is_v ? vbase : kbase) + (size_t)b * bstride + off : g_zero_tile + off;
+        const uint8_t *src = b >= 0 ? (is_v ? vbase : kbase) + (size_t)b * bstride : zero;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) dst[v] = *reinterpret_cast<const u32x4_t *>(src + 8 * v);
+        for (int v = 0; v < NV; ++v)
+            if (NP % 64 == 0 || lane + 64 * v < NP)
+                dst[v] = *reinterpret_cast<const u32x4_t *>(src + (size_t)(lane + 64 * v) * 16);
     };
 
     TileState<DT> spl, qtr;
@@ -739,22 +925,24 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     // the same registers, then compute step c.
     auto step = [&](int c, u32x4_t (&pre)[NV]) {
         const int kc = c * kStep;
-        uint16_t *buf = lds[c & 1];
+        uint8_t *buf = lds[c & 1];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            // piece (off + 8 v) / 8 of the tile: K chunk/token or V row/half
-            const int pc = (off >> 3) + v;
-            const int pos = is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
-                                 : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
-            *reinterpret_cast<u32x4_t *>(buf + wave * TILE + 8 * pos) = pre[v];
-        }
+        for (int v = 0; v < NV; ++v)
+            if (NP % 64 == 0 || lane + 64 * v < NP)
+                *reinterpret_cast<u32x4_t *>(buf + wave * TB + lds_pos(lane + 64 * v) * 16) = pre[v];
         fetch(pre, c + 2);
         __syncthreads();
         if (kc <= wave_pmax) {
-            StepRegs<D> r;
-            load_step_lds<D>(r, buf, buf + 2 * TILE, buf + TILE, buf + 3 * TILE, g, n);
-            mask_tail<D>(r, kc, ctx, g);
-            step_update<D>(qtr, r, qop, kc, ri.prow, g, P.scale_log2);
+            Regs r;
+            if constexpr (Q8)
+                load_step8<D>(r, buf, buf + 2 * TB, buf + TB, buf + 3 * TB, g, n, [](int t) { return lds_k_pos(t); },
+                              [](int row, int h) { return lds_v_half(row, h); });
+            else
+                load_step_lds<D>(r, reinterpret_cast<const uint16_t *>(buf), reinterpret_cast<const uint16_t *>(buf + 2 * TB),
+                                 reinterpret_cast<const uint16_t *>(buf + TB),
+                                 reinterpret_cast<const uint16_t *>(buf + 3 * TB), g, n);
+            PoolT::mask(r, kc, ctx, g);
+            PoolT::update(qtr, r, qop, kc, ri.prow, g, P.scale_log2);
         }
         // quarter and split boundaries fall on step boundaries
         const int next = kc + kStep;
@@ -999,6 +1187,138 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
 }
 
 // ---------------------------------------------------------------------------
+// Scatter-write into 8-bit pools: one workgroup per 16 consecutive new tokens
+// and one KV head; 16 lanes per token. Each (token, head) row is quantized:
+// s = amax / 448, codes = E4M3 of x / s clamped to [-448, 448], rounded to
+// nearest with ties to the even code by the conversion instruction (both
+// divisions IEEE float32); a zero row stores s = 0 and zero codes. Codes and
+// scales are then placed as in the tile layout: whole blocks written in order
+// as 16-byte pieces gathered through LDS, other tokens piece by piece.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void scatter8_kernel(const uint16_t *__restrict__ kn, const uint16_t *__restrict__ vn,
+                                                      const int32_t *__restrict__ slots, int n, uint8_t *kp,
+                                                      uint8_t *vp, int num_blocks, int Hkv) {
+    constexpr int TB = q8_tile_bytes<D>();
+    constexpr int CPT = D / 16;  // channels per lane
+    const int tid = threadIdx.x;
+    const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
+    __shared__ int s_slot[kBlock];
+    __shared__ int s_full;
+    __shared__ __attribute__((aligned(16))) uint8_t kc[kBlock][D], vc[kBlock][D];
+    __shared__ float ksc[kBlock], vsc[kBlock];
+    if (tid < kBlock) {
+        const int i = i0 + tid;
+        const int sl = i < n ? slots[i] : -1;
+        s_slot[tid] = (sl >= 0 && sl < num_blocks * kBlock) ? sl : -1;
+    }
+    const int t = tid >> 4, part = tid & 15;  // token of the group, channel group
+    const int i = i0 + t;
+    const bool have = i < n;
+    float xk[CPT], xv[CPT];
+    {
+        const uint16_t *rk = kn + ((size_t)i * Hkv + h) * D + part * CPT;
+        const uint16_t *rv = vn + ((size_t)i * Hkv + h) * D + part * CPT;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            xk[c] = have ? __builtin_bit_cast(float, (uint32_t)rk[c] << 16) : 0.f;
+            xv[c] = have ? __builtin_bit_cast(float, (uint32_t)rv[c] << 16) : 0.f;
+        }
+    }
+    auto quantize = [&](float (&x)[CPT], uint8_t *codes_row, float *scale_slot) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) amax = fmaxf(amax, fabsf(x[c]));
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float sc = __fdiv_rn(amax, 448.f);
+        const float safe = sc > 0.f ? sc : 1.f;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 2) {
+            const float r0 = fminf(fmaxf(__fdiv_rn(x[c], safe), -448.f), 448.f);
+            const float r1 = fminf(fmaxf(__fdiv_rn(x[c + 1], safe), -448.f), 448.f);
+            const uint32_t w = sc > 0.f ? (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false) : 0u;
+            codes_row[part * CPT + c] = (uint8_t)(w & 0xFF);
+            codes_row[part * CPT + c + 1] = (uint8_t)((w >> 8) & 0xFF);
+        }
+        if (part == 0) *scale_slot = sc;
+    };
+    quantize(xk, kc[t], &ksc[t]);
+    quantize(xv, vc[t], &vsc[t]);
+    __syncthreads();
+    if (tid < 64) {
+        const int sl0 = s_slot[0];
+        const bool ok = tid >= kBlock || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlock == 0);
+        const bool full = __all(ok);
+        if (tid == 0) s_full = full;
+    }
+    __syncthreads();
+    // bytes of piece pc of a tile, from the group's codes (token tok of the
+    // group sits at offset tok of the block in the whole-block case)
+    auto k_piece = [&](int pc, int tok) {  // K piece ((p*4 + g)*16 + o): jj = 0 bytes then jj = 1 bytes
+        const int q = pc >> 4, p = q >> 2, g = q & 3;
+        uint8_t b[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            b[e] = kc[tok][64 * p + 8 * g + e];
+            b[8 + e] = kc[tok][64 * p + 32 + 8 * g + e];
+        }
+        u32x4_t w;
+        __builtin_memcpy(&w, b, 16);
+        return w;
+    };
+    if (s_full) {
+        const int blk = s_slot[0] / kBlock;
+        uint8_t *kt = kp + ((size_t)blk * Hkv + h) * TB;
+        uint8_t *vt = vp + ((size_t)blk * Hkv + h) * TB;
+        for (int pc = tid; pc < D; pc += 256) {  // K code pieces: (p*4 + g)*16 + o
+            *reinterpret_cast<u32x4_t *>(kt + (size_t)pc * 16) = k_piece(pc, pc & 15);
+            // V piece ((d*16 + nn)*2 + hh): dd = 0 then dd = 1, tokens 8 hh + e
+            const int row = pc >> 1, hh = pc & 1, d = row >> 4, nn = row & 15;
+            uint8_t b[16];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                b[e] = vc[8 * hh + e][16 * (2 * d) + nn];
+                b[8 + e] = vc[8 * hh + e][16 * (2 * d + 1) + nn];
+            }
+            u32x4_t w;
+            __builtin_memcpy(&w, b, 16);
+            *reinterpret_cast<u32x4_t *>(vt + (size_t)pc * 16) = w;
+        }
+        if (tid < kBlock) {
+            reinterpret_cast<float *>(kt + 16 * D)[tid] = ksc[tid];
+            reinterpret_cast<float *>(vt + 16 * D)[tid] = vsc[tid];
+        }
+        return;
+    }
+    const int sl = s_slot[t];
+    if (!have || sl < 0) return;
+    const int blk = sl / kBlock, o = sl % kBlock;
+    uint8_t *kt = kp + ((size_t)blk * Hkv + h) * TB;
+    uint8_t *vt = vp + ((size_t)blk * Hkv + h) * TB;
+    // K: the token's D/8 runs of 8 codes (p, g, jj)
+    for (int r = part; r < D / 8; r += 16) {
+        const int p = r >> 3, g = (r >> 1) & 3, jj = r & 1;
+        uint8_t b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) b[e] = kc[t][64 * p + 32 * jj + 8 * g + e];
+        u32x2_t w;
+        __builtin_memcpy(&w, b, 8);
+        *reinterpret_cast<u32x2_t *>(kt + ((size_t)((p * 4 + g) * kBlock + o)) * 16 + jj * 8) = w;
+    }
+    // V: one code per channel
+#pragma unroll
+    for (int c = part * CPT; c < part * CPT + CPT; ++c) {
+        const int dt = c >> 4, nn = c & 15, d = dt >> 1, dd = dt & 1, hh = o >> 3, e = o & 7;
+        vt[(((d * 16 + nn) * 2 + hh) * 2 + dd) * 8 + e] = vc[t][c];
+    }
+    if (part == 0) {
+        reinterpret_cast<float *>(kt + 16 * D)[o] = ksc[t];
+        reinterpret_cast<float *>(vt + 16 * D)[o] = vsc[t];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 // Workspace: the split maxima and sums, then the split accumulators.
@@ -1035,39 +1355,40 @@ static int device_cus() {
     return cus;
 }
 
-template <int D, int NT, bool APPEND>
+template <int D, int NT, bool APPEND, bool Q8>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
     const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.max_splits;
     if constexpr (NT == 1) {
         if (nwg <= device_cus()) {
-            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, Q8>), dim3((unsigned)nwg), dim3(256), 0, st, P);
             return;
         }
     }
-    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND, Q8>), dim3((unsigned)nwg), dim3(256), 0, st, P);
 }
 
-template <int D, int NT>
+template <int D, int NT, bool Q8>
 static void launch_parallel(const AttnParams &P, hipStream_t st) {
-    if (P.k_new) launch_parallel_as<D, NT, true>(P, st);
-    else launch_parallel_as<D, NT, false>(P, st);
+    if constexpr (Q8) launch_parallel_as<D, NT, false, true>(P, st);
+    else if (P.k_new) launch_parallel_as<D, NT, true, false>(P, st);
+    else launch_parallel_as<D, NT, false, false>(P, st);
 }
 
-template <int D>
-static void launch_bf16(const AttnParams &P, int max_q_len, int max_context_len, int total_rows,
+template <int D, bool Q8>
+static void launch_mfma(const AttnParams &P, int max_q_len, int max_context_len, int total_rows,
                         hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
     const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
-        launch_parallel<D, 1>(P, st);
+        launch_parallel<D, 1, Q8>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P);
     } else {
-        launch_parallel<D, 2>(P, st);
+        launch_parallel<D, 2, Q8>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
-        hipLaunchKernelGGL((attn_sequential<D>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((attn_sequential<D, Q8>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
     }
 }
 
@@ -1098,7 +1419,7 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                         float scale, const float *sinks, float *out, void *workspace, size_t workspace_bytes,
                         void *hip_stream, const AppendArgs *app) {
-    if (dtype != KV_BF16 && dtype != KV_F32)
+    if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: dtype %d not supported", dtype);
     if (head_dim != 64 && head_dim != 128)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: head_dim %d not supported (64, 128)", head_dim);
@@ -1188,8 +1509,11 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
 
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
-        if (head_dim == 64) launch_bf16<64>(P, max_q_len, max_context_len, total_q_rows, st);
-        else launch_bf16<128>(P, max_q_len, max_context_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma<64, false>(P, max_q_len, max_context_len, total_q_rows, st);
+        else launch_mfma<128, false>(P, max_q_len, max_context_len, total_q_rows, st);
+    } else if (dtype == KV_FP8) {
+        if (head_dim == 64) launch_mfma<64, true>(P, max_q_len, max_context_len, total_q_rows, st);
+        else launch_mfma<128, true>(P, max_q_len, max_context_len, total_q_rows, st);
     } else {
         const dim3 grid(total_q_rows, num_q_heads);
         if (head_dim == 64) hipLaunchKernelGGL((attn_f32<64>), grid, dim3(64), 0, st, P);
@@ -1247,8 +1571,10 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
                       void *k_pool, void *v_pool, int32_t num_blocks, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int32_t dtype, void *hip_stream) {
     using namespace pkv;
-    if (dtype != KV_BF16 && dtype != KV_F32)
+    if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8)
         PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: dtype %d not supported", dtype);
+    if (dtype == KV_FP8 && head_dim != 64 && head_dim != 128)
+        PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: 8-bit pools need head_dim 64 or 128, not %d", head_dim);
     if (block_size != kBlock)
         PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: block_size %d not supported (16)", block_size);
     if (head_dim <= 0 || head_dim % 16 || head_dim > 256)
@@ -1266,7 +1592,18 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     const dim3 grid((unsigned)groups, (unsigned)num_kv_heads);
-    if (dtype == KV_BF16)
+    if (dtype == KV_FP8) {
+        auto kn = static_cast<const uint16_t *>(k_new);
+        auto vn = static_cast<const uint16_t *>(v_new);
+        auto kpp = static_cast<uint8_t *>(k_pool);
+        auto vpp = static_cast<uint8_t *>(v_pool);
+        if (head_dim == 64)
+            hipLaunchKernelGGL(scatter8_kernel<64>, grid, dim3(256), 0, st, kn, vn, slot_mapping, n, kpp, vpp, num_blocks,
+                               num_kv_heads);
+        else
+            hipLaunchKernelGGL(scatter8_kernel<128>, grid, dim3(256), 0, st, kn, vn, slot_mapping, n, kpp, vpp,
+                               num_blocks, num_kv_heads);
+    } else if (dtype == KV_BF16)
         hipLaunchKernelGGL(scatter_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(k_new),
                            static_cast<const uint16_t *>(v_new), slot_mapping, n, static_cast<uint16_t *>(k_pool),
                            static_cast<uint16_t *>(v_pool), num_blocks, num_kv_heads, head_dim);

@@ -40,13 +40,15 @@ class Staged:
 
 
 def _torch_dtype(name):
+    """Element type of the pools for a workload dtype ("fp8": 8-bit pools)."""
     import torch
-    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[name]
 
 
 def _to_device(a, dtype_name, device):
+    """Rows (queries, new K/V) to the device; "fp8" workloads carry bf16 rows."""
     import torch
-    if dtype_name == "bf16":
+    if dtype_name in ("bf16", "fp8"):
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
         return t.view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
@@ -77,7 +79,10 @@ def stage(w, device="cuda", copies: int = 1, poison: bool = True, scatter_step: 
     dt = _torch_dtype(w.dtype)
     Hkv, D = w.num_kv_heads, w.head_dim
     k0, v0 = empty_pools(w.num_blocks, Hkv, D, dt, device)
-    if poison:
+    if poison and w.dtype == "fp8":
+        k0.fill_(0xFF)   # code 0xFF is NaN in E4M3FN, four 0xFF bytes a NaN scale
+        v0.fill_(0xFF)
+    elif poison:
         k0.fill_(float("nan"))
         v0.fill_(float("nan"))
     else:

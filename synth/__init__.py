@@ -55,7 +55,7 @@ class Seq:
 @dataclass
 class Workload:
     name: str
-    dtype: str               # 'bf16' | 'f32' (storage and Q type)
+    dtype: str               # 'bf16' | 'f32' (storage and Q type) | 'fp8' (bf16 rows, 8-bit pools)
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
@@ -164,22 +164,27 @@ def tiny_decode(seed=1001):
                  pool_blocks=64, scale=1.0 / 8.0)
 
 
-def mid_decode(seed=1002):
-    """4 decode rows, contexts ~ U[780, 820], 32 q / 8 KV heads, D 128, bf16."""
+def _named(name, dtype):
+    return name if dtype == "bf16" else f"{name}_{dtype}"
+
+
+def mid_decode(seed=1002, dtype="bf16"):
+    """4 decode rows, contexts ~ U[780, 820], 32 q / 8 KV heads, D 128, bf16
+    (dtype "fp8": the same bf16 rows stored in 8-bit pools)."""
     rng = np.random.default_rng(seed)
     ctxs = rng.integers(780, 820, size=4, endpoint=True)
-    return build("mid_decode", "bf16", 32, 8, 128, ctxs, [1] * 4, seed + 10_000)
+    return build(_named("mid_decode", dtype), dtype, 32, 8, 128, ctxs, [1] * 4, seed + 10_000)
 
 
-def sink_decode(seed=1003):
+def sink_decode(seed=1003, dtype="bf16"):
     """32 decode rows, contexts log-uniform in [1024, 8192], 64 q / 8 KV heads,
     D 64, bf16, one sink logit ~ N(0, 1) per query head."""
     rng = np.random.default_rng(seed)
     ctxs = _log_uniform_int(rng, 1024, 8192, 32)
-    return build("sink_decode", "bf16", 64, 8, 64, ctxs, [1] * 32, seed + 10_000, sinks=True)
+    return build(_named("sink_decode", dtype), dtype, 64, 8, 64, ctxs, [1] * 32, seed + 10_000, sinks=True)
 
 
-def mixed_step(seed=1004, n_decode=48, prefix=2900, tail=(64, 1024), n_prefill=2, chunk=1024):
+def mixed_step(seed=1004, n_decode=48, prefix=2900, tail=(64, 1024), n_prefill=2, chunk=1024, dtype="bf16"):
     """48 decode rows sharing a 2900-token prefix with private tails ~ U[64, 1024]
     plus one new token each, and 2 prefill chunks of 1024 causal rows on fresh
     1024-token contexts; 32 q / 8 KV heads, D 128, bf16."""
@@ -187,18 +192,21 @@ def mixed_step(seed=1004, n_decode=48, prefix=2900, tail=(64, 1024), n_prefill=2
     tails = rng.integers(tail[0], tail[1], size=n_decode, endpoint=True)
     ctxs = [prefix + int(t) + 1 for t in tails] + [chunk] * n_prefill
     q_lens = [1] * n_decode + [chunk] * n_prefill
-    return build("mixed_step", "bf16", 32, 8, 128, ctxs, q_lens, seed + 10_000,
+    return build(_named("mixed_step", dtype), dtype, 32, 8, 128, ctxs, q_lens, seed + 10_000,
                  shared_prefix=prefix, n_shared=n_decode)
 
 
-def verify_window(seed=1005, n=16, lo=4096, hi=16384, window=8):
+def verify_window(seed=1005, n=16, lo=4096, hi=16384, window=8, dtype="bf16"):
     """16 sequences, contexts ~ U[4096, 16384] including 8 draft rows each,
     causal inside the window; 32 q / 8 KV heads, D 128, bf16."""
     rng = np.random.default_rng(seed)
     ctxs = rng.integers(lo, hi, size=n, endpoint=True)
-    return build("verify_window", "bf16", 32, 8, 128, ctxs, [window] * n, seed + 10_000)
+    return build(_named("verify_window", dtype), dtype, 32, 8, 128, ctxs, [window] * n, seed + 10_000)
 
 
 def by_name(name, **kw):
+    """A named workload; the suffix "_fp8" selects 8-bit pools for the same rows."""
+    if name.endswith("_fp8") and name != "tiny_decode_fp8":
+        return by_name(name[:-4], dtype="fp8", **kw)
     return {"tiny_decode": tiny_decode, "mid_decode": mid_decode, "sink_decode": sink_decode,
             "mixed_step": mixed_step, "verify_window": verify_window}[name](**kw)

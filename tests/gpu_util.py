@@ -7,7 +7,7 @@ import numpy as np
 import oracle
 import synth
 
-TOL = {"bf16": 2e-3, "f32": 1e-5}
+TOL = {"bf16": 2e-3, "f32": 1e-5, "fp8": 2e-3}
 
 
 def oracle_side(w, fill_nan=True):
@@ -23,17 +23,31 @@ def oracle_side(w, fill_nan=True):
         row, nb, ctx, slots = a.alloc(s, seq.tokens[seq.ctx - seq.n_step:], maxb)
         tables.append(row)
         step.append(slots)
-    nan = np.uint16(0x7FC0) if w.dtype == "bf16" else np.float32(np.nan)
-    kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype,
-                                fill=nan if fill_nan else None)
+    if w.dtype == "fp8":
+        kp, vp = oracle.fp8_empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim,
+                                        fill=np.uint8(0xFF) if fill_nan else None)
+        put = oracle.fp8_scatter
+    else:
+        nan = np.uint16(0x7FC0) if w.dtype == "bf16" else np.float32(np.nan)
+        kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype,
+                                    fill=nan if fill_nan else None)
+        put = oracle.scatter
     for s, seq in enumerate(w.seqs):
         n_res = seq.ctx - seq.n_step
-        oracle.scatter(kp, vp, seq.k[:n_res], seq.v[:n_res], res[s])
-        oracle.scatter(kp, vp, seq.k[n_res:], seq.v[n_res:], step[s])
+        put(kp, vp, seq.k[:n_res], seq.v[:n_res], res[s])
+        put(kp, vp, seq.k[n_res:], seq.v[n_res:], step[s])
     tables = np.array(tables, dtype=np.int32)
     out = oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
                                  w.num_kv_heads, w.scale, w.sinks, w.dtype)
     return tables, kp, vp, out
+
+
+def _dense(rows, dtype):
+    """Dense K or V rows as the attention sees them: for 8-bit pools the
+    oracle's quantize-then-dequantize of each (token, KV head) row."""
+    if dtype == "fp8":
+        return oracle.fp8_dequantize(*oracle.fp8_quantize_rows(rows))
+    return rows
 
 
 def oracle_rows(w, rows):
@@ -44,8 +58,8 @@ def oracle_rows(w, rows):
         s = int(np.searchsorted(qsl, i, side="right") - 1)
         seq = w.seqs[s]
         p = seq.ctx - seq.q_len + (i - int(qsl[s]))
-        ks.append(seq.k[:p + 1])
-        vs.append(seq.v[:p + 1])
+        ks.append(_dense(seq.k[:p + 1], w.dtype))
+        vs.append(_dense(seq.v[:p + 1], w.dtype))
         qsel.append(w.q[i])
     q = np.stack(qsel)
     return oracle.attention(q, ks, vs, np.arange(len(rows) + 1, dtype=np.int32), w.num_q_heads,

@@ -27,6 +27,8 @@ def pk():
 
 def _bits(t):
     import torch
+    if t.dtype == torch.uint8:
+        return t.cpu().numpy()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).cpu().numpy()
     return t.cpu().numpy().view(np.uint32)
@@ -81,6 +83,12 @@ def test_sink_decode_large_grid(pk):
     _check(pk, synth.sink_decode(), oracle_sample=[0, 7, 31])
 
 
+def test_decode_into_8bit_pools(pk):
+    """Decode rows into 8-bit pools: the new tokens are quantized by the
+    scatter launch, then attended."""
+    _check(pk, synth.sink_decode(dtype="fp8"), oracle_sample=[0, 7, 31])
+
+
 @pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 64), (40, 2, 128), (4, 4, 128)])
 def test_block_and_split_boundaries(pk, Hq, Hkv, D):
     """New tokens at every offset class in a block and next to split edges;
@@ -97,9 +105,9 @@ def test_resident_token_slot_minus_one(pk):
     _check(pk, w, resident_slots=(1, 3))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
 def test_other_batches_scatter_first(pk, dtype):
-    """Verify windows, prefill chunks and fp32 pools take the scatter launch
-    first; the result is the same as two calls."""
+    """Verify windows, prefill chunks, fp32 and 8-bit pools take the scatter
+    launch first; the result is the same as two calls."""
     w = custom(dtype, 16, 4, 64, [300, 1100, 70, 40], [8, 130, 1, 40], seed=99)
     _check(pk, w)
