@@ -83,6 +83,11 @@ def _lib():
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]
+        lib.oracle_attention_masked.restype = ctypes.c_int
+        lib.oracle_attention_masked.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32]
         _LIB = lib
     return _LIB
 
@@ -151,17 +156,27 @@ def scatter(k_pool, v_pool, k_new, v_new, slots):
     v_pool[b, :, :, o] = vn
 
 
-def gather(k_pool, v_pool, block_table_row, ctx):
-    """Dense K, V [ctx, Hkv, D] of one sequence, read through its block table."""
+def gather(k_pool, v_pool, block_table_row, ctx, dropped_nan=False):
+    """Dense K, V [ctx, Hkv, D] of one sequence, read through its block table.
+    dropped_nan: table entries -1 (blocks freed below a sliding window) give
+    NaN rows instead of an error."""
     nb, hkv, dx, B, X = k_pool.shape
     t = np.arange(ctx, dtype=np.int64)
     bt = np.asarray(block_table_row, dtype=np.int64)
     b = bt[t // B]
-    if ctx and (b.min() < 0 or b.max() >= nb):
+    gone = b < 0 if dropped_nan else np.zeros(ctx, dtype=bool)
+    if ctx and (b[~gone].min(initial=0) < 0 or b.max(initial=0) >= nb):
         raise ValueError("block table points outside the pool")
+    b = np.where(gone, 0, b)
     o = t % B
     k = k_pool[b, :, :, o, :].reshape(ctx, hkv, dx * X)
     v = v_pool[b, :, :, o]
+    if gone.any():
+        nan = np.uint16(0x7FC0) if k.dtype == np.uint16 else np.float32(np.nan)
+        k = k.copy()
+        v = v.copy()
+        k[gone] = nan
+        v[gone] = nan
     return k, v
 
 
@@ -171,11 +186,13 @@ def gather(k_pool, v_pool, block_table_row, ctx):
 
 
 def attention(q, k_seqs, v_seqs, qsl, num_q_heads, num_kv_heads, scale, sinks=None,
-              dtype="f32", threads=None):
+              dtype="f32", threads=None, tree_mask=None, window=0):
     """fp64 attention over gathered K/V (see attention.c).
 
     q: [total_rows, Hq, D] storage dtype; k_seqs/v_seqs: lists of [ctx_s, Hkv, D];
-    qsl: [S+1]; sinks: [Hq] float32 or None. Returns float64 [total_rows, Hq, D].
+    qsl: [S+1]; sinks: [Hq] float32 or None; tree_mask: [total_rows] uint32 or
+    None (causal); window: sliding window in keys, 0 = none.
+    Returns float64 [total_rows, Hq, D].
     """
     kv64 = dtype == "fp8"   # K/V come as float64 dequantized values; q is bf16
     q32 = np.ascontiguousarray(to_f32(q, "bf16" if kv64 else dtype))
@@ -193,29 +210,43 @@ def attention(q, k_seqs, v_seqs, qsl, num_q_heads, num_kv_heads, scale, sinks=No
     qsl = np.ascontiguousarray(np.asarray(qsl, dtype=np.int32))
     out = np.zeros((int(qsl[-1]), num_q_heads, D), dtype=np.float64)
     sk = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, dtype=np.float32))
-    fn = _lib().oracle_attention_kv64 if kv64 else _lib().oracle_attention
-    rc = fn(
-        q32.ctypes.data, k32.ctypes.data, v32.ctypes.data, key_start.ctypes.data, qsl.ctypes.data,
-        len(ctxs), num_q_heads, num_kv_heads, D, float(scale),
-        None if sk is None else sk.ctypes.data, out.ctypes.data,
-        int(threads or default_threads()))
+    nthr = int(threads or default_threads())
+    if tree_mask is None and not window:
+        fn = _lib().oracle_attention_kv64 if kv64 else _lib().oracle_attention
+        rc = fn(
+            q32.ctypes.data, k32.ctypes.data, v32.ctypes.data, key_start.ctypes.data, qsl.ctypes.data,
+            len(ctxs), num_q_heads, num_kv_heads, D, float(scale),
+            None if sk is None else sk.ctypes.data, out.ctypes.data, nthr)
+    else:
+        tm = None
+        if tree_mask is not None:
+            tm = np.ascontiguousarray(np.asarray(tree_mask, dtype=np.uint32))
+            if tm.shape != (int(qsl[-1]),):
+                raise ValueError("tree_mask needs one word per query row")
+        rc = _lib().oracle_attention_masked(
+            q32.ctypes.data, k32.ctypes.data, v32.ctypes.data, int(kv64), key_start.ctypes.data,
+            qsl.ctypes.data, len(ctxs), num_q_heads, num_kv_heads, D, float(scale),
+            None if sk is None else sk.ctypes.data, None if tm is None else tm.ctypes.data, int(window),
+            out.ctypes.data, nthr)
     if rc != 0:
         raise ValueError("oracle_attention: inconsistent sizes")
     return out
 
 
 def paged_attention(q, k_pool, v_pool, block_tables, context_lens, qsl, num_q_heads,
-                    num_kv_heads, scale, sinks=None, dtype="f32", threads=None):
+                    num_kv_heads, scale, sinks=None, dtype="f32", threads=None, tree_mask=None, window=0):
     """Gather every sequence through its block table, then attention()."""
     ks, vs = [], []
+    dropped = bool(window)   # blocks below a sliding window may be freed (-1)
     for s, ctx in enumerate(context_lens):
         if dtype == "fp8":
-            k, v = fp8_gather(k_pool, v_pool, block_tables[s], int(ctx))
+            k, v = fp8_gather(k_pool, v_pool, block_tables[s], int(ctx), dropped)
         else:
-            k, v = gather(k_pool, v_pool, block_tables[s], int(ctx))
+            k, v = gather(k_pool, v_pool, block_tables[s], int(ctx), dropped)
         ks.append(k)
         vs.append(v)
-    return attention(q, ks, vs, qsl, num_q_heads, num_kv_heads, scale, sinks, dtype, threads)
+    return attention(q, ks, vs, qsl, num_q_heads, num_kv_heads, scale, sinks, dtype, threads,
+                     tree_mask=tree_mask, window=window)
 
 
 # ----------------------------------------------------------------------------
@@ -341,8 +372,9 @@ def fp8_scatter(k_pool, v_pool, k_new_bf16, v_new_bf16, slots):
             v_pool[b, h, 16 * D + 4 * o:16 * D + 4 * o + 4] = np.frombuffer(vs[i, h].tobytes(), np.uint8)
 
 
-def fp8_gather(k_pool, v_pool, block_table_row, ctx):
-    """Dequantized float64 K, V [ctx, Hkv, D] of one sequence."""
+def fp8_gather(k_pool, v_pool, block_table_row, ctx, dropped_nan=False):
+    """Dequantized float64 K, V [ctx, Hkv, D] of one sequence (dropped_nan as
+    for gather)."""
     nb, hkv, tile = k_pool.shape
     D = (tile - 64) // 16
     offk, offv = _fp8_k_offsets(D), _fp8_v_offsets(D)
@@ -351,6 +383,10 @@ def fp8_gather(k_pool, v_pool, block_table_row, ctx):
     v = np.zeros((ctx, hkv, D))
     for t in range(ctx):
         b, o = int(bt[t // 16]), t % 16
+        if b < 0 and dropped_nan:
+            k[t] = np.nan
+            v[t] = np.nan
+            continue
         if b < 0 or b >= nb:
             raise ValueError("block table points outside the pool")
         sk = k_pool[b, :, 16 * D + 4 * o:16 * D + 4 * o + 4].copy().view(np.float32)[:, 0]
@@ -449,7 +485,8 @@ class Allocator:
         # phase 1 (read only): hits can only form an unbroken run of full new
         # blocks starting at a block boundary
         hits = []
-        if n0 % B == 0:
+        dropped = st is not None and st.get("dropped", False)
+        if n0 % B == 0 and not dropped:
             parent_hash = hashes[-1] if hashes else 0
             parent = blocks[-1] if blocks else None
             for j in range(nb0, nb1):
@@ -472,7 +509,7 @@ class Allocator:
             raise OutOfBlocks("pool exhausted")
 
         # phase 2: commit
-        st = self.seqs.setdefault(seq_id, {"tokens": [], "blocks": [], "hashes": []})
+        st = self.seqs.setdefault(seq_id, {"tokens": [], "blocks": [], "hashes": [], "dropped": False})
         slots = []
         # fill the existing partial block
         if n0 % B:
@@ -484,7 +521,8 @@ class Allocator:
                 ph = st["hashes"][-1] if st["hashes"] else 0
                 h = self.hash_fn(ph, all_tokens[j * B:(j + 1) * B])
                 st["hashes"].append(h)
-                self._register(b, h, st["blocks"][j - 1] if j > 0 else None, all_tokens[j * B:(j + 1) * B])
+                if not st["dropped"]:
+                    self._register(b, h, st["blocks"][j - 1] if j > 0 else None, all_tokens[j * B:(j + 1) * B])
         for b, h in hits:
             if self.in_free[b]:
                 self.free.remove(b)
@@ -504,7 +542,8 @@ class Allocator:
                 ph = st["hashes"][-1] if st["hashes"] else 0
                 h = self.hash_fn(ph, blk_tokens)
                 st["hashes"].append(h)
-                self._register(b, h, parent, blk_tokens)
+                if not st["dropped"]:
+                    self._register(b, h, parent, blk_tokens)
         st["tokens"] = all_tokens
         row = st["blocks"] + [-1] * (max_blocks - len(st["blocks"]))
         return row, len(st["blocks"]), n1, slots
@@ -514,13 +553,144 @@ class Allocator:
         if st is None:
             raise KeyError(seq_id)
         for b in reversed(st["blocks"]):
+            if b < 0:
+                continue
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
                 self.in_free[b] = True
+
+    def drop_prefix(self, seq_id: int, first_kept: int):
+        """Free the blocks wholly below position first_kept (a sliding window's
+        rows never see them again); they read -1 in the table from now on, and
+        the sequence neither shares nor registers blocks afterwards."""
+        st = self.seqs.get(seq_id)
+        if st is None:
+            raise KeyError(seq_id)
+        if first_kept < 0:
+            raise ValueError("first_kept must be >= 0")
+        upto = min(first_kept, len(st["tokens"])) // self.B
+        for j in reversed(range(upto)):
+            b = st["blocks"][j]
+            if b < 0:
+                continue
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+                self.in_free[b] = True
+            st["blocks"][j] = -1
+            st["dropped"] = True
+
+    def truncate(self, seq_id: int, new_len: int):
+        """Roll a sequence back to its first new_len tokens (rejected drafts,
+        TensorFold page, GPU accept kernel section: a rollback restores every
+        state after the accepted path, the KV cache included).
+
+        Blocks wholly past new_len go back as release() returns them (last
+        block first, hash entries kept). When new_len ends inside a block that
+        was full, the slots after it will be written again: a block the
+        sequence alone holds loses its hash entry and starts a new reuse
+        generation (so no chain through its old contents can be followed); a
+        block other sequences also hold is replaced by a fresh block popped
+        from the free list, and (src, dst) is returned for the caller to copy
+        on the device before writing to it. Returns (src, dst) or (-1, -1).
+        Raises OutOfBlocks with the state unchanged when a copy needs a block
+        and none would be free.
+        """
+        st = self.seqs.get(seq_id)
+        if st is None:
+            raise KeyError(seq_id)
+        n = len(st["tokens"])
+        if not 0 <= new_len <= n:
+            raise ValueError("new_len must lie in 0 .. context length")
+        B = self.B
+        keep = -(-new_len // B)
+        drop = st["blocks"][keep:]
+        tail_was_full = new_len % B != 0 and len(st["hashes"]) >= keep
+        tail = st["blocks"][keep - 1] if tail_was_full else None
+        if tail_was_full and tail < 0:
+            raise ValueError("new_len ends inside a dropped block")
+        shared = tail_was_full and self.ref[tail] > 1
+        if shared:
+            freed = sum(1 for b in drop if b >= 0 and self.ref[b] == 1)
+            if len(self.free) + freed < 1:
+                raise OutOfBlocks("no free block for the copy of a shared tail block")
+        for b in reversed(drop):
+            if b < 0:
+                continue
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+                self.in_free[b] = True
+        st["blocks"] = st["blocks"][:keep]
+        st["hashes"] = st["hashes"][:new_len // B]
+        st["tokens"] = st["tokens"][:new_len]
+        if not tail_was_full:
+            return -1, -1
+        if shared:
+            self.ref[tail] -= 1
+            dst = self._pop()
+            st["blocks"][keep - 1] = dst
+            return tail, dst
+        h = self.blk_hash[tail]
+        if h is not None:
+            del self.table[h]
+            self.blk_hash[tail] = None
+        self.gen[tail] += 1
+        return -1, -1
+
+    def table_row(self, seq_id: int, max_blocks: int):
+        st = self.seqs[seq_id]
+        return st["blocks"] + [-1] * (max_blocks - len(st["blocks"]))
 
     def stats(self):
         free = len(self.free)
         cached = sum(1 for b in self.free if self.blk_hash[b] is not None)
         live = sum(1 for r in self.ref if r > 0)
         return free, cached, live
+
+
+def copy_blocks(k_pool, v_pool, src, dst):
+    """Copy whole blocks (every KV head, every slot) src[i] -> dst[i] in both
+    pools, in order; the copy a truncate into a shared block asks for."""
+    for a, b in zip(np.asarray(src, dtype=np.int64), np.asarray(dst, dtype=np.int64)):
+        k_pool[b] = k_pool[a]
+        v_pool[b] = v_pool[a]
+
+
+# ----------------------------------------------------------------------------
+# tree verify windows
+# ----------------------------------------------------------------------------
+#
+# TensorFold page, section on the GPU accept kernel: a verify round lays its
+# drafts out as a chain or a tree of at most 16 rows, the tree carrying
+# alternative paths; the accept step walks from the root along the first child
+# whose draft token equals the target model's choice. Window row r's parent is
+# parents[r] (a row before r, or -1 for the token before the window).
+
+
+def tree_masks(parents):
+    """Ancestor masks of a window: bit j of masks[r] is set when row j is r or
+    one of its ancestors."""
+    masks = []
+    for r, p in enumerate(parents):
+        p = int(p)
+        if not -1 <= p < r:
+            raise ValueError("a parent must be -1 or an earlier row")
+        masks.append((1 << r) | (masks[p] if p >= 0 else 0))
+    return np.array(masks, dtype=np.uint32)
+
+
+def accept_path(parents, draft_tokens, choices, root_choice):
+    """Walk the tree: from the root, while some child of the current node has
+    draft token equal to the current choice, move to the first such child (in
+    row order); the choice is then that row's. choices[r] is the target's
+    token after row r; root_choice the target's token after the root.
+    Returns (accepted rows in path order, the target's token after the path)."""
+    path, cur, want = [], -1, int(root_choice)
+    while True:
+        nxt = next((r for r in range(len(parents)) if int(parents[r]) == cur and int(draft_tokens[r]) == want), None)
+        if nxt is None:
+            return path, want
+        path.append(nxt)
+        cur, want = nxt, int(choices[nxt])

@@ -1,0 +1,335 @@
+"""Pins of the oracle's tree windows, sliding windows, truncate and accept
+walk (CPU only).
+
+Tree windows and the accept walk follow the TensorFold page, section on the
+GPU accept kernel (drafts laid out as a chain or a tree of at most 16 rows;
+the accepted path follows the first child whose token equals the target's
+choice; a rollback restores the KV cache after the accepted path). Sliding
+windows follow the sliding-window attention the same pages give their
+drafters and models.
+
+The masked attention is checked against a dense brute force whose mask matrix
+is built by walking parent pointers (not from the mask words the oracle
+reads), against closed forms (a one-key window returns that key's value), and
+against the causal oracle on compacted sequences (a tree row sees exactly its
+ancestors, so it equals a causal row over resident keys + ancestors + itself).
+"""
+import copy
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import oracle
+
+
+def _ancestors(parents, r):
+    out = {r}
+    p = int(parents[r])
+    while p >= 0:
+        out.add(p)
+        p = int(parents[p])
+    return out
+
+
+def brute_masked(q, ks, vs, q_lens, parents_list, window, Hq, Hkv, scale, sinks=None):
+    """Dense attention with an explicit [q_len, ctx] visibility matrix: key t
+    is visible to row r when t <= p, t > p - window (window > 0), and, inside
+    the window of a tree, t - base is r or one of r's ancestors (walked from
+    the parent pointers)."""
+    outs, row = [], 0
+    for k, v, ql, parents in zip(ks, vs, q_lens, parents_list):
+        ctx = k.shape[0]
+        base = ctx - ql
+        vis = np.zeros((ql, ctx), dtype=bool)
+        for r in range(ql):
+            p = base + r
+            anc = None if parents is None else _ancestors(parents, r)
+            for t in range(ctx):
+                ok = t <= p and (window == 0 or t > p - window)
+                if ok and anc is not None and t >= base:
+                    ok = (t - base) in anc
+                vis[r, t] = ok
+        kr = np.repeat(k.astype(np.float64), Hq // Hkv, axis=1)
+        vr = np.repeat(v.astype(np.float64), Hq // Hkv, axis=1)
+        qs = q[row:row + ql].astype(np.float64)
+        scores = np.einsum("rhd,thd->hrt", qs, kr) * scale
+        scores = np.where(vis[None], scores, -np.inf)
+        if sinks is not None:
+            col = np.broadcast_to(np.asarray(sinks, np.float64)[:, None, None], (Hq, ql, 1))
+            scores = np.concatenate([scores, col], axis=2)
+            vr = np.concatenate([vr, np.zeros((1,) + vr.shape[1:])], axis=0)
+        w = softmax(scores, axis=2)
+        outs.append(np.einsum("hrt,thd->rhd", w, vr))
+        row += ql
+    return np.concatenate(outs, axis=0)
+
+
+def random_parents(rng, n):
+    return [-1] + [int(rng.integers(-1, r)) for r in range(1, n)]
+
+
+def case(rng, ctxs, q_lens, Hq=4, Hkv=2, D=8, sinks=False):
+    q = rng.standard_normal((sum(q_lens), Hq, D)).astype(np.float32)
+    ks = [rng.standard_normal((c, Hkv, D)).astype(np.float32) for c in ctxs]
+    vs = [rng.standard_normal((c, Hkv, D)).astype(np.float32) for c in ctxs]
+    sk = rng.standard_normal(Hq).astype(np.float32) * 2 if sinks else None
+    qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    return q, ks, vs, qsl, sk
+
+
+@pytest.mark.parametrize("sinks", [False, True])
+@pytest.mark.parametrize("window", [0, 1, 3, 17])
+def test_tree_and_window_against_brute_force(sinks, window):
+    rng = np.random.default_rng(11 + window + 100 * sinks)
+    ctxs, q_lens = [9, 30, 16, 40], [3, 16, 1, 12]
+    q, ks, vs, qsl, sk = case(rng, ctxs, q_lens, sinks=sinks)
+    parents_list = [random_parents(rng, n) for n in q_lens]
+    masks = np.concatenate([oracle.tree_masks(p) for p in parents_list])
+    got = oracle.attention(q, ks, vs, qsl, 4, 2, 0.4, sk, "f32", tree_mask=masks, window=window)
+    want = brute_masked(q, ks, vs, q_lens, parents_list, window, 4, 2, 0.4, sk)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 5, 64])
+def test_window_without_tree_against_brute_force(window):
+    rng = np.random.default_rng(21 + window)
+    ctxs, q_lens = [70, 33, 5], [1, 20, 5]
+    q, ks, vs, qsl, sk = case(rng, ctxs, q_lens, sinks=True)
+    got = oracle.attention(q, ks, vs, qsl, 4, 2, 0.3, sk, "f32", window=window)
+    want = brute_masked(q, ks, vs, q_lens, [None] * 3, window, 4, 2, 0.3, sk)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_chain_mask_is_causal_exactly():
+    rng = np.random.default_rng(31)
+    ctxs, q_lens = [40, 17], [16, 8]
+    q, ks, vs, qsl, sk = case(rng, ctxs, q_lens, sinks=True)
+    chain = np.concatenate([oracle.tree_masks(list(range(-1, n - 1))) for n in q_lens])
+    assert chain[3] == 0b1111
+    a = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, sk, "f32")
+    b = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, sk, "f32", tree_mask=chain)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_window_covering_the_context_changes_nothing():
+    rng = np.random.default_rng(32)
+    ctxs, q_lens = [40, 17], [6, 17]
+    q, ks, vs, qsl, sk = case(rng, ctxs, q_lens)
+    a = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, None, "f32")
+    b = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, None, "f32", window=40)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_one_key_window_closed_form():
+    """W = 1: the row sees only its own key: out = v_p, or with a sink
+    v_p / (1 + exp(sigma - x_p)), x_p = scale * <q, k_p>."""
+    rng = np.random.default_rng(33)
+    ctxs, q_lens = [12, 7], [4, 1]
+    q, ks, vs, qsl, sk = case(rng, ctxs, q_lens, Hq=2, Hkv=2, D=4, sinks=True)
+    plain = oracle.attention(q, ks, vs, qsl, 2, 2, 0.7, None, "f32", window=1)
+    sunk = oracle.attention(q, ks, vs, qsl, 2, 2, 0.7, sk, "f32", window=1)
+    row = 0
+    for k, v, ql in zip(ks, vs, q_lens):
+        for r in range(ql):
+            p = k.shape[0] - ql + r
+            for h in range(2):
+                vp = v[p, h].astype(np.float64)
+                assert np.array_equal(plain[row + r, h], vp)
+                x = 0.7 * float(np.dot(q[row + r, h].astype(np.float64), k[p, h].astype(np.float64)))
+                np.testing.assert_allclose(sunk[row + r, h], vp / (1.0 + np.exp(float(sk[h]) - x)),
+                                           rtol=1e-14, atol=1e-15)
+        row += ql
+
+
+def test_tree_row_equals_causal_row_over_its_ancestors():
+    """A tree row attends to resident keys + its ancestors + itself: the same
+    as the causal last row of a sequence made of exactly those keys."""
+    rng = np.random.default_rng(34)
+    base, W = 23, 12
+    parents = [-1, 0, 0, 1, 1, 2, -1, 6, 3, 8, 4, 9]
+    q, ks, vs, qsl, sk = case(rng, [base + W], [W], sinks=True)
+    got = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, sk, "f32", tree_mask=oracle.tree_masks(parents))
+    for r in range(W):
+        keep = list(range(base)) + sorted(base + j for j in _ancestors(parents, r))
+        kc, vc = ks[0][keep], vs[0][keep]
+        want = oracle.attention(q[r:r + 1], [kc], [vc], np.array([0, 1], np.int32), 4, 2, 0.5, sk, "f32")
+        np.testing.assert_allclose(got[r], want[0], rtol=0, atol=1e-15)
+
+
+def test_mask_bits_outside_the_ancestry_rule():
+    """Bits at or above the row's own index are ignored; the own key is
+    visible even with an all-zero mask."""
+    rng = np.random.default_rng(35)
+    q, ks, vs, qsl, _ = case(rng, [20], [5])
+    zeros = np.zeros(5, np.uint32)
+    high = np.array([0xFFFFFFFE, 0xFFFFFFFC, 0xFFFFFFF8, 0xFFFFFFF0, 0xFFFFFFE0], np.uint32)
+    a = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, None, "f32", tree_mask=zeros)
+    b = oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, None, "f32", tree_mask=high)
+    np.testing.assert_array_equal(a, b)
+    want = brute_masked(q, ks, vs, [5], [[-1] * 5], 0, 4, 2, 0.5)
+    np.testing.assert_allclose(a, want, rtol=0, atol=1e-12)
+
+
+def test_masked_oracle_rejects_long_windows():
+    rng = np.random.default_rng(36)
+    q, ks, vs, qsl, _ = case(rng, [40], [33])
+    with pytest.raises(ValueError):
+        oracle.attention(q, ks, vs, qsl, 4, 2, 0.5, None, "f32", tree_mask=np.zeros(33, np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# accept walk
+# ---------------------------------------------------------------------------
+
+def test_accept_walk_by_hand():
+    #        root
+    #       /    \
+    #     0(5)   4(5)
+    #     /  \
+    #   1(6) 2(7)
+    #    |
+    #   3(8)
+    parents = [-1, 0, 0, 1, -1]
+    drafts = [5, 6, 7, 8, 5]
+    assert oracle.accept_path(parents, drafts, [6, 1, 9, 2, 0], 5) == ([0, 1], 1)
+    assert oracle.accept_path(parents, drafts, [7, 8, 9, 4, 0], 5) == ([0, 2], 9)
+    assert oracle.accept_path(parents, drafts, [6, 8, 9, 4, 0], 5) == ([0, 1, 3], 4)
+    assert oracle.accept_path(parents, drafts, [6, 8, 9, 4, 0], 3) == ([], 3)
+
+
+def test_accept_walk_on_a_chain_is_the_longest_matching_prefix():
+    rng = np.random.default_rng(37)
+    for _ in range(50):
+        n = int(rng.integers(1, 17))
+        drafts = rng.integers(0, 4, n)
+        target = rng.integers(0, 4, n + 1)   # target[i]: the target's token at draft position i
+        k = 0
+        while k < n and drafts[k] == target[k]:
+            k += 1
+        path, bonus = oracle.accept_path(list(range(-1, n - 1)), drafts, target[1:], target[0])
+        assert path == list(range(k)) and bonus == target[k]
+
+
+# ---------------------------------------------------------------------------
+# truncate (KV rollback on the host side)
+# ---------------------------------------------------------------------------
+
+def invariants(a):
+    refs = [0] * a.n
+    for st in a.seqs.values():
+        assert len(st["blocks"]) == -(-len(st["tokens"]) // a.B)
+        assert len(st["hashes"]) == len(st["tokens"]) // a.B
+        for b in st["blocks"]:
+            refs[b] += 1
+    assert refs == a.ref
+    free = list(a.free)
+    assert len(set(free)) == len(free)
+    assert sorted(free) == [b for b in range(a.n) if refs[b] == 0]
+    assert all(a.in_free[b] == (b in free) for b in range(a.n))
+    for h, (b, _, _, _) in a.table.items():
+        assert a.blk_hash[b] == h
+
+
+def test_truncate_at_a_boundary_then_regrow_reuses_the_blocks():
+    a = oracle.Allocator(16, 4, list(range(16))[::-1])
+    toks = list(range(1, 15))                  # 3 full blocks + 2
+    row0, _, _, _ = a.alloc(1, toks, 8)
+    assert a.truncate(1, 4) == (-1, -1)
+    invariants(a)
+    assert a.table_row(1, 8)[:2] == [row0[0], -1]
+    row1, nb, ctx, slots = a.alloc(1, toks[4:], 8)
+    invariants(a)
+    assert ctx == 14 and nb == 4
+    assert row1[:3] == row0[:3]                # full blocks found again through their hashes
+    assert slots[:8] == [-1] * 8               # already resident
+
+
+def test_truncate_inside_own_full_block_unhashes_it():
+    a = oracle.Allocator(16, 4)
+    toks = list(range(1, 13))                  # 3 full blocks
+    row0, _, _, _ = a.alloc(1, toks, 8)
+    assert a.truncate(1, 6) == (-1, -1)        # block 1 keeps slots 0, 1
+    invariants(a)
+    assert a.table_row(1, 8)[:2] == row0[:2]
+    assert a.blk_hash[row0[1]] is None
+    # a new sequence with the old prefix shares block 0 only
+    row2, _, _, slots = a.alloc(2, toks, 8)
+    invariants(a)
+    assert row2[0] == row0[0] and row2[1] != row0[1]
+    assert slots[:4] == [-1] * 4 and -1 not in slots[4:]
+
+
+def test_truncate_inside_a_shared_block_copies_it():
+    a = oracle.Allocator(16, 4)
+    toks = list(range(1, 13))
+    row_a, _, _, _ = a.alloc(1, toks, 8)
+    row_b, _, _, _ = a.alloc(2, toks, 8)
+    assert row_a[:3] == row_b[:3]
+    src, dst = a.truncate(2, 5)
+    invariants(a)
+    assert src == row_a[1] and dst not in row_a[:3]
+    assert a.table_row(2, 8)[:2] == [row_a[0], dst]
+    assert a.table_row(1, 8)[:3] == row_a[:3]  # the other sequence keeps its blocks
+    assert a.ref[row_a[1]] == 1 and a.ref[dst] == 1
+    assert a.blk_hash[row_a[1]] is not None    # still hashed: sequence 1 holds it full
+
+
+def test_truncate_out_of_blocks_leaves_state_unchanged():
+    a = oracle.Allocator(3, 4)
+    toks = list(range(1, 13))
+    a.alloc(1, toks, 8)
+    a.alloc(2, toks, 8)
+    assert len(a.free) == 0
+    before = copy.deepcopy(a.__dict__)
+    with pytest.raises(oracle.OutOfBlocks):
+        a.truncate(2, 5)
+    assert a.__dict__ == before
+
+
+def test_truncate_edges():
+    a = oracle.Allocator(8, 4)
+    a.alloc(1, list(range(10)), 4)
+    assert a.truncate(1, 10) == (-1, -1)
+    assert a.table_row(1, 4)[:3] != [-1] * 3
+    with pytest.raises(ValueError):
+        a.truncate(1, 11)
+    with pytest.raises(KeyError):
+        a.truncate(9, 0)
+    assert a.truncate(1, 0) == (-1, -1)
+    invariants(a)
+    assert a.table_row(1, 4) == [-1] * 4 and len(a.free) == 8
+
+
+def test_rollback_after_a_tree_round_matches_serial_appends():
+    """Window rows scattered at window positions; accept a tree path; roll
+    back by truncating to the window base, allocating the accepted tokens and
+    scattering their rows. The gathered cache then equals a cache built by
+    appending the accepted tokens one by one."""
+    rng = np.random.default_rng(38)
+    B, Hkv, D = 16, 2, 16
+    base = 37
+    parents = [-1, 0, 0, 1, 2, 3, -1, 6]
+    drafts = [3, 4, 5, 6, 7, 8, 3, 1]
+    path, _ = oracle.accept_path(parents, drafts, [5, 0, 7, 0, 2, 0, 0, 0], 3)
+    assert path == [0, 2, 4]
+    ctx_tokens = list(rng.integers(0, 50, base))
+    kr = oracle.to_f32(rng.standard_normal((base, Hkv, D)).astype(np.float32), "f32")
+    vr = rng.standard_normal((base, Hkv, D)).astype(np.float32)
+    kw = rng.standard_normal((len(parents), Hkv, D)).astype(np.float32)
+    vw = rng.standard_normal((len(parents), Hkv, D)).astype(np.float32)
+
+    a = oracle.Allocator(32, B, rng.permutation(32))
+    kp, vp = oracle.empty_pools(32, Hkv, D, B, "f32", fill=np.float32(np.nan))
+    _, _, _, s0 = a.alloc(1, ctx_tokens, 8)
+    oracle.scatter(kp, vp, kr, vr, s0)
+    _, _, _, s1 = a.alloc(1, drafts, 8)
+    oracle.scatter(kp, vp, kw, vw, s1)
+    src, dst = a.truncate(1, base)
+    assert (src, dst) == (-1, -1)
+    row, _, ctx, s2 = a.alloc(1, [drafts[r] for r in path], 8)
+    oracle.scatter(kp, vp, kw[path], vw[path], s2)
+    invariants(a)
+    k_got, v_got = oracle.gather(kp, vp, row, ctx)
+    np.testing.assert_array_equal(k_got, np.concatenate([kr, kw[path]]))
+    np.testing.assert_array_equal(v_got, np.concatenate([vr, vw[path]]))
