@@ -164,6 +164,88 @@ int kv_pool_stats(const kv_pool *pool, int32_t *free_blocks, int32_t *cached_blo
  * the token ids and the parent block. Errors: KV_EINVAL (null pool). */
 int kv_pool_set_hash_mask(kv_pool *pool, uint64_t mask);
 
+/*
+ * Roll sequence `seq_id` back to its first new_len tokens, the KV side of a
+ * speculative round's rollback (TensorFold page, section on the GPU accept
+ * kernel: the state after the accepted path is restored, the KV cache
+ * included). Blocks wholly past new_len are returned as kv_pool_release
+ * returns them (last first, hash entries kept). When new_len ends inside a
+ * block that was full, its later slots will be written again:
+ *   - a block only this sequence holds loses its hash entry and starts a new
+ *     reuse generation (no chain through its old contents can be followed);
+ *   - a block other sequences hold too is replaced, in this sequence only, by
+ *     a block popped from the free list: *copy_src and *copy_dst name the old
+ *     and the new block, and the caller copies the old block's K/V into the
+ *     new one (kv_copy_blocks) before writing to it. Otherwise both are -1.
+ * The sequence's table row is then kv_pool_alloc(pool, seq_id, NULL, 0, ...)'s.
+ * new_len = 0 keeps an empty sequence. Nothing changes on error.
+ * Errors: KV_EINVAL (null pool or outputs, unknown sequence, new_len outside
+ * 0 .. context length, new_len ending inside a dropped block), KV_ENOMEM (a
+ * copy is needed and no block would be free).
+ */
+int kv_pool_truncate(kv_pool *pool, int64_t seq_id, int32_t new_len, int32_t *copy_src,
+                     int32_t *copy_dst);
+
+/*
+ * Free the blocks of sequence `seq_id` that lie wholly below position
+ * first_kept (blocks j with (j + 1) * block_size <= first_kept), for
+ * sliding-window attention, whose rows never see them again (the
+ * sliding-window attention of the drafters and models on the TensorFold
+ * pages). Freed blocks lose one reference each, go to the back of the free
+ * list when unreferenced (hash entries kept) and read -1 in the sequence's
+ * table row from now on; positions keep their meaning. Blocks that later
+ * become full after a freed block are not registered for sharing, and no
+ * sharing is looked up for the sequence after a freed block.
+ * Errors: KV_EINVAL (null pool, unknown sequence, first_kept < 0).
+ */
+int kv_pool_drop_prefix(kv_pool *pool, int64_t seq_id, int32_t first_kept);
+
+/*
+ * Copy whole blocks of both pools, every KV head and slot: block src[i] to
+ * block dst[i], i < n (the copy kv_pool_truncate asks for). src and dst are
+ * device int32 [n]; no dst may appear twice or among the src. Pools, sizes
+ * and dtype as for kv_append_scatter; entries outside 0 .. num_blocks - 1
+ * copy nothing. Stream-ordered, asynchronous.
+ * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
+ */
+int kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *src, const int32_t *dst, int32_t n,
+                   int32_t num_blocks, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int32_t dtype, void *hip_stream);
+
+/*
+ * Ancestor masks of one tree window (host): bit j of masks[r] is set when
+ * window row j is row r or one of its ancestors, parents[r] being -1 (the
+ * token before the window) or an earlier row. These are the tree_mask words
+ * paged_attention_masked_forward takes. n <= 32.
+ * Errors: KV_EINVAL (null pointer, n outside 0 .. 32, a parent not in
+ * -1 .. r - 1); masks is unchanged on error.
+ */
+int kv_tree_masks(const int32_t *parents, int32_t n, uint32_t *masks);
+
+/*
+ * The accept walk of a verify round on the device (TensorFold page, section
+ * on the GPU accept kernel: each draft is compared with the target's choice
+ * and the accepted path follows, from the root, the first child whose draft
+ * token equals that choice). Sequence s owns window rows
+ * query_start_loc[s] .. query_start_loc[s + 1]; for window row r
+ * (index within the sequence) parents[qsl[s] + r] is the parent row index, or
+ * -1 for the token before the window; draft_tokens[qsl[s] + r] is the row's
+ * draft token and choices[qsl[s] + r] the target's token after the row;
+ * root_choices[s] is the target's token after the token before the window.
+ * The walk starts at the root with want = root_choices[s], moves to the first
+ * row (lowest index) whose parent is the current node and whose draft token
+ * is want, then takes want = that row's choice, until no such row exists.
+ * Out: path[qsl[s] + k] = k-th accepted window row index (the rest of the
+ * sequence's entries -1), path_len[s], bonus[s] = the final want (the target's
+ * token after the accepted path). All arrays are device int32. Parents outside
+ * -1 .. r - 1 give an unspecified path; the walk ends after at most q_len
+ * moves whatever the input. Stream-ordered, asynchronous.
+ * Errors: KV_EINVAL (null pointer, negative size), KV_EDEVICE.
+ */
+int kv_accept_paths(const int32_t *parents, const int32_t *draft_tokens, const int32_t *choices,
+                    const int32_t *root_choices, const int32_t *query_start_loc, int32_t num_seqs,
+                    int32_t *path, int32_t *path_len, int32_t *bonus, void *hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Device entry points                                                        */
 /* ------------------------------------------------------------------------ */
@@ -267,6 +349,37 @@ int paged_attention_append_forward(const void *q, const void *k_new, const void 
                                    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                                    const float *sinks, float *out, void *workspace, size_t workspace_bytes,
                                    void *hip_stream);
+
+/*
+ * paged_attention_forward with fewer visible keys per row.
+ * Tree windows (TensorFold page, section on the GPU accept kernel: a verify
+ * round lays its drafts out as a chain or a tree of at most 16 rows, the tree
+ * carrying alternative paths): tree_mask is device uint32 [total_q_rows] or
+ * NULL. With base = context_lens[s] - q_len, row r of sequence s sees every
+ * key below base, its own key base + r, and the key base + j (j < r) when bit
+ * j of tree_mask[query_start_loc[s] + r] is set; bits at or above r are
+ * ignored. All bits below r set is the causal window. With a tree_mask every
+ * q_len must be at most 32 (max_q_len > 32: KV_EINVAL).
+ * Sliding window (the sliding-window attention of the drafters and models on
+ * the same pages): sliding_window = 0 for none, else the row at position p
+ * sees only keys t > p - sliding_window. Table entries of blocks that no row
+ * of the call can see may be -1 (kv_pool_drop_prefix).
+ * Both only remove keys; the row's own key always stays visible. With
+ * tree_mask NULL and sliding_window 0 the call is paged_attention_forward.
+ * Each row's result depends only on its query, its position, its visible keys,
+ * scale and sink: the same row gives the same bits in any batch, and a tree
+ * row equals itself in the window cut after it.
+ * Other arguments, ownership and errors are those of paged_attention_forward;
+ * tree_mask is 4-byte aligned; sliding_window < 0 is KV_EINVAL.
+ */
+int paged_attention_masked_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                   int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                   const float *sinks, const uint32_t *tree_mask, int32_t sliding_window,
+                                   float *out, void *workspace, size_t workspace_bytes, void *hip_stream);
 
 #ifdef __cplusplus
 }

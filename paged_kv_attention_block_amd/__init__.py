@@ -24,8 +24,9 @@ __all__ = [
     "KV_OK", "KV_EINVAL", "KV_ENOMEM", "KV_EUNSUPPORTED", "KV_EDEVICE", "KV_EINTERNAL",
     "KV_F32", "KV_BF16", "KV_FP8", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
-    "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_workspace_size",
-    "paged_attention_forward", "paged_attention_append_forward", "empty_pools", "BLOCK_SIZE",
+    "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks", "kv_append_scatter",
+    "kv_copy_blocks", "kv_accept_paths", "paged_attention_workspace_size", "paged_attention_forward",
+    "paged_attention_append_forward", "paged_attention_masked_forward", "empty_pools", "BLOCK_SIZE",
 ]
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
@@ -52,6 +53,11 @@ _lib.kv_pool_alloc.argtypes = [_p, _i64, _p, _i32, _p, _i32, _p, _p, _p]
 _lib.kv_pool_release.argtypes = [_p, _i64]
 _lib.kv_pool_stats.argtypes = [_p, _p, _p, _p]
 _lib.kv_pool_set_hash_mask.argtypes = [_p, _u64]
+_lib.kv_pool_truncate.argtypes = [_p, _i64, _i32, _p, _p]
+_lib.kv_pool_drop_prefix.argtypes = [_p, _i64, _i32]
+_lib.kv_tree_masks.argtypes = [_p, _i32, _p]
+_lib.kv_copy_blocks.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]
+_lib.kv_accept_paths.argtypes = [_p, _p, _p, _p, _p, _i32, _p, _p, _p, _p]
 _lib.kv_append_scatter.argtypes = [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]
 _lib.paged_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
 _lib.paged_attention_workspace_size.restype = _sz
@@ -61,9 +67,13 @@ _lib.paged_attention_forward.argtypes = [
 _lib.paged_attention_append_forward.argtypes = [
     _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
     _f32, _p, _p, _p, _sz, _p]
+_lib.paged_attention_masked_forward.argtypes = [
+    _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    _f32, _p, _p, _i32, _p, _p, _sz, _p]
 for _name in ("kv_pool_create", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
-              "kv_pool_set_hash_mask", "kv_append_scatter", "paged_attention_forward",
-              "paged_attention_append_forward"):
+              "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks",
+              "kv_append_scatter", "kv_copy_blocks", "kv_accept_paths", "paged_attention_forward",
+              "paged_attention_append_forward", "paged_attention_masked_forward"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -145,6 +155,25 @@ def kv_pool_stats(pool: _Pool):
 
 def kv_pool_set_hash_mask(pool: _Pool, mask: int) -> None:
     _check(_lib.kv_pool_set_hash_mask(pool.ptr, mask & 0xFFFFFFFFFFFFFFFF))
+
+
+def kv_pool_truncate(pool: _Pool, seq_id: int, new_len: int):
+    """Roll a sequence back to new_len tokens; returns (copy_src, copy_dst), -1 when no copy is needed."""
+    a, b = _i32(), _i32()
+    _check(_lib.kv_pool_truncate(pool.ptr, seq_id, new_len, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def kv_pool_drop_prefix(pool: _Pool, seq_id: int, first_kept: int) -> None:
+    _check(_lib.kv_pool_drop_prefix(pool.ptr, seq_id, first_kept))
+
+
+def kv_tree_masks(parents) -> np.ndarray:
+    """Ancestor masks (uint32 [n]) of one tree window from its parent rows."""
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32).reshape(-1))
+    out = np.zeros(max(1, par.size), dtype=np.uint32)
+    _check(_lib.kv_tree_masks(par.ctypes.data if par.size else out.ctypes.data, par.size, out.ctypes.data))
+    return out[:par.size]
 
 
 # ---------------------------------------------------------------------------
@@ -239,6 +268,49 @@ def kv_append_scatter(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None) -
                                   code, _stream_ptr(stream)))
 
 
+def kv_copy_blocks(k_pool, v_pool, src, dst, stream=None) -> None:
+    """Copy whole blocks src[i] -> dst[i] (device int32 [n]) in both pools."""
+    torch = _torch()
+    _need(src, "src", dtype=torch.int32, ndim=1)
+    _need(dst, "dst", dtype=torch.int32, ndim=1)
+    if src.shape != dst.shape:
+        raise KVError(KV_EINVAL, "src and dst sizes disagree")
+    if k_pool.dtype == torch.uint8:
+        hkv, d = k_pool.shape[1], (k_pool.shape[2] - 64) // 16
+        elem = torch.bfloat16
+    else:
+        hkv, d, elem = k_pool.shape[1], k_pool.shape[2] * k_pool.shape[4], k_pool.dtype
+    code, nb = _pools(k_pool, v_pool, elem, hkv, d)
+    _check(_lib.kv_copy_blocks(k_pool.data_ptr(), v_pool.data_ptr(), src.data_ptr(), dst.data_ptr(), src.shape[0],
+                               nb, hkv, d, BLOCK_SIZE, code, _stream_ptr(stream)))
+
+
+def kv_accept_paths(parents, draft_tokens, choices, root_choices, query_start_loc, path=None, path_len=None,
+                    bonus=None, stream=None):
+    """The accept walk of every sequence's verify window on the device; returns (path, path_len, bonus)."""
+    torch = _torch()
+    for t, name in ((parents, "parents"), (draft_tokens, "draft_tokens"), (choices, "choices"),
+                    (root_choices, "root_choices"), (query_start_loc, "query_start_loc")):
+        _need(t, name, dtype=torch.int32, ndim=1)
+    rows, S = parents.shape[0], root_choices.shape[0]
+    if draft_tokens.shape[0] != rows or choices.shape[0] != rows or query_start_loc.shape[0] != S + 1:
+        raise KVError(KV_EINVAL, "parents, draft_tokens, choices, root_choices and query_start_loc disagree")
+    if path is None:
+        path = torch.empty(rows, dtype=torch.int32, device=parents.device)
+    if path_len is None:
+        path_len = torch.empty(S, dtype=torch.int32, device=parents.device)
+    if bonus is None:
+        bonus = torch.empty(S, dtype=torch.int32, device=parents.device)
+    for t, name, n in ((path, "path", rows), (path_len, "path_len", S), (bonus, "bonus", S)):
+        _need(t, name, dtype=torch.int32, ndim=1)
+        if t.shape[0] != n:
+            raise KVError(KV_EINVAL, f"{name} has the wrong size")
+    _check(_lib.kv_accept_paths(parents.data_ptr(), draft_tokens.data_ptr(), choices.data_ptr(),
+                                root_choices.data_ptr(), query_start_loc.data_ptr(), S, path.data_ptr(),
+                                path_len.data_ptr(), bonus.data_ptr(), _stream_ptr(stream)))
+    return path, path_len, bonus
+
+
 def paged_attention_workspace_size(num_seqs: int, total_q_rows: int, num_q_heads: int, head_dim: int,
                                    max_context_len: int) -> int:
     return int(_lib.paged_attention_workspace_size(num_seqs, total_q_rows, num_q_heads, head_dim,
@@ -310,4 +382,25 @@ def paged_attention_append_forward(q, k_new, v_new, slot_mapping, k_pool, v_pool
         query_start_loc.data_ptr(), S, total, max_q_len, max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
         _stream_ptr(stream)))
+    return out
+
+
+def paged_attention_masked_forward(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
+                                   max_context_len: int, scale: float, sinks=None, tree_mask=None,
+                                   sliding_window: int = 0, out=None, workspace=None, stream=None):
+    """paged_attention_forward with tree-window masks (device uint32 [total_rows] or None) and a
+    sliding window (0 = none); see pagedkv.h."""
+    torch = _torch()
+    S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
+    if tree_mask is not None:
+        _need(tree_mask, "tree_mask", dtype=torch.int32, ndim=1)
+        if tree_mask.shape[0] != total:
+            raise KVError(KV_EINVAL, "tree_mask needs one word per query row")
+    _check(_lib.paged_attention_masked_forward(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), code, block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len, max_context_len, hq, hkv, d,
+        BLOCK_SIZE, nb, float(scale), None if sinks is None else sinks.data_ptr(),
+        None if tree_mask is None else tree_mask.data_ptr(), int(sliding_window), out.data_ptr(),
+        workspace.data_ptr(), ws_bytes, _stream_ptr(stream)))
     return out

@@ -86,6 +86,11 @@ struct AttnParams {
     const uint16_t *k_new, *v_new;
     const int32_t *slots;
     uint16_t *kp_w, *vp_w;
+    // Restricted visibility (paged_attention_masked_forward), else null / 0:
+    // one ancestor mask word per query row of a tree window, and a sliding
+    // window of `window` keys ending at each row's position.
+    const uint32_t *tree_mask;
+    int32_t window;
 };
 
 // A zero (block, head) tile: loads of blocks past the end of a sequence read it.
@@ -274,10 +279,38 @@ __device__ inline void patch_new_key(StepRegs<D> &r, const u32x4_t (&knew)[D / 3
 // take the keys' K scales (ksc, the lane's 8 keys) and whose probabilities
 // take the keys' V scales (vsc) before the PV product; the sum l takes the
 // unscaled probabilities.
-template <int D, bool SCALED, class KOp, class VOp>
+// The keys one query row sees: positions up to prow; with a restricted
+// visibility also none below lo, and of the tree window starting at wbase only
+// those whose bit in tm is set (the row's own bit included). Unrestricted rows
+// carry lo far below 0 and wbase far above any position.
+struct RowVis {
+    int prow;
+    int lo;
+    int wbase;
+    uint32_t tm;
+};
+
+constexpr int kFarBelow = -(1 << 30), kFarAbove = 1 << 30;
+
+// Visibility of the lane's 8 keys key0 .. key0 + 7 as bits 0 .. 7.
+__device__ inline uint32_t visible8(const RowVis &v, int key0) {
+    const int hi = v.prow - key0;  // keys i <= hi
+    const int lo = v.lo - key0;    // keys i >= lo
+    uint32_t m = hi >= 7 ? 0xFFu : hi < 0 ? 0u : (0xFFu >> (7 - hi));
+    m &= lo <= 0 ? 0xFFu : lo >= 8 ? 0u : ((0xFFu << lo) & 0xFFu);
+    // 64-bit word: bits 0..31 stand for the 32 keys below wbase (visible),
+    // bits 32 + j for window key j
+    const int sh = key0 - v.wbase + 32;
+    const uint64_t ext = ((uint64_t)v.tm << 32) | 0xFFFFFFFFull;
+    m &= sh < 0 ? 0xFFu : sh >= 64 ? 0u : (uint32_t)(ext >> sh) & 0xFFu;
+    return m;
+}
+
+template <int D, bool SCALED, bool MASKED, class KOp, class VOp>
 __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const float (&ksc)[8],
-                                 const float (&vsc)[8], const u32x4_t (&qop)[D / 32], int kc, int prow, int g,
-                                 float scale_log2) {
+                                 const float (&vsc)[8], const u32x4_t (&qop)[D / 32], int kc, const RowVis &rv,
+                                 int g, float scale_log2) {
+    const int prow = rv.prow;
     constexpr int KJ = D / 32, DT = D / 16;
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -288,20 +321,25 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     }
     float sc[8];
     const int lim = prow - (kc + key_off(g));  // the row sees the lane's keys 0 .. lim
+    uint32_t vm = 0;
+    if constexpr (MASKED) vm = visible8(rv, kc + key_off(g));
+    auto vis = [&](int i) { return MASKED ? ((vm >> i) & 1u) != 0 : i <= lim; };
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (SCALED) {
-            sc[i] = i <= lim ? (s0[i] * ksc[i]) * scale_log2 : -INFINITY;
-            sc[4 + i] = i + 4 <= lim ? (s1[i] * ksc[4 + i]) * scale_log2 : -INFINITY;
+            sc[i] = vis(i) ? (s0[i] * ksc[i]) * scale_log2 : -INFINITY;
+            sc[4 + i] = vis(i + 4) ? (s1[i] * ksc[4 + i]) * scale_log2 : -INFINITY;
         } else {
-            sc[i] = i <= lim ? s0[i] * scale_log2 : -INFINITY;
-            sc[4 + i] = i + 4 <= lim ? s1[i] * scale_log2 : -INFINITY;
+            sc[i] = vis(i) ? s0[i] * scale_log2 : -INFINITY;
+            sc[4 + i] = vis(i + 4) ? s1[i] * scale_log2 : -INFINITY;
         }
     }
     float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool has = kc <= prow;  // the row sees at least one key of the chunk
+    // the row sees at least one key of the chunk (with a restricted
+    // visibility: its maximum over the chunk is a score)
+    const bool has = MASKED ? mx != -INFINITY : kc <= prow;
     const float m_new = fmaxf(st.m, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(st.m - m_use);
@@ -338,13 +376,13 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     st.m = has ? m_new : st.m;
 }
 
-template <int D>
+template <int D, bool MASKED>
 __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
-                                   int prow, int g, float scale_log2) {
+                                   const RowVis &rv, int g, float scale_log2) {
     const float none[8] = {};
-    step_core<D, false>(
+    step_core<D, false, MASKED>(
         st, [&](int tau, int j) { return __builtin_bit_cast(bf16x8_t, r.k[tau][j]); },
-        [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, prow, g, scale_log2);
+        [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, rv, g, scale_log2);
 }
 
 // ---------------------------------------------------------------------------
@@ -433,9 +471,9 @@ __device__ inline void mask_tail8(StepRegs8<D> &r, int kc, int ctx, int g) {
     }
 }
 
-template <int D>
+template <int D, bool MASKED>
 __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r, const u32x4_t (&qop)[D / 32],
-                                    int kc, int prow, int g, float scale_log2) {
+                                    int kc, const RowVis &rv, int g, float scale_log2) {
     float ksc[8], vsc[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -444,7 +482,7 @@ __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r
         vsc[i] = r.vs[0][i];
         vsc[4 + i] = r.vs[1][i];
     }
-    step_core<D, true>(
+    step_core<D, true, MASKED>(
         st,
         [&](int tau, int j) {
             const u32x4_t w = r.k[tau][j >> 1];
@@ -454,7 +492,7 @@ __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r
             const u32x4_t w = r.v[dt >> 1];
             return (dt & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
         },
-        ksc, vsc, qop, kc, prow, g, scale_log2);
+        ksc, vsc, qop, kc, rv, g, scale_log2);
 }
 
 // Pool access of the parallel and sequential shapes for bf16 (Q8 = false)
@@ -472,9 +510,10 @@ struct Pool<D, false> {
                      reinterpret_cast<const uint16_t *>(k1), reinterpret_cast<const uint16_t *>(v1), g, n);
     }
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail<D>(r, kc, ctx, g); }
+    template <bool MASKED>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
-                                  int prow, int g, float sl2) {
-        step_update<D>(st, r, qop, kc, prow, g, sl2);
+                                  const RowVis &rv, int g, float sl2) {
+        step_update<D, MASKED>(st, r, qop, kc, rv, g, sl2);
     }
 };
 
@@ -487,9 +526,10 @@ struct Pool<D, true> {
         load_step8<D>(r, k0, v0, k1, v1, g, n);
     }
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail8<D>(r, kc, ctx, g); }
+    template <bool MASKED>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
-                                  int prow, int g, float sl2) {
-        step_update8<D>(st, r, qop, kc, prow, g, sl2);
+                                  const RowVis &rv, int g, float sl2) {
+        step_update8<D, MASKED>(st, r, qop, kc, rv, g, sl2);
     }
 };
 
@@ -507,6 +547,30 @@ __device__ inline RowInfo row_info(int rho, int rows_total, int G, int ctx, int 
     ri.hl = valid ? rho - ri.r * G : 0;
     ri.prow = valid ? ctx - q_len + ri.r : -1;
     return ri;
+}
+
+// Visibility of a row (see RowVis); q0 is the sequence's first row, wbase
+// the position of its first query row.
+template <bool MASKED>
+__device__ inline RowVis row_vis(const AttnParams &P, const RowInfo &ri, int q0, int wbase) {
+    RowVis v;
+    v.prow = ri.prow;
+    v.lo = kFarBelow;
+    v.wbase = kFarAbove;
+    v.tm = 0xFFFFFFFFu;
+    if constexpr (MASKED) {
+        if (P.window > 0) v.lo = ri.prow - P.window + 1;
+        if (P.tree_mask && ri.prow >= 0) {
+            v.wbase = wbase;
+            v.tm = P.tree_mask[q0 + ri.r] | (1u << ri.r);
+        }
+    }
+    return v;
+}
+
+// Lowest position any row of a sequence can see, from its first query row.
+__device__ inline int seq_lowest_key(const AttnParams &P, int wbase) {
+    return P.window > 0 ? wbase - P.window + 1 : 0;
 }
 
 // Q of the lane's row; padding rows read the sequence's first row, which
@@ -563,7 +627,7 @@ struct ParLds {
     float2 ml[3][NT][64];
 };
 
-template <int D, int NT, bool PF, bool APPEND, bool Q8>
+template <int D, int NT, bool PF, bool APPEND, bool Q8, bool MASKED>
 __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnParams P) {
     using PoolT = Pool<D, Q8>;
     using Regs = typename PoolT::Regs;
@@ -596,7 +660,9 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     const int ns_item = min(num_splits(p_max + 1), P.max_splits);
     // (uniform over the workgroup)
     if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT && p_max >= 0)) return;
-    if (j >= ns_item) {
+    const int wbase = ctx - q_len;                              // position of the first query row
+    const int lo_seq = MASKED ? seq_lowest_key(P, wbase) : 0;  // no row sees a key below it
+    if (j >= ns_item || (MASKED && split_begin(j + 1) <= lo_seq)) {
         // No row sees this split: its slot holds an empty state, so that the
         // fold reads every slot without first learning the context length.
         if (wave == 0) {
@@ -611,12 +677,14 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
         return;
     }
     RowInfo ri[NT];
+    RowVis rv[NT];
     u32x4_t qop[NT][KJ];
     TileState<DT> st[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         state_clear(st[t]);
         ri[t] = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
+        rv[t] = row_vis<MASKED>(P, ri[t], q0, wbase);
     }
     {
 #pragma unroll
@@ -671,17 +739,20 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
             PoolT::mask(r, kc, ctx, g);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                if (16 * t < rows_total) PoolT::update(st[t], r, qop[t], kc, ri[t].prow, g, P.scale_log2);
+                if (16 * t < rows_total) PoolT::template update<MASKED>(st[t], r, qop[t], kc, rv[t], g, P.scale_log2);
         };
+        // Steps wholly below every row's lowest visible key change no state:
+        // the wave starts at the step holding lo_seq.
+        const int kstart = (MASKED && lo_seq > kq0) ? kq0 + (lo_seq - kq0) / kStep * kStep : kq0;
         if constexpr (PF) {
             // Two register stages, each refilled as soon as it is consumed,
             // so that two steps are in flight; unrolled so that each stage
             // keeps fixed registers (a copy between stages would wait for the
             // loads it copies).
             Regs r0, r1;
-            fetch(r0, kq0);
-            if (kq0 + kStep < kq1) fetch(r1, kq0 + kStep);
-            for (int kc = kq0; kc < kq1; kc += 2 * kStep) {
+            if (!MASKED || kstart < kq1) fetch(r0, kstart);
+            if (kstart + kStep < kq1) fetch(r1, kstart + kStep);
+            for (int kc = kstart; kc < kq1; kc += 2 * kStep) {
                 compute(r0, kc);
                 if (kc + 2 * kStep < kq1) fetch(r0, kc + 2 * kStep);
                 if (kc + kStep < kq1) {
@@ -690,7 +761,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                 }
             }
         } else {
-            for (int kc = kq0; kc < kq1; kc += kStep) {
+            for (int kc = kstart; kc < kq1; kc += kStep) {
                 Regs r;
                 fetch(r, kc);
                 compute(r, kc);
@@ -832,7 +903,7 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
     return false;
 }
 
-template <int D, bool Q8>
+template <int D, bool Q8, bool MASKED>
 __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     using PoolT = Pool<D, Q8>;
     using Regs = typename PoolT::Regs;
@@ -858,12 +929,16 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     if (p_max < 0) return;
 
     const RowInfo ri = row_info(row0 + 16 * wave + n, rows_total, P.G, ctx, q_len);
+    const RowVis rv = row_vis<MASKED>(P, ri, q0, ctx - q_len);
     u32x4_t qop[KJ];
     load_q<D>(qop, P, q0, ri, kvh, g);
     // last key any row of this wave's tile sees (wave-uniform, -1 if no rows)
     const int wave_row0 = row0 + 16 * wave;
     const int wave_pmax =
         wave_row0 < rows_total ? ctx - q_len + min(wave_row0 + 15, rows_total - 1) / P.G : -1;
+    // lowest key any row of the wave's tile, or of the workgroup, sees
+    const int wave_lo = MASKED ? seq_lowest_key(P, ctx - q_len + wave_row0 / P.G) : 0;
+    const int blk_lo = MASKED ? seq_lowest_key(P, ctx - q_len + row0 / P.G) : 0;
 
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * TB];
     // the row state of each wave's tile, touched only at split ends
@@ -898,8 +973,12 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     const int32_t *bt_row = P.bt + (size_t)s * P.max_blocks_per_seq;
     const int jb_max = min(nblk_seq, P.max_blocks_per_seq);  // blocks past it read the zero tile
     auto load_bids = [&](int first) { return bt_row[min(first + lane, P.max_blocks_per_seq - 1)]; };
-    int bw = 0;  // window of the steps being computed
-    int bcur = load_bids(0), bnxt = load_bids(64);
+    // Steps wholly below every row's lowest visible key change no state: the
+    // walk starts at an even step at or below blk_lo (an even start keeps
+    // the two prefetch stages in order).
+    const int c_start = blk_lo > 0 ? blk_lo / (2 * kStep) * 2 : 0;
+    int bw = c_start >> 5;  // window of the steps being computed
+    int bcur = load_bids(64 * bw), bnxt = load_bids(64 * (bw + 1));
     // Step c's piece into dst; fetches run two steps ahead of the compute
     // (so into the next window at a window's end) and past the last step
     // they read the zero tile.
@@ -932,7 +1011,7 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
                 *reinterpret_cast<u32x4_t *>(buf + wave * TB + lds_pos(lane + 64 * v) * 16) = pre[v];
         fetch(pre, c + 2);
         __syncthreads();
-        if (kc <= wave_pmax) {
+        if (kc <= wave_pmax && (!MASKED || kc + kStep > wave_lo)) {
             Regs r;
             if constexpr (Q8)
                 load_step8<D>(r, buf, buf + 2 * TB, buf + TB, buf + 3 * TB, g, n, [](int t) { return lds_k_pos(t); },
@@ -942,7 +1021,7 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
                                  reinterpret_cast<const uint16_t *>(buf + TB),
                                  reinterpret_cast<const uint16_t *>(buf + 3 * TB), g, n);
             PoolT::mask(r, kc, ctx, g);
-            PoolT::update(qtr, r, qop, kc, ri.prow, g, P.scale_log2);
+            PoolT::template update<MASKED>(qtr, r, qop, kc, rv, g, P.scale_log2);
         }
         // quarter and split boundaries fall on step boundaries
         const int next = kc + kStep;
@@ -969,14 +1048,14 @@ __global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
     };
     // two register stages, unrolled so that each stays in fixed registers
     u32x4_t pre0[NV], pre1[NV];
-    fetch(pre0, 0);
-    fetch(pre1, 1);
+    fetch(pre0, c_start);
+    fetch(pre1, c_start + 1);
     // An even number of steps keeps the two stages in one order at the loop
     // head; a step past the last computes nothing and folds empty states,
     // which is exact.
     const int nsteps2 = (nsteps + 1) & ~1;
-    for (int w0 = 0; w0 < nsteps2; w0 += 32, ++bw) {
-        const int wend = min(w0 + 32, nsteps2);
+    for (int w0 = c_start; w0 < nsteps2; w0 = (w0 & ~31) + 32, ++bw) {
+        const int wend = min((w0 & ~31) + 32, nsteps2);
         for (int c = w0; c < wend; c += 2) {
             step(c, pre0);
             step(c + 1, pre1);
@@ -1017,9 +1096,15 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
     const int s = seq_of_row(P.qsl, P.num_seqs, i);
     const int q_len = P.qsl[s + 1] - P.qsl[s];
     const int ctx = P.ctx_lens[s];
-    const int p = ctx - q_len + (i - P.qsl[s]);
+    const int r = i - P.qsl[s];
+    const int p = ctx - q_len + r;
     if (p < 0) return;
     const int kvh = h / P.G;
+    // restricted visibility (tree window, sliding window)
+    const int wbase = ctx - q_len;
+    const int lo = P.window > 0 ? p - P.window + 1 : 0;
+    const bool tree = P.tree_mask != nullptr;
+    const uint32_t tm = tree ? P.tree_mask[i] | (1u << r) : 0xFFFFFFFFu;
 
     __shared__ float qs[D];
     const float *qrow = reinterpret_cast<const float *>(P.q) + ((size_t)i * P.Hq + h) * D;
@@ -1035,11 +1120,13 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) acc[u] = 0.f;
 
-    for (int kc = 0; kc <= p; kc += 64) {
+    for (int kc = lo > 0 ? lo / 64 * 64 : 0; kc <= p; kc += 64) {
         const int key = kc + lane;
-        const bool vis = key <= p;
+        const bool vis = key <= p && key >= lo && (!tree || key < wbase || ((tm >> (key - wbase)) & 1u));
+        // the key's block, for every key up to p: lane 16 bb names block bb of
+        // the chunk in the value pass, visible or not
         int phys = -1;
-        if (vis) {
+        if (key <= p) {
             const int jb = key / kBlock;
             if (jb < P.max_blocks_per_seq) {
                 const int b = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
@@ -1047,7 +1134,7 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
             }
         }
         float dot = 0.f;
-        if (phys >= 0) {
+        if (vis && phys >= 0) {
             const float *kb = kp + ((size_t)phys * P.Hkv + kvh) * tile;
             const int o = key % kBlock;
 #pragma unroll
@@ -1063,6 +1150,7 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
         float mx = sc;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (mx == -INFINITY) continue;  // no visible key in the chunk (wave-uniform)
         const float m_new = fmaxf(m, mx);
         const float alpha = fast_exp2(m - m_new);
         const float pv = fast_exp2(sc - m_new);
@@ -1338,6 +1426,7 @@ static WsLayout ws_layout(int64_t rows, int64_t Hq, int64_t D, int64_t splits) {
 }
 
 static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // A grid that leaves CUs free takes the two-stage variant: per-workgroup
 // latency then decides the time, and occupancy does not matter.
@@ -1355,41 +1444,47 @@ static int device_cus() {
     return cus;
 }
 
-template <int D, int NT, bool APPEND, bool Q8>
+template <int D, int NT, bool APPEND, bool Q8, bool MASKED>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
     const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.max_splits;
     if constexpr (NT == 1) {
         if (nwg <= device_cus()) {
-            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, Q8>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, Q8, MASKED>), dim3((unsigned)nwg), dim3(256), 0,
+                               st, P);
             return;
         }
     }
-    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND, Q8>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND, Q8, MASKED>), dim3((unsigned)nwg), dim3(256), 0, st, P);
 }
 
-template <int D, int NT, bool Q8>
+template <int D, int NT, bool Q8, bool MASKED>
 static void launch_parallel(const AttnParams &P, hipStream_t st) {
-    if constexpr (Q8) launch_parallel_as<D, NT, false, true>(P, st);
-    else if (P.k_new) launch_parallel_as<D, NT, true, false>(P, st);
-    else launch_parallel_as<D, NT, false, false>(P, st);
+    if constexpr (Q8 || MASKED) launch_parallel_as<D, NT, false, Q8, MASKED>(P, st);
+    else if (P.k_new) launch_parallel_as<D, NT, true, false, false>(P, st);
+    else launch_parallel_as<D, NT, false, false, false>(P, st);
 }
 
-template <int D, bool Q8>
-static void launch_mfma(const AttnParams &P, int max_q_len, int max_context_len, int total_rows,
-                        hipStream_t st) {
+template <int D, bool Q8, bool MASKED>
+static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
     const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
-        launch_parallel<D, 1, Q8>(P, st);
+        launch_parallel<D, 1, Q8, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P);
     } else {
-        launch_parallel<D, 2, Q8>(P, st);
+        launch_parallel<D, 2, Q8, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
-        hipLaunchKernelGGL((attn_sequential<D, Q8>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((attn_sequential<D, Q8, MASKED>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
     }
+}
+
+template <int D, bool Q8>
+static void launch_mfma_vis(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
+    if (P.tree_mask || P.window > 0) launch_mfma<D, Q8, true>(P, max_q_len, total_rows, st);
+    else launch_mfma<D, Q8, false>(P, max_q_len, total_rows, st);
 }
 
 }  // namespace pkv
@@ -1412,13 +1507,18 @@ struct AppendArgs {
     const int32_t *slots;
 };
 
+struct MaskArgs {
+    const uint32_t *tree_mask;
+    int32_t window;
+};
+
 static int forward_impl(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
                         const int32_t *block_tables, int32_t max_blocks_per_seq,
                         const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
                         int32_t total_q_rows, int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                         float scale, const float *sinks, float *out, void *workspace, size_t workspace_bytes,
-                        void *hip_stream, const AppendArgs *app) {
+                        void *hip_stream, const AppendArgs *app, const MaskArgs *mk) {
     if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: dtype %d not supported", dtype);
     if (head_dim != 64 && head_dim != 128)
@@ -1433,6 +1533,13 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     if (num_q_heads > 65535)
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: too many heads");
     if (!std::isfinite(scale)) PKV_FAIL(KV_EINVAL, "paged_attention_forward: scale is not finite");
+    if (mk && mk->window < 0)
+        PKV_FAIL(KV_EINVAL, "paged_attention_masked_forward: sliding_window %d < 0", mk->window);
+    if (mk && mk->tree_mask && max_q_len > 32)
+        PKV_FAIL(KV_EINVAL, "paged_attention_masked_forward: tree masks cover 32 window rows, max_q_len is %d",
+                 max_q_len);
+    if (mk && mk->tree_mask && !aligned4(mk->tree_mask))
+        PKV_FAIL(KV_EINVAL, "paged_attention_masked_forward: tree_mask must be 4-byte aligned");
     if (num_seqs == 0 || total_q_rows == 0) return KV_OK;
     if (max_q_len < 1 || max_context_len < 1)
         PKV_FAIL(KV_EINVAL, "paged_attention_forward: max_q_len and max_context_len must be >= 1");
@@ -1486,6 +1593,8 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     P.k_new = P.v_new = nullptr;
     P.slots = nullptr;
     P.kp_w = P.vp_w = nullptr;
+    P.tree_mask = mk ? mk->tree_mask : nullptr;
+    P.window = mk ? mk->window : 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
 
     if (app) {
@@ -1509,11 +1618,11 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
 
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
-        if (head_dim == 64) launch_mfma<64, false>(P, max_q_len, max_context_len, total_q_rows, st);
-        else launch_mfma<128, false>(P, max_q_len, max_context_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, false>(P, max_q_len, total_q_rows, st);
+        else launch_mfma_vis<128, false>(P, max_q_len, total_q_rows, st);
     } else if (dtype == KV_FP8) {
-        if (head_dim == 64) launch_mfma<64, true>(P, max_q_len, max_context_len, total_q_rows, st);
-        else launch_mfma<128, true>(P, max_q_len, max_context_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, true>(P, max_q_len, total_q_rows, st);
+        else launch_mfma_vis<128, true>(P, max_q_len, total_q_rows, st);
     } else {
         const dim3 grid(total_q_rows, num_q_heads);
         if (head_dim == 64) hipLaunchKernelGGL((attn_f32<64>), grid, dim3(64), 0, st, P);
@@ -1540,7 +1649,22 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
     return pkv::forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens,
                              query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, workspace,
-                             workspace_bytes, hip_stream, nullptr);
+                             workspace_bytes, hip_stream, nullptr, nullptr);
+}
+
+int paged_attention_masked_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                   int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                   const float *sinks, const uint32_t *tree_mask, int32_t sliding_window,
+                                   float *out, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    const pkv::MaskArgs mk{tree_mask, sliding_window};
+    return pkv::forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens,
+                             query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, workspace,
+                             workspace_bytes, hip_stream, nullptr, &mk);
 }
 
 int paged_attention_append_forward(const void *q, const void *k_new, const void *v_new,
@@ -1564,7 +1688,8 @@ int paged_attention_append_forward(const void *q, const void *k_new, const void 
     const AppendArgs app{k_new, v_new, slot_mapping};
     return forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens, query_start_loc,
                         num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads, num_kv_heads, head_dim,
-                        block_size, num_blocks, scale, sinks, out, workspace, workspace_bytes, hip_stream, &app);
+                        block_size, num_blocks, scale, sinks, out, workspace, workspace_bytes, hip_stream, &app,
+                        nullptr);
 }
 
 int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_mapping, int32_t n,

@@ -6,6 +6,7 @@
 // section "内存优化" (paged KV block pool with LRU eviction and cross-session
 // content-hash reuse). The exact policy is spelled out at kv_pool_alloc in
 // pagedkv.h; this file implements it with O(1) free-list operations.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -57,8 +58,9 @@ struct Entry {
 
 struct Seq {
     std::vector<int32_t> tokens;
-    std::vector<int32_t> blocks;
+    std::vector<int32_t> blocks;   // -1 for blocks freed by kv_pool_drop_prefix
     std::vector<uint64_t> hashes;  // one per full block
+    bool dropped = false;          // some block was freed: no sharing from here on
 };
 
 }  // namespace
@@ -198,7 +200,7 @@ int kv_pool_alloc(kv_pool *pool, int64_t seq_id, const int32_t *new_token_ids, i
         // Phase 1 (read only): the run of shared blocks starting at a block boundary.
         struct Hit { int32_t block; uint64_t hash; };
         std::vector<Hit> hits;
-        if (n0 % B == 0) {
+        if (n0 % B == 0 && !cur.dropped) {
             uint64_t ph = cur.hashes.empty() ? 0 : cur.hashes.back();
             int32_t parent = cur.blocks.empty() ? -1 : cur.blocks.back();
             for (int64_t j = nb0; j < nb1; ++j) {
@@ -237,7 +239,7 @@ int kv_pool_alloc(kv_pool *pool, int64_t seq_id, const int32_t *new_token_ids, i
                 const uint64_t ph = st.hashes.empty() ? 0 : st.hashes.back();
                 const uint64_t h = pool->hash(ph, all.data() + j * B);
                 st.hashes.push_back(h);
-                pool->reg(b, h, j > 0 ? st.blocks[j - 1] : -1, all.data() + j * B);
+                if (!st.dropped) pool->reg(b, h, j > 0 ? st.blocks[j - 1] : -1, all.data() + j * B);
             }
         }
         for (const Hit &h : hits) {
@@ -258,7 +260,7 @@ int kv_pool_alloc(kv_pool *pool, int64_t seq_id, const int32_t *new_token_ids, i
                 const uint64_t ph = st.hashes.empty() ? 0 : st.hashes.back();
                 const uint64_t h = pool->hash(ph, all.data() + j * B);
                 st.hashes.push_back(h);
-                pool->reg(b, h, parent, all.data() + j * B);
+                if (!st.dropped) pool->reg(b, h, parent, all.data() + j * B);
             }
         }
         st.tokens.swap(all);
@@ -282,12 +284,101 @@ int kv_pool_release(kv_pool *pool, int64_t seq_id) {
             PKV_FAIL(KV_EINVAL, "kv_pool_release: unknown sequence %lld", (long long)seq_id);
         const std::vector<int32_t> &bl = it->second.blocks;
         for (auto b = bl.rbegin(); b != bl.rend(); ++b)
-            if (--pool->ref[*b] == 0) pool->push_back(*b);
+            if (*b >= 0 && --pool->ref[*b] == 0) pool->push_back(*b);
         pool->seqs.erase(it);
         return KV_OK;
     } catch (...) {
         PKV_FAIL(KV_EINTERNAL, "kv_pool_release: unexpected exception");
     }
+}
+
+int kv_pool_truncate(kv_pool *pool, int64_t seq_id, int32_t new_len, int32_t *copy_src, int32_t *copy_dst) {
+    try {
+        if (!pool || !copy_src || !copy_dst) PKV_FAIL(KV_EINVAL, "kv_pool_truncate: pool or an output is NULL");
+        auto it = pool->seqs.find(seq_id);
+        if (it == pool->seqs.end())
+            PKV_FAIL(KV_EINVAL, "kv_pool_truncate: unknown sequence %lld", (long long)seq_id);
+        pkv::Seq &st = it->second;
+        const int64_t n = int64_t(st.tokens.size());
+        if (new_len < 0 || new_len > n)
+            PKV_FAIL(KV_EINVAL, "kv_pool_truncate: new_len %d outside 0 .. %lld", new_len, (long long)n);
+        const int32_t B = pool->B;
+        const int64_t nb = int64_t(st.blocks.size());
+        const int64_t keep = (int64_t(new_len) + B - 1) / B;
+        // the new last block was full: its later slots will be written again
+        const bool tail_full = new_len % B != 0 && int64_t(st.hashes.size()) >= keep;
+        const int32_t tail = tail_full ? st.blocks[keep - 1] : -1;
+        if (tail_full && tail < 0)
+            PKV_FAIL(KV_EINVAL, "kv_pool_truncate: new_len %d ends inside a dropped block", new_len);
+        const bool shared = tail_full && pool->ref[tail] > 1;
+        if (shared) {
+            int64_t freed = 0;
+            for (int64_t j = keep; j < nb; ++j) freed += st.blocks[j] >= 0 && pool->ref[st.blocks[j]] == 1;
+            if (pool->free_count + freed < 1)
+                PKV_FAIL(KV_ENOMEM, "kv_pool_truncate: a shared block must be copied and no block is free");
+        }
+        for (int64_t j = nb - 1; j >= keep; --j) {
+            const int32_t b = st.blocks[j];
+            if (b >= 0 && --pool->ref[b] == 0) pool->push_back(b);
+        }
+        st.blocks.resize(size_t(keep));
+        st.hashes.resize(size_t(new_len / B));
+        st.tokens.resize(size_t(new_len));
+        *copy_src = *copy_dst = -1;
+        if (tail_full) {
+            if (shared) {
+                --pool->ref[tail];
+                const int32_t d = pool->pop();
+                st.blocks[size_t(keep - 1)] = d;
+                *copy_src = tail;
+                *copy_dst = d;
+            } else {
+                if (pool->has_hash[tail]) {
+                    pool->table.erase(pool->blk_hash[tail]);
+                    pool->has_hash[tail] = 0;
+                }
+                ++pool->gen[tail];
+            }
+        }
+        return KV_OK;
+    } catch (...) {
+        PKV_FAIL(KV_EINTERNAL, "kv_pool_truncate: unexpected exception");
+    }
+}
+
+int kv_pool_drop_prefix(kv_pool *pool, int64_t seq_id, int32_t first_kept) {
+    try {
+        if (!pool) PKV_FAIL(KV_EINVAL, "kv_pool_drop_prefix: pool is NULL");
+        auto it = pool->seqs.find(seq_id);
+        if (it == pool->seqs.end())
+            PKV_FAIL(KV_EINVAL, "kv_pool_drop_prefix: unknown sequence %lld", (long long)seq_id);
+        if (first_kept < 0) PKV_FAIL(KV_EINVAL, "kv_pool_drop_prefix: first_kept %d < 0", first_kept);
+        pkv::Seq &st = it->second;
+        const int64_t upto = std::min<int64_t>(first_kept, int64_t(st.tokens.size())) / pool->B;
+        for (int64_t j = upto - 1; j >= 0; --j) {
+            const int32_t b = st.blocks[size_t(j)];
+            if (b < 0) continue;
+            if (--pool->ref[b] == 0) pool->push_back(b);
+            st.blocks[size_t(j)] = -1;
+            st.dropped = true;
+        }
+        return KV_OK;
+    } catch (...) {
+        PKV_FAIL(KV_EINTERNAL, "kv_pool_drop_prefix: unexpected exception");
+    }
+}
+
+int kv_tree_masks(const int32_t *parents, int32_t n, uint32_t *masks) {
+    if (!parents || !masks || n < 0 || n > 32)
+        PKV_FAIL(KV_EINVAL, "kv_tree_masks: null pointer or n %d outside 0 .. 32", n);
+    uint32_t m[32];
+    for (int32_t r = 0; r < n; ++r) {
+        const int32_t p = parents[r];
+        if (p < -1 || p >= r) PKV_FAIL(KV_EINVAL, "kv_tree_masks: parent %d of row %d is not -1 or an earlier row", p, r);
+        m[r] = (1u << r) | (p >= 0 ? m[p] : 0u);
+    }
+    for (int32_t r = 0; r < n; ++r) masks[r] = m[r];
+    return KV_OK;
 }
 
 int kv_pool_stats(const kv_pool *pool, int32_t *free_blocks, int32_t *cached_blocks,

@@ -10,9 +10,11 @@ import synth
 TOL = {"bf16": 2e-3, "f32": 1e-5, "fp8": 2e-3}
 
 
-def oracle_side(w, fill_nan=True):
+def oracle_side(w, fill_nan=True, tree_mask=None, window=0, drop=None):
     """Oracle allocation (same call order as the device staging), oracle
-    scatter into NaN-filled pools, oracle paged attention."""
+    scatter into NaN-filled pools, oracle paged attention (with tree masks
+    and a sliding window when given). drop: {sequence: first kept position}
+    frees those sequences' blocks below it after the scatter."""
     a = oracle.Allocator(w.num_blocks, w.block_size, w.free_order)
     maxb = w.max_blocks_per_seq
     res, step = [], []
@@ -36,9 +38,13 @@ def oracle_side(w, fill_nan=True):
         n_res = seq.ctx - seq.n_step
         put(kp, vp, seq.k[:n_res], seq.v[:n_res], res[s])
         put(kp, vp, seq.k[n_res:], seq.v[n_res:], step[s])
+    if drop:
+        for s, first in drop.items():
+            a.drop_prefix(s, first)
+        tables = [a.table_row(s, maxb) for s in range(len(w.seqs))]
     tables = np.array(tables, dtype=np.int32)
     out = oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
-                                 w.num_kv_heads, w.scale, w.sinks, w.dtype)
+                                 w.num_kv_heads, w.scale, w.sinks, w.dtype, tree_mask=tree_mask, window=window)
     return tables, kp, vp, out
 
 

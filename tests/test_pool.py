@@ -1,7 +1,8 @@
 """Product block manager (C++, host only) against the oracle allocator:
 identical block tables, slot mappings and counters, bit for bit, over scripted
-and random scenarios, including pool exhaustion, releases, LRU reuse and forced
-hash collisions."""
+and random scenarios, including pool exhaustion, releases, LRU reuse, forced
+hash collisions, rollbacks (truncate, with copy-on-write of shared blocks) and
+freed prefixes below a sliding window."""
 import numpy as np
 import pytest
 
@@ -47,6 +48,37 @@ class Pair:
         self.pk.kv_pool_release(self.c, seq)
         self.check_stats()
 
+    def truncate(self, seq, new_len, maxb=64):
+        try:
+            want = self.o.truncate(seq, new_len)
+        except oracle.OutOfBlocks:
+            with pytest.raises(self.pk.KVError) as e:
+                self.pk.kv_pool_truncate(self.c, seq, new_len)
+            assert e.value.code == self.pk.KV_ENOMEM
+            self.check_stats()
+            return None
+        except ValueError:
+            with pytest.raises(self.pk.KVError) as e:
+                self.pk.kv_pool_truncate(self.c, seq, new_len)
+            assert e.value.code == self.pk.KV_EINVAL
+            return None
+        got = self.pk.kv_pool_truncate(self.c, seq, new_len)
+        assert got == tuple(want)
+        self.check_row(seq, maxb)
+        self.check_stats()
+        return want
+
+    def drop_prefix(self, seq, first_kept, maxb=64):
+        self.o.drop_prefix(seq, first_kept)
+        self.pk.kv_pool_drop_prefix(self.c, seq, first_kept)
+        self.check_row(seq, maxb)
+        self.check_stats()
+
+    def check_row(self, seq, maxb):
+        row, nb, ctx, _ = self.pk.kv_pool_alloc(self.c, seq, [], maxb)
+        assert list(row) == self.o.table_row(seq, maxb)
+        assert ctx == len(self.o.seqs[seq]["tokens"])
+
     def check_stats(self):
         assert self.pk.kv_pool_stats(self.c) == self.o.stats()
 
@@ -70,6 +102,81 @@ def test_mixed_step_shares_prefix_in_product(pk):
         assert (rows[s][:181] == rows[0][:181]).all()
     live = sum(-(-seq.ctx // 16) for seq in w.seqs) - 181 * 47
     assert pk.kv_pool_stats(p)[2] == live
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("collide", [False, True])
+def test_random_scenarios_with_rollback_identical(pk, seed, collide):
+    """Appends, releases, truncates (into own, shared and partial blocks,
+    to block boundaries, to zero) and dropped prefixes, in random order."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.choice([2, 4, 16]))
+    nb = int(rng.integers(10, 48))
+    pair = Pair(pk, nb, B, rng.permutation(nb), collide)
+    prefixes = [list(rng.integers(0, 4, size=int(rng.integers(B, 4 * B)))) for _ in range(2)]
+    live = set()
+    counts = {"truncate": 0, "copy": 0, "drop": 0}
+    for step in range(200):
+        op = rng.random()
+        if op < 0.45 or not live:
+            seq = int(rng.integers(0, 6))
+            if seq not in live:
+                toks = prefixes[int(rng.integers(0, 2))] + list(rng.integers(0, 4, size=int(rng.integers(0, 2 * B))))
+            else:
+                toks = list(rng.integers(0, 4, size=int(rng.integers(0, 3 * B + 1))))
+            if pair.alloc(seq, toks, 64) is not None:
+                live.add(seq)
+        elif op < 0.75:
+            seq = sorted(live)[int(rng.integers(0, len(live)))]
+            n = len(pair.o.seqs[seq]["tokens"])
+            new_len = int(rng.integers(0, n + 1)) if rng.random() < 0.8 else n + 1   # sometimes invalid
+            got = pair.truncate(seq, new_len)
+            counts["truncate"] += got is not None
+            counts["copy"] += got is not None and got[0] >= 0
+        elif op < 0.82:
+            seq = sorted(live)[int(rng.integers(0, len(live)))]
+            n = len(pair.o.seqs[seq]["tokens"])
+            pair.drop_prefix(seq, int(rng.integers(0, n + 1)))
+            counts["drop"] += 1
+        else:
+            seq = sorted(live)[int(rng.integers(0, len(live)))]
+            pair.release(seq)
+            live.discard(seq)
+    assert counts["truncate"] > 10 and counts["drop"] > 3
+
+
+def test_truncate_copy_on_write_in_product(pk):
+    pair = Pair(pk, 16, 4)
+    toks = list(range(1, 13))
+    a = pair.alloc(1, toks, 8)
+    pair.alloc(2, toks, 8)
+    src, dst = pair.truncate(2, 5, 8)
+    assert src == a[0][1] and dst >= 0
+    row, _, _, _ = pk.kv_pool_alloc(pair.c, 2, [], 8)
+    assert row[1] == dst and row[0] == a[0][0]
+
+
+def test_truncate_enomem_is_atomic(pk):
+    pair = Pair(pk, 3, 4)
+    toks = list(range(1, 13))
+    pair.alloc(1, toks, 8)
+    pair.alloc(2, toks, 8)
+    before = pk.kv_pool_stats(pair.c)
+    assert pair.truncate(2, 5, 8) is None          # needs a copy, no block free
+    assert pk.kv_pool_stats(pair.c) == before
+    row, _, ctx, _ = pk.kv_pool_alloc(pair.c, 2, [], 8)
+    assert ctx == 12
+
+
+def test_tree_masks_match_oracle_and_reject_bad_parents(pk):
+    rng = np.random.default_rng(7)
+    for n in [0, 1, 5, 16, 32]:
+        parents = [-1] + [int(rng.integers(-1, r)) for r in range(1, n)] if n else []
+        np.testing.assert_array_equal(pk.kv_tree_masks(parents), oracle.tree_masks(parents))
+    for bad in ([0], [-1, 1], [-2], [-1] * 33):
+        with pytest.raises(pk.KVError) as e:
+            pk.kv_tree_masks(bad)
+        assert e.value.code == pk.KV_EINVAL
 
 
 @pytest.mark.parametrize("seed", range(6))
