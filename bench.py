@@ -56,11 +56,46 @@ def unique_kv_bytes(w, tables):
     return tokens * w.num_kv_heads * row_bytes(w) * 2
 
 
+def visible_kv_bytes(w, window):
+    """K+V bytes of the keys some row of each sequence sees under a sliding
+    window (the workloads given a window share no block inside it)."""
+    tokens = sum(seq.ctx - max(0, seq.ctx - seq.q_len - window + 1) for seq in w.seqs)
+    return tokens * w.num_kv_heads * row_bytes(w) * 2
+
+
+def parse_workload(name):
+    """A synthetic workload name with optional suffixes: "_tree" (each
+    sequence's window is a seeded random draft tree, attended through
+    paged_attention_masked_forward) and "_swa<W>" (a sliding window of W
+    keys, the blocks below every row's window freed first)."""
+    tree, window, base = False, 0, name
+    if "_swa" in base:
+        base, w = base.rsplit("_swa", 1)
+        window = int(w)
+    if base.endswith("_tree"):
+        base, tree = base[:-5], True
+    return base, tree, window
+
+
+def tree_mask_words(w, seed=1234):
+    """Ancestor masks of one random tree per window (parent of row r drawn
+    from -1 .. r - 1), bit r set for the row itself."""
+    rng = np.random.default_rng(seed)
+    words = []
+    for seq in w.seqs:
+        masks = []
+        for r in range(seq.q_len):
+            p = int(rng.integers(-1, r)) if r else -1
+            masks.append((1 << r) | (masks[p] if p >= 0 else 0))
+        words += masks
+    return np.array(words, dtype=np.uint32)
+
+
 def logical_kv_bytes(w):
     return sum(seq.ctx for seq in w.seqs) * w.num_kv_heads * row_bytes(w) * 2
 
 
-def cpu_baseline(w, kv_bytes, rows, seconds):
+def cpu_baseline(w, kv_bytes, rows, seconds, tree_mask=None, window=0):
     """The oracle, as it stands, on the host cores: its own allocation and
     scatter build the pools once; each timed call is gather + fp64 attention
     over the whole batch of one layer."""
@@ -84,7 +119,8 @@ def cpu_baseline(w, kv_bytes, rows, seconds):
     while time.perf_counter() < t_end or len(times) < 2:
         t1 = time.perf_counter()
         oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
-                               w.num_kv_heads, w.scale, w.sinks, w.dtype, threads)
+                               w.num_kv_heads, w.scale, w.sinks, w.dtype, threads, tree_mask=tree_mask,
+                               window=window)
         times.append(time.perf_counter() - t1)
         if len(times) >= 500:
             break
@@ -136,6 +172,15 @@ def _short(name):
     return name.split("(")[0].replace("void ", "").replace("pkv::", "").strip()
 
 
+def _appending(kernel):
+    """True for attn_parallel instances with the appending path: template
+    arguments <head_dim, tiles, prefetch, append, 8-bit pools>."""
+    if not kernel.startswith("attn_parallel<"):
+        return False
+    args = [a.strip() for a in kernel[kernel.index("<") + 1:kernel.rindex(">")].split(",")]
+    return len(args) == 5 and args[3] == "true"
+
+
 def _counter_means(d, counter):
     """Mean of `counter` per dispatch, per kernel, in the counter's unit."""
     acc = {}
@@ -185,7 +230,7 @@ def summarize_profile(d, workload, commands):
         fb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
         # the attention call as paged_attention_forward issues it: split
         # kernels without the appending path (its last template argument)
-        if k.startswith(ATTN_KERNELS) and not (k.startswith("attn_parallel") and k.endswith("true>")):
+        if k.startswith(ATTN_KERNELS) and not _appending(k):
             traffic += fb + wb
         lines.append(f"| {k} | {fn} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
     lines += ["", "Traffic of one paged_attention_forward call (the bench's attention-only timing): the split",
@@ -246,8 +291,13 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.by_name(args.workload)
+    base, tree, window = parse_workload(args.workload)
+    w = synth.by_name(base)
+    w.name = args.workload
     elt = elem_bytes(w)
+    if tree and max(seq.q_len for seq in w.seqs) > 32:
+        print("bench.py: tree windows take at most 32 rows per sequence", file=sys.stderr)
+        return 2
 
     # host block allocation for the batch, timed on its own
     t0 = time.perf_counter()
@@ -258,9 +308,22 @@ def main(argv=None):
     del pool
 
     pool_bytes = w.num_blocks * w.num_kv_heads * 16 * row_bytes(w) * 2
-    layers = args.layers or max(1, math.ceil(MIN_FOOTPRINT / pool_bytes))
+    # enough pool copies that one step touches more than the last-level cache
+    # holds; a sliding window touches only its keys, so its copies are counted
+    # from those (at most 40 GiB of pools)
+    touched = visible_kv_bytes(w, window) if window else pool_bytes
+    layers = args.layers or max(1, min(math.ceil(MIN_FOOTPRINT / touched), (40 << 30) // pool_bytes))
     st = stage(w, device=dev, copies=layers, poison=False)
-    kv_bytes = unique_kv_bytes(w, st.tables_np)
+    kv_bytes = unique_kv_bytes(w, st.tables_np) if not window else visible_kv_bytes(w, window)
+    tables = st.tables
+    if window:
+        # blocks below every row's window go back to the pool
+        for s, seq in enumerate(w.seqs):
+            pk.kv_pool_drop_prefix(st.pool, s, max(0, seq.ctx - seq.q_len - window + 1))
+        rows_np = np.stack([pk.kv_pool_alloc(st.pool, s, [], st.max_blocks)[0] for s in range(len(w.seqs))])
+        tables = torch.from_numpy(rows_np.astype(np.int32)).to(dev)
+    tmask = torch.from_numpy(tree_mask_words(w).view(np.int32)).to(dev) if tree else None
+    masked = tree or window > 0
     rows = w.total_rows
     q_bytes = rows * w.num_q_heads * w.head_dim * elt
     out_bytes = rows * w.num_q_heads * w.head_dim * 4
@@ -268,11 +331,27 @@ def main(argv=None):
     scatter_bytes = n_step_tok * w.num_kv_heads * (w.head_dim * elt + row_bytes(w)) * 2
     stream = torch.cuda.current_stream()
 
+    def attend(l):
+        if masked:
+            pk.paged_attention_masked_forward(st.q, st.k_pools[l], st.v_pools[l], tables, st.context_lens, st.qsl,
+                                              st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks,
+                                              tree_mask=tmask, sliding_window=window, out=st.out,
+                                              workspace=st.workspace)
+        else:
+            pk.paged_attention_forward(st.q, st.k_pools[l], st.v_pools[l], tables, st.context_lens, st.qsl,
+                                       st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
+                                       workspace=st.workspace)
+
     def layer_call(l):
-        pk.paged_attention_append_forward(st.q, st.k_step, st.v_step, st.step_slots, st.k_pools[l],
-                                          st.v_pools[l], st.tables, st.context_lens, st.qsl, st.max_q_len,
-                                          st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
-                                          workspace=st.workspace)
+        if masked:
+            # masked calls take no appended rows: scatter, then attend
+            pk.kv_append_scatter(st.k_step, st.v_step, st.step_slots, st.k_pools[l], st.v_pools[l])
+            attend(l)
+        else:
+            pk.paged_attention_append_forward(st.q, st.k_step, st.v_step, st.step_slots, st.k_pools[l],
+                                              st.v_pools[l], tables, st.context_lens, st.qsl, st.max_q_len,
+                                              st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
+                                              workspace=st.workspace)
 
     def step():
         for l in range(layers):
@@ -280,9 +359,7 @@ def main(argv=None):
 
     def attention_only():
         for l in range(layers):
-            pk.paged_attention_forward(st.q, st.k_pools[l], st.v_pools[l], st.tables, st.context_lens, st.qsl,
-                                       st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
-                                       workspace=st.workspace)
+            attend(l)
 
     # Both loops are captured once into HIP graphs and replayed, as a serving
     # loop replays its decode step: host launch cost stays out of the timing.
@@ -334,7 +411,7 @@ def main(argv=None):
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, kv_bytes, rows, args.cpu_seconds)
+        cpu = cpu_baseline(w, kv_bytes, rows, args.cpu_seconds, tree_mask_words(w) if tree else None, window)
 
     line = {
         "metric": METRIC,
@@ -353,6 +430,7 @@ def main(argv=None):
             "workload": w.name, "seqs": len(w.seqs), "context_lens": [int(s.ctx) for s in w.seqs],
             "rows_per_layer": rows, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": 16, "layers_per_step": layers,
+            "tree_windows": tree, "sliding_window": window,
             "kv_bytes_per_layer": kv_bytes, "logical_kv_bytes_per_layer": logical_kv_bytes(w),
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

@@ -77,6 +77,10 @@ struct AttnParams {
     float *ws_acc;      // [rows][Hq][max_splits][D]
     float *out;         // [rows][Hq][D]
     int32_t num_seqs, total_rows, Hq, Hkv, G, max_blocks_per_seq, num_blocks, max_splits;
+    // split slots per sequence in the parallel grid: max_splits, or under a
+    // sliding window the splits from the one holding the sequence's lowest
+    // visible key on (no more can hold a visible key)
+    int32_t grid_splits;
     int32_t decode_only;  // every sequence has q_len == 1 (rows packed in sequence order)
     int32_t seq_stride;   // sequence slots per split slot in the parallel grid (>= num_seqs)
     float scale_log2;
@@ -638,7 +642,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     const int kvh = blockIdx.x % P.Hkv;
     const int rest = blockIdx.x / P.Hkv;
     const int s = rest % P.seq_stride;
-    const int j = split_of_slot(rest / P.seq_stride, P.max_splits);
+    int j = split_of_slot(rest / P.seq_stride, P.max_splits);
     if (s >= P.num_seqs) return;  // padding slot
 
     // Loads that need nothing but the grid position go out together: the context
@@ -647,6 +651,12 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     // (no branches among them, so that none waits for another)
     const int ctx = P.ctx_lens[s];
     const int qa = P.qsl[s], qb = P.qsl[s + 1];
+    if constexpr (MASKED) {
+        if (P.grid_splits < P.max_splits) {  // grid slot z: the z-th split from the lowest visible key's
+            j = split_index(max(ctx - (P.decode_only ? 1 : qb - qa) - P.window + 1, 0)) + rest / P.seq_stride;
+            if (j >= P.max_splits) return;
+        }
+    }
     const int ks = split_begin(j);
     const int ql = (split_begin(j + 1) - ks) >> 2;
     const int kq0 = ks + wave * ql;
@@ -838,14 +848,20 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
     const size_t base0 = ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * P.max_splits;
     TileState<DW> acc;
     state_clear(acc);
+    // the slots the parallel grid wrote (all, or a sliding window's run)
+    int j0 = 0, j1 = P.max_splits;
+    if (P.grid_splits < P.max_splits) {
+        j0 = split_index(max(P.ctx_lens[s] - q_len - P.window + 1, 0));
+        j1 = min(j0 + P.grid_splits, P.max_splits);
+    }
     // eight split states per round trip
     constexpr int U = 8;
-    for (int j = 0; j < P.max_splits; j += U) {
+    for (int j = j0; j < j1; j += U) {
         TileState<DW> x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             state_clear(x[u]);
-            if (j + u < P.max_splits) {
+            if (j + u < j1) {
                 const float2 ml = P.ws_ml[base0 + j + u];
                 x[u].m = ml.x;
                 x[u].l = ml.y;
@@ -1446,7 +1462,7 @@ static int device_cus() {
 
 template <int D, int NT, bool APPEND, bool Q8, bool MASKED>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
-    const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.max_splits;
+    const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.grid_splits;
     if constexpr (NT == 1) {
         if (nwg <= device_cus()) {
             hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, Q8, MASKED>), dim3((unsigned)nwg), dim3(256), 0,
@@ -1587,8 +1603,15 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     // by count, not by work. A sequence stride of 1 mod 4 (padding slots exit
     // at once) moves each sequence to the next engine at every split slot,
     // so that no engine gets all the splits of the same long sequences.
+    // Under a sliding window, the keys some row of a sequence sees span at most
+    // window + max_q_len - 1 positions, which meet at most that many keys / 256
+    // (rounded up) + 1 splits.
+    P.grid_splits = max_splits;
+    if (mk && mk->window > 0)
+        P.grid_splits = (int32_t)std::min<int64_t>(
+            max_splits, ((int64_t)mk->window + max_q_len - 1 + kSplitA - 1) / kSplitA + 1);
     P.seq_stride = num_seqs;
-    if ((int64_t)num_kv_heads * num_seqs * max_splits > device_cus()) P.seq_stride += (5 - num_seqs % 4) % 4;
+    if ((int64_t)num_kv_heads * num_seqs * P.grid_splits > device_cus()) P.seq_stride += (5 - num_seqs % 4) % 4;
     P.scale_log2 = scale * kLog2e;
     P.k_new = P.v_new = nullptr;
     P.slots = nullptr;
