@@ -694,3 +694,80 @@ def accept_path(parents, draft_tokens, choices, root_choice):
             return path, want
         path.append(nxt)
         cur, want = nxt, int(choices[nxt])
+
+
+# ----------------------------------------------------------------------------
+# QK-norm + RoPE before the scatter-write
+# ----------------------------------------------------------------------------
+#
+# TensorSharp "高级功能" page: for Qwen 3.5/3.6 one kernel applies QK-Norm and
+# NeoX RoPE on the prefill path; the batched forward pairs its projection with
+# the paged K/V scatter-write. The pages fix no formula beyond those names.
+# The reading used here:
+#
+# * QK-norm: RMSNorm over the head dimension, per (token, head) row:
+#   y = x / sqrt(mean(x^2) + eps) * (offset + w), w one weight per dimension
+#   (bf16), offset 0 (weights multiply) or 1 (zero-centred weights);
+# * NeoX RoPE on the first rotary_dim dimensions: pairs (i, i + rotary_dim/2),
+#   i < rotary_dim/2, turned by the angle pos * theta^(-2i/rotary_dim):
+#   (a, b) -> (a cos - b sin, b cos + a sin); later dimensions pass through;
+# * exact arithmetic, one rounding to bf16 (nearest, ties to even) at the end;
+# * K (normed, rotated) and V (as given) then go into the pools at their
+#   slots, as the scatter-write puts them.
+
+
+def f64_to_bf16_bits(x):
+    """Round float64 values to bf16 once (nearest, ties to even), raw bits.
+    The quantum of x is 2^(e - 8) for x in [2^(e-1), 2^e), at least 2^-133
+    (bf16's subnormal step)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    qexp = np.maximum(e - 8, -133)
+    r = np.rint(np.ldexp(x, -qexp))             # np.rint rounds halves to even
+    v = np.ldexp(r, qexp).astype(np.float32)    # exact: 8 significant bits fit
+    return (v.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rms_norm(x, weight, eps, weight_offset=0.0):
+    """x [..., D] float64; weight [D] float64 (or None: no weight)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    y = x / np.sqrt(ms + float(eps))
+    if weight is not None:
+        y = y * (float(weight_offset) + np.asarray(weight, dtype=np.float64))
+    return y
+
+
+def rope_neox(x, positions, theta, rotary_dim):
+    """x [n, H, D] float64, positions [n]: NeoX rotation of the first
+    rotary_dim dimensions."""
+    x = np.array(x, dtype=np.float64)
+    half = rotary_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    inv_freq = float(theta) ** (-2.0 * i / rotary_dim)                     # [half]
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None]  # [n, half]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = x[..., :half].copy(), x[..., half:rotary_dim].copy()
+    x[..., :half] = a * c - b * s
+    x[..., half:rotary_dim] = b * c + a * s
+    return x
+
+
+def qknorm_rope(q, k, positions, q_weight, k_weight, eps, theta, rotary_dim, weight_offset=0.0):
+    """q [n, Hq, D], k [n, Hkv, D] bf16 bits; weights [D] bf16 bits or None
+    (no weight: the normalized row itself). Returns (q_out, k_out) bf16 bits."""
+    qw = None if q_weight is None else to_f32(q_weight, "bf16").astype(np.float64)
+    kw = None if k_weight is None else to_f32(k_weight, "bf16").astype(np.float64)
+    qn = rms_norm(to_f32(q, "bf16"), qw, eps, weight_offset)
+    kn = rms_norm(to_f32(k, "bf16"), kw, eps, weight_offset)
+    return (f64_to_bf16_bits(rope_neox(qn, positions, theta, rotary_dim)),
+            f64_to_bf16_bits(rope_neox(kn, positions, theta, rotary_dim)))
+
+
+def qknorm_rope_scatter(k_pool, v_pool, q, k, v, positions, slots, q_weight, k_weight, eps, theta,
+                        rotary_dim, weight_offset=0.0):
+    """The whole producer step: normed, rotated Q is returned; normed,
+    rotated K and V are written into the (bf16) pools at the slots."""
+    q_out, k_out = qknorm_rope(q, k, positions, q_weight, k_weight, eps, theta, rotary_dim, weight_offset)
+    scatter(k_pool, v_pool, k_out, np.asarray(v), slots)
+    return q_out
