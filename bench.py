@@ -258,6 +258,67 @@ def committed_traffic(workload):
     return None
 
 
+def producer_bench(args, torch, synth, pk):
+    """kv_qknorm_rope_scatter over the step tokens of a bf16 workload (every
+    row of every sequence: its Q, K and V heads), Qwen3-like settings (norm
+    weights, NeoX RoPE over the whole head, theta 1e6). Enough copies of the
+    inputs and pools that one timed step misses the last-level cache."""
+    w = synth.by_name(args.workload)
+    if w.dtype != "bf16":
+        print("bench.py: the producer step writes bf16 pools", file=sys.stderr)
+        return 2
+    n, Hq, Hkv, D = w.total_rows, w.num_q_heads, w.num_kv_heads, w.head_dim
+    alg = 2 * n * (Hq + 2 * Hkv) * D * 2 + 8 * n        # rows read and written, positions and slots
+    copies = args.layers or max(1, math.ceil(MIN_FOOTPRINT / alg))
+    g = torch.Generator(device="cuda").manual_seed(7)
+    mk = lambda *s: torch.randn(s, generator=g, device="cuda").to(torch.bfloat16)
+    nb = -(-n // 16) + 1
+    sets = []
+    pos = torch.from_numpy(np.concatenate([np.arange(s.ctx - s.q_len, s.ctx) for s in w.seqs]).astype(np.int32)).cuda()
+    slots = torch.arange(n, dtype=torch.int32, device="cuda") + 16    # whole blocks where the rows allow
+    for _ in range(copies):
+        kp, vp = pk.empty_pools(nb + 1, Hkv, D, torch.bfloat16, "cuda")
+        sets.append((mk(n, Hq, D), mk(n, Hkv, D), mk(n, Hkv, D), torch.empty(n, Hq, D, dtype=torch.bfloat16,
+                                                                            device="cuda"), kp, vp))
+    qw, kw = mk(D), mk(D)
+
+    def step():
+        for q, k, v, qo, kp, vp in sets:
+            pk.kv_qknorm_rope_scatter(q, k, v, pos, slots, kp, vp, q_norm_weight=qw, k_norm_weight=kw, eps=1e-6,
+                                      rope_theta=1e6, rotary_dim=D, q_out=qo)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    us_call = ms * 1e3 / copies
+    gbs = alg / (us_call * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "kv_qknorm_rope_scatter GB/s (QK-norm + NeoX RoPE + paged scatter), 1 GPU", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded N(0,1) rows)",
+        "config": {"workload": args.workload, "tokens": n, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "copies_per_step": copies},
+        "call_us": round(us_call, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "qknorm_rope_scatter_kernel", "alg_bytes_per_launch": alg},
+    }), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -270,6 +331,8 @@ def main(argv=None):
                     help="only run a plain device copy of BYTES (for counter calibration) and exit")
     ap.add_argument("--summarize", metavar="DIR", help="only write the profile summary from rocprofv3 output")
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the summary")
+    ap.add_argument("--producer", action="store_true",
+                    help="time kv_qknorm_rope_scatter on the workload's step tokens instead of the attention step")
     args = ap.parse_args(argv)
 
     if args.summarize:
@@ -291,6 +354,8 @@ def main(argv=None):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.producer:
+        return producer_bench(args, torch, synth, pk)
     base, tree, window = parse_workload(args.workload)
     w = synth.by_name(base)
     w.name = args.workload

@@ -273,6 +273,34 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
                       int32_t dtype, void *hip_stream);
 
 /*
+ * The producer step before attention in one pass (TensorSharp "高级功能"
+ * page: a fused QK-Norm + NeoX RoPE kernel for Qwen 3.5/3.6, and the batched
+ * forward's paged K/V scatter-write). For token i (position positions[i]) and
+ * every head row x of q ([n][num_q_heads][head_dim]) and k
+ * ([n][num_kv_heads][head_dim]), all bf16:
+ *   y = x / sqrt(mean(x^2) + eps) * (weight_offset + w)   (w: q_norm_weight or
+ *       k_norm_weight, bf16 [head_dim]; NULL: no weight factor)
+ *   the first rotary_dim dimensions of y turn in NeoX pairs (j, j + rotary_dim/2)
+ *       by the angle positions[i] * rope_theta^(-2j / rotary_dim):
+ *       (a, b) -> (a cos - b sin, b cos + a sin); the rest pass through
+ *   the result is rounded once to bf16 (computed in float32, the angle in float64).
+ * Q rows go to q_out ([n][num_q_heads][head_dim] bf16); K rows and the v rows
+ * (unchanged) go into the bf16 pools at slot_mapping[i] as kv_append_scatter
+ * writes them (-1: not written). weight_offset 1 serves zero-centred norm
+ * weights. Supported: dtype KV_BF16, head_dim 64, 128 or 256, block_size 16,
+ * rotary_dim even, at most head_dim, rotary_dim / 2 a multiple of head_dim / 16
+ * (0: no rotation). Rows, q_out and pools are 16-byte aligned.
+ * Stream-ordered, asynchronous.
+ * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
+ */
+int kv_qknorm_rope_scatter(const void *q, const void *k, const void *v, const int32_t *positions,
+                           const void *q_norm_weight, const void *k_norm_weight, float eps, float weight_offset,
+                           float rope_theta, int32_t rotary_dim, const int32_t *slot_mapping, int32_t n,
+                           void *q_out, void *k_pool, void *v_pool, int32_t num_blocks, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                           void *hip_stream);
+
+/*
  * Bytes of device workspace paged_attention_forward needs for these sizes
  * (0 on invalid sizes). The workspace holds per-split partial results; its
  * contents need no initialisation and are meaningless after a call. Calls that

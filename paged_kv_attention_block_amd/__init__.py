@@ -25,7 +25,7 @@ __all__ = [
     "KV_F32", "KV_BF16", "KV_FP8", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
     "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks", "kv_append_scatter",
-    "kv_copy_blocks", "kv_accept_paths", "paged_attention_workspace_size", "paged_attention_forward",
+    "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter", "paged_attention_workspace_size", "paged_attention_forward",
     "paged_attention_append_forward", "paged_attention_masked_forward", "empty_pools", "BLOCK_SIZE",
 ]
 
@@ -58,6 +58,8 @@ _lib.kv_pool_drop_prefix.argtypes = [_p, _i64, _i32]
 _lib.kv_tree_masks.argtypes = [_p, _i32, _p]
 _lib.kv_copy_blocks.argtypes = [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p]
 _lib.kv_accept_paths.argtypes = [_p, _p, _p, _p, _p, _i32, _p, _p, _p, _p]
+_lib.kv_qknorm_rope_scatter.argtypes = [_p, _p, _p, _p, _p, _p, _f32, _f32, _f32, _i32, _p, _i32, _p, _p, _p,
+                                        _i32, _i32, _i32, _i32, _i32, _i32, _p]
 _lib.kv_append_scatter.argtypes = [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p]
 _lib.paged_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
 _lib.paged_attention_workspace_size.restype = _sz
@@ -72,7 +74,8 @@ _lib.paged_attention_masked_forward.argtypes = [
     _f32, _p, _p, _i32, _p, _p, _sz, _p]
 for _name in ("kv_pool_create", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
               "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks",
-              "kv_append_scatter", "kv_copy_blocks", "kv_accept_paths", "paged_attention_forward",
+              "kv_append_scatter", "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter",
+              "paged_attention_forward",
               "paged_attention_append_forward", "paged_attention_masked_forward"):
     getattr(_lib, _name).restype = ctypes.c_int
 
@@ -309,6 +312,43 @@ def kv_accept_paths(parents, draft_tokens, choices, root_choices, query_start_lo
                                 root_choices.data_ptr(), query_start_loc.data_ptr(), S, path.data_ptr(),
                                 path_len.data_ptr(), bonus.data_ptr(), _stream_ptr(stream)))
     return path, path_len, bonus
+
+
+def kv_qknorm_rope_scatter(q, k, v, positions, slot_mapping, k_pool, v_pool, q_norm_weight=None,
+                           k_norm_weight=None, eps: float = 1e-6, weight_offset: float = 0.0,
+                           rope_theta: float = 1e6, rotary_dim=None, q_out=None, stream=None):
+    """QK-norm + NeoX RoPE of q [n, Hq, D] and k [n, Hkv, D] (bf16), rotated Q returned (q_out), rotated
+    K and v written into the bf16 pools at slot_mapping [n] (see pagedkv.h)."""
+    torch = _torch()
+    _need(q, "q", dtype=torch.bfloat16, ndim=3)
+    _need(k, "k", dtype=torch.bfloat16, ndim=3)
+    _need(v, "v", dtype=torch.bfloat16, ndim=3)
+    _need(positions, "positions", dtype=torch.int32, ndim=1)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
+    n, hq, d = q.shape
+    if k.shape[0] != n or v.shape != k.shape or k.shape[2] != d or positions.shape[0] != n or \
+            slot_mapping.shape[0] != n:
+        raise KVError(KV_EINVAL, "q, k, v, positions and slot_mapping sizes disagree")
+    hkv = k.shape[1]
+    code, nb = _pools(k_pool, v_pool, torch.bfloat16, hkv, d)
+    for w, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        if w is not None:
+            _need(w, name, dtype=torch.bfloat16, ndim=1)
+            if w.shape[0] != d:
+                raise KVError(KV_EINVAL, f"{name} needs head_dim values")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    _need(q_out, "q_out", dtype=torch.bfloat16, ndim=3)
+    if q_out.shape != q.shape:
+        raise KVError(KV_EINVAL, "q_out has the wrong shape")
+    _check(_lib.kv_qknorm_rope_scatter(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), positions.data_ptr(),
+        None if q_norm_weight is None else q_norm_weight.data_ptr(),
+        None if k_norm_weight is None else k_norm_weight.data_ptr(), float(eps), float(weight_offset),
+        float(rope_theta), d if rotary_dim is None else int(rotary_dim), slot_mapping.data_ptr(), n,
+        q_out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), nb, hq, hkv, d, BLOCK_SIZE, code,
+        _stream_ptr(stream)))
+    return q_out
 
 
 def paged_attention_workspace_size(num_seqs: int, total_q_rows: int, num_q_heads: int, head_dim: int,
