@@ -174,11 +174,11 @@ def _short(name):
 
 def _appending(kernel):
     """True for attn_parallel instances with the appending path: template
-    arguments <head_dim, tiles, prefetch, append, 8-bit pools>."""
+    arguments <head_dim, tiles, prefetch, append, 8-bit pools, masked>."""
     if not kernel.startswith("attn_parallel<"):
         return False
     args = [a.strip() for a in kernel[kernel.index("<") + 1:kernel.rindex(">")].split(",")]
-    return len(args) == 5 and args[3] == "true"
+    return len(args) >= 4 and args[3] == "true"
 
 
 def _counter_means(d, counter):

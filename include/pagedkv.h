@@ -189,9 +189,9 @@ int kv_pool_truncate(kv_pool *pool, int64_t seq_id, int32_t new_len, int32_t *co
 /*
  * Free the blocks of sequence `seq_id` that lie wholly below position
  * first_kept (blocks j with (j + 1) * block_size <= first_kept), for
- * sliding-window attention, whose rows never see them again (the
- * sliding-window attention of the drafters and models on the TensorFold
- * pages). Freed blocks lose one reference each, go to the back of the free
+ * sliding-window attention, whose rows never see them again (TensorSharp
+ * "高级功能" page, "性能优化": sliding-window layers, prefix reuse bounded by
+ * the window). Freed blocks lose one reference each, go to the back of the free
  * list when unreferenced (hash entries kept) and read -1 in the sequence's
  * table row from now on; positions keep their meaning. Blocks that later
  * become full after a freed block are not registered for sharing, and no
@@ -388,8 +388,9 @@ int paged_attention_append_forward(const void *q, const void *k_new, const void 
  * j of tree_mask[query_start_loc[s] + r] is set; bits at or above r are
  * ignored. All bits below r set is the causal window. With a tree_mask every
  * q_len must be at most 32 (max_q_len > 32: KV_EINVAL).
- * Sliding window (the sliding-window attention of the drafters and models on
- * the same pages): sliding_window = 0 for none, else the row at position p
+ * Sliding window (TensorSharp "高级功能" page: SWA-1024 drafters in
+ * "MTP / NextN 推测解码", sliding-window layers in "性能优化"):
+ * sliding_window = 0 for none, else the row at position p
  * sees only keys t > p - sliding_window. Table entries of blocks that no row
  * of the call can see may be -1 (kv_pool_drop_prefix).
  * Both only remove keys; the row's own key always stays visible. With

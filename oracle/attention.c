@@ -31,8 +31,10 @@
  *     rows): with base = ctx - q_len, row r sees every key below base, its
  *     own key base + r, and the window key base + j (j < r) when bit j of its
  *     mask is set; a chain is the mask with every bit below r set;
- *   - a sliding window of W keys (the sliding-window attention of the drafters
- *     and models on the same pages): row r also needs t > p - W.
+ *   - a sliding window of W keys (TensorSharp "高级功能" page: the drafters'
+ *     sliding-window KV rings and SWA-1024 in "MTP / NextN 推测解码", the
+ *     sliding-window layers and window-bounded prefix reuse in "性能优化"):
+ *     row r also needs t > p - W.
  * Both only remove keys; the row's own key always stays visible.
  *
  * Inputs arrive as float (every bf16 and fp32 value is exact in float), or K/V

@@ -5,8 +5,8 @@ Tree windows and the accept walk follow the TensorFold page, section on the
 GPU accept kernel (drafts as a chain or a tree of at most 16 rows; the
 accepted path follows the first child whose draft equals the target's
 choice; a rollback restores the KV cache after the path). Sliding windows
-follow the sliding-window attention of the drafters and models on the same
-pages. Tolerances are those of the unmasked parity tests (2e-3 bf16 and
+follow the TensorSharp "高级功能" page (SWA-1024 drafters in "MTP / NextN
+推测解码"; sliding-window layers in "性能优化"). Tolerances are those of the unmasked parity tests (2e-3 bf16 and
 8-bit pools, 1e-5 fp32); block copies, masks and accept paths are exact;
 row invariance is bitwise.
 """

@@ -5,8 +5,8 @@ Tree windows and the accept walk follow the TensorFold page, section on the
 GPU accept kernel (drafts laid out as a chain or a tree of at most 16 rows;
 the accepted path follows the first child whose token equals the target's
 choice; a rollback restores the KV cache after the accepted path). Sliding
-windows follow the sliding-window attention the same pages give their
-drafters and models.
+windows follow the TensorSharp "高级功能" page (SWA-1024 drafters in
+"MTP / NextN 推测解码"; sliding-window layers in "性能优化").
 
 The masked attention is checked against a dense brute force whose mask matrix
 is built by walking parent pointers (not from the mask words the oracle
