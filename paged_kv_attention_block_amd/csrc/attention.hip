@@ -919,8 +919,11 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
     return false;
 }
 
+// Two workgroups per CU (the LDS staging allows no more): bounding the
+// registers to that occupancy keeps the MFMA accumulators in VGPRs, where the
+// per-step rescale and select use them without copies.
 template <int D, bool Q8, bool MASKED>
-__global__ __launch_bounds__(256) void attn_sequential(AttnParams P) {
+__global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     using PoolT = Pool<D, Q8>;
     using Regs = typename PoolT::Regs;
     constexpr int DT = D / 16, KJ = D / 32;
