@@ -98,6 +98,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
     __shared__ int s_slot[kBlk];
     __shared__ int s_full;
     __shared__ __attribute__((aligned(16))) uint16_t sv[kBlk][D];
+    __shared__ double s_inv_freq[D / 2];  // theta^(-2i / rotary_dim), i < rotary_dim / 2
+    if (tid < half) s_inv_freq[tid] = exp2(-(2.0 * tid / A.rotary_dim) * A.log2_theta);
     if (tid < kBlk) {
         const int i = i0 + tid;
         const int sl = i < A.n ? A.slots[i] : -1;
@@ -122,26 +124,30 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
         load_row<CPT>(src, xs[j]);
     }
 
-    // cosine and sine of the lane's dimensions (identity past rotary_dim)
+    __syncthreads();
+    // cosine and sine of the lane's dimensions (identity past rotary_dim):
+    // lanes of the lower half of each pair compute them, their partners
+    // `shift` lanes up take them by shuffle
     float cs[CPT], sn[CPT];
     {
         const double p = have ? (double)A.pos[tok] : 0.0;
+        const bool lower = part * CPT < half;
 #pragma unroll
         for (int e = 0; e < CPT; ++e) {
             const int c = part * CPT + e;
-            cs[e] = 1.f;
-            sn[e] = 0.f;
-            if (c < A.rotary_dim) {
-                const int i = c < half ? c : c - half;
-                const double inv_freq = exp2(-(2.0 * i / A.rotary_dim) * A.log2_theta);
-                const double ang = p * inv_freq;
+            float cv = 1.f, sv_ = 0.f;
+            if (lower) {
+                const double ang = p * s_inv_freq[c];
                 const double turns = rint(ang * (1.0 / (2.0 * M_PI)));
-                const float r = (float)fma(-turns, 2.0 * M_PI, ang);
-                sincosf(r, &sn[e], &cs[e]);
+                sincosf((float)fma(-turns, 2.0 * M_PI, ang), &sv_, &cv);
             }
+            const int src = lower || !shift ? lane : lane - shift;
+            const float co = __shfl(cv, src, 64), so = __shfl(sv_, src, 64);
+            const bool rot = c < A.rotary_dim;
+            cs[e] = rot ? co : 1.f;
+            sn[e] = rot ? so : 0.f;
         }
     }
-    __syncthreads();
     if (tid < 64) {
         const int sl0 = s_slot[0];
         const bool ok = tid >= kBlk || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlk == 0);
