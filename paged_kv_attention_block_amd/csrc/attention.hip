@@ -380,11 +380,109 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     st.m = has ? m_new : st.m;
 }
 
+// Two 16-row tiles through one step: each K operand piece meets both tiles'
+// score MFMAs and each V operand piece both tiles' PV MFMAs as soon as it is
+// formed, so no converted operand outlives its use. Per tile the sequence of
+// operations is step_core's exactly.
+template <int D, bool SCALED, bool MASKED, class KOp, class VOp>
+__device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, const float (&ksc)[8],
+                                  const float (&vsc)[8], const u32x4_t (&qop)[2][D / 32], int kc,
+                                  const RowVis (&rv)[2], int g, float scale_log2) {
+    constexpr int KJ = D / 32, DT = D / 16;
+    f32x4_t s0[2], s1[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) s0[t] = s1[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+        const bf16x8_t k0 = kop(0, j), k1 = kop(1, j);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bf16x8_t b = __builtin_bit_cast(bf16x8_t, qop[t][j]);
+            s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, b, s0[t], 0, 0, 0);
+            s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, b, s1[t], 0, 0, 0);
+        }
+    }
+    bf16x8_t phi[2], plo[2];
+    float alpha[2], m_new[2], rs[2];
+    bool has[2], rescale[2], all_has[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int prow = rv[t].prow;
+        float sc[8];
+        const int lim = prow - (kc + key_off(g));
+        uint32_t vm = 0;
+        if constexpr (MASKED) vm = visible8(rv[t], kc + key_off(g));
+        auto vis = [&](int i) { return MASKED ? ((vm >> i) & 1u) != 0 : i <= lim; };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (SCALED) {
+                sc[i] = vis(i) ? (s0[t][i] * ksc[i]) * scale_log2 : -INFINITY;
+                sc[4 + i] = vis(i + 4) ? (s1[t][i] * ksc[4 + i]) * scale_log2 : -INFINITY;
+            } else {
+                sc[i] = vis(i) ? s0[t][i] * scale_log2 : -INFINITY;
+                sc[4 + i] = vis(i + 4) ? s1[t][i] * scale_log2 : -INFINITY;
+            }
+        }
+        float mx =
+            fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        has[t] = MASKED ? mx != -INFINITY : kc <= prow;
+        m_new[t] = fmaxf(st[t].m, mx);
+        const float m_use = m_new[t] == -INFINITY ? 0.f : m_new[t];
+        alpha[t] = fast_exp2(st[t].m - m_use);
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
+        float r = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        r += __shfl_xor(r, 16, 64);
+        r += __shfl_xor(r, 32, 64);
+        rs[t] = r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float w = pv[e];
+            if constexpr (SCALED) w = w * vsc[e];
+            const __bf16 x = (__bf16)w;
+            phi[t][e] = x;
+            plo[t][e] = (__bf16)(w - (float)x);
+        }
+        rescale[t] = __any(alpha[t] != 1.f);
+        all_has[t] = __all(has[t]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8_t va = vop(dt);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4_t a = st[t].acc[dt];
+            if (rescale[t]) a *= alpha[t];
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], a, 0, 0, 0);
+            st[t].acc[dt] = (all_has[t] || has[t]) ? a : st[t].acc[dt];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const float l_new = fmaf(alpha[t], st[t].l, rs[t]);
+        st[t].l = has[t] ? l_new : st[t].l;
+        st[t].m = has[t] ? m_new[t] : st[t].m;
+    }
+}
+
 template <int D, bool MASKED>
 __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
                                    const RowVis &rv, int g, float scale_log2) {
     const float none[8] = {};
     step_core<D, false, MASKED>(
+        st, [&](int tau, int j) { return __builtin_bit_cast(bf16x8_t, r.k[tau][j]); },
+        [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, rv, g, scale_log2);
+}
+
+template <int D, bool MASKED>
+__device__ inline void step_update2(TileState<D / 16> (&st)[2], const StepRegs<D> &r, const u32x4_t (&qop)[2][D / 32],
+                                    int kc, const RowVis (&rv)[2], int g, float scale_log2) {
+    const float none[8] = {};
+    step_core2<D, false, MASKED>(
         st, [&](int tau, int j) { return __builtin_bit_cast(bf16x8_t, r.k[tau][j]); },
         [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, rv, g, scale_log2);
 }
@@ -476,6 +574,31 @@ __device__ inline void mask_tail8(StepRegs8<D> &r, int kc, int ctx, int g) {
 }
 
 template <int D, bool MASKED>
+__device__ inline void step_update8x2(TileState<D / 16> (&st)[2], const StepRegs8<D> &r,
+                                      const u32x4_t (&qop)[2][D / 32], int kc, const RowVis (&rv)[2], int g,
+                                      float scale_log2) {
+    float ksc[8], vsc[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ksc[i] = r.ks[0][i];
+        ksc[4 + i] = r.ks[1][i];
+        vsc[i] = r.vs[0][i];
+        vsc[4 + i] = r.vs[1][i];
+    }
+    step_core2<D, true, MASKED>(
+        st,
+        [&](int tau, int j) {
+            const u32x4_t w = r.k[tau][j >> 1];
+            return (j & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+        },
+        [&](int dt) {
+            const u32x4_t w = r.v[dt >> 1];
+            return (dt & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+        },
+        ksc, vsc, qop, kc, rv, g, scale_log2);
+}
+
+template <int D, bool MASKED>
 __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r, const u32x4_t (&qop)[D / 32],
                                     int kc, const RowVis &rv, int g, float scale_log2) {
     float ksc[8], vsc[8];
@@ -519,6 +642,11 @@ struct Pool<D, false> {
                                   const RowVis &rv, int g, float sl2) {
         step_update<D, MASKED>(st, r, qop, kc, rv, g, sl2);
     }
+    template <bool MASKED>
+    __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
+                                   const RowVis (&rv)[2], int g, float sl2) {
+        step_update2<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+    }
 };
 
 template <int D>
@@ -534,6 +662,11 @@ struct Pool<D, true> {
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
                                   const RowVis &rv, int g, float sl2) {
         step_update8<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+    }
+    template <bool MASKED>
+    __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
+                                   const RowVis (&rv)[2], int g, float sl2) {
+        step_update8x2<D, MASKED>(st, r, qop, kc, rv, g, sl2);
     }
 };
 
@@ -747,9 +880,17 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
             if constexpr (APPEND && !Q8)
                 if (fused && kc <= pn && pn < kc + kStep) patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
             PoolT::mask(r, kc, ctx, g);
+            if constexpr (NT == 2) {
+                if (rows_total > 16)  // uniform: both tiles in one pass over the operands
+                    PoolT::template update2<MASKED>(st, r, qop, kc, rv, g, P.scale_log2);
+                else
+                    PoolT::template update<MASKED>(st[0], r, qop[0], kc, rv[0], g, P.scale_log2);
+            } else {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                if (16 * t < rows_total) PoolT::template update<MASKED>(st[t], r, qop[t], kc, rv[t], g, P.scale_log2);
+                for (int t = 0; t < NT; ++t)
+                    if (16 * t < rows_total)
+                        PoolT::template update<MASKED>(st[t], r, qop[t], kc, rv[t], g, P.scale_log2);
+            }
         };
         // Steps wholly below every row's lowest visible key change no state:
         // the wave starts at the step holding lo_seq.
