@@ -51,10 +51,12 @@ constexpr int kParRows = 32;   // rows per (sequence, KV head) the parallel shap
 constexpr int kSeqRows = 64;   // rows per workgroup in the sequential shape
 
 // ---------------------------------------------------------------------------
-// Fixed partition of absolute key positions: 256-key splits below 2048,
-// 1024-key splits from there on; each split has four equal quarters.
+// Fixed partition of absolute key positions: 256-key splits below 1024,
+// 1024-key splits from there on; each split has four equal quarters. (Short
+// contexts get enough splits to spread over the CUs; long ones few partial
+// states to fold.)
 // ---------------------------------------------------------------------------
-constexpr int kEdge = 2048, kSplitA = 256, kSplitB = 1024;
+constexpr int kEdge = 1024, kSplitA = 256, kSplitB = 1024;
 constexpr int kSplitsA = kEdge / kSplitA;
 
 __host__ __device__ inline int split_index(int pos) {
