@@ -149,12 +149,14 @@ def copy_calibrate(nbytes, reps):
 # rocprofv3 summaries: kernel durations and HBM traffic per attention launch.
 # ---------------------------------------------------------------------------
 ATTN_SOURCE = os.path.join(ROOT, "paged_kv_attention_block_amd", "csrc", "attention.hip")
+PRODUCER_SOURCE = os.path.join(ROOT, "paged_kv_attention_block_amd", "csrc", "producer.hip")
 ATTN_KERNELS = ("attn_parallel", "attn_fold", "attn_sequential", "attn_f32")
+PRODUCER_KERNEL = "qknorm_rope_scatter_kernel"
 
 
-def source_digest():
+def source_digest(path=ATTN_SOURCE):
     import hashlib
-    with open(ATTN_SOURCE, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -169,6 +171,7 @@ def _csv_rows(d, suffix):
 
 
 def _short(name):
+    name = name.replace("(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "").replace("pkv::", "").strip()
 
 
@@ -191,7 +194,7 @@ def _counter_means(d, counter):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
-def summarize_profile(d, workload, commands):
+def summarize_profile(d, workload, commands, producer=False):
     """Write profiles/attention_<workload>.md from a directory holding the
     rocprofv3 outputs: stats/ (--kernel-trace --stats), fetch/ and write/
     (--pmc FETCH_SIZE, --pmc WRITE_SIZE over the bench), copy_fetch/ and
@@ -206,8 +209,10 @@ def summarize_profile(d, workload, commands):
     w_scale = cbytes / (cw[max(cw, key=lambda k: cw[k][0])][0] * 1024.0)
     fetch = _counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
     write = _counter_means(os.path.join(d, "write"), "WRITE_SIZE")
-    lines = [f"# Attention kernels, workload {workload}", "",
-             f"Source digest (sha256/16 of attention.hip): `{source_digest()}`", "",
+    src = PRODUCER_SOURCE if producer else ATTN_SOURCE
+    title = "Producer kernel (kv_qknorm_rope_scatter)" if producer else "Attention kernels"
+    lines = [f"# {title}, workload {workload}", "",
+             f"Source digest (sha256/16 of {os.path.basename(src)}): `{source_digest(src)}`", "",
              "Commands (repository root, rocprofv3 output under gpurun_out/):", ""]
     lines += [f"    {c}" for c in commands]
     lines += ["", "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
@@ -223,6 +228,15 @@ def summarize_profile(d, workload, commands):
               "|---|---|---|---|---|---|"]
     traffic = 0.0
     for k in sorted(set(fetch) | set(write)):
+        if producer:
+            if PRODUCER_KERNEL not in k:
+                continue
+            fk, fn = fetch.get(k, (0.0, 0))
+            wk, _ = write.get(k, (0.0, 0))
+            fb, wb = fk * 1024 * f_scale, wk * 1024 * w_scale
+            traffic += fb + wb
+            lines.append(f"| {k} | {fn} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
+            continue
         if not k.startswith(ATTN_KERNELS) and "scatter" not in k:
             continue
         fk, fn = fetch.get(k, (0.0, 0))
@@ -233,27 +247,32 @@ def summarize_profile(d, workload, commands):
         if k.startswith(ATTN_KERNELS) and not _appending(k):
             traffic += fb + wb
         lines.append(f"| {k} | {fn} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.2f} | {wb / 1e6:.2f} |")
-    lines += ["", "Traffic of one paged_attention_forward call (the bench's attention-only timing): the split",
-              "kernels without the appending path, the fold, the prefill shape.", "",
-              f"traffic_bytes_per_attention_call: {traffic:.0f}", ""]
-    out = os.path.join(ROOT, "profiles", f"attention_{workload}.md")
+    if producer:
+        lines += ["", "Traffic of one kv_qknorm_rope_scatter launch.", "",
+                  f"traffic_bytes_per_producer_call: {traffic:.0f}", ""]
+    else:
+        lines += ["", "Traffic of one paged_attention_forward call (the bench's attention-only timing): the split",
+                  "kernels without the appending path, the fold, the prefill shape.", "",
+                  f"traffic_bytes_per_attention_call: {traffic:.0f}", ""]
+    out = os.path.join(ROOT, "profiles", f"{'producer' if producer else 'attention'}_{workload}.md")
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print(out)
     return 0
 
 
-def committed_traffic(workload):
-    """HBM bytes per attention call from the committed summary, or None when
-    there is none or the kernels changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", f"attention_{workload}.md")
+def committed_traffic(workload, producer=False):
+    """HBM bytes per call from the committed summary, or None when there is
+    none or the kernels changed since it was taken."""
+    kind, src = ("producer", PRODUCER_SOURCE) if producer else ("attention", ATTN_SOURCE)
+    p = os.path.join(ROOT, "profiles", f"{kind}_{workload}.md")
     if not os.path.exists(p):
         return None
     txt = open(p).read()
-    if f"`{source_digest()}`" not in txt:
+    if f"`{source_digest(src)}`" not in txt:
         return None
     for line in txt.splitlines():
-        if line.startswith("traffic_bytes_per_attention_call:"):
+        if line.startswith(f"traffic_bytes_per_{kind}_call:"):
             return float(line.split(":")[1])
     return None
 
@@ -313,7 +332,7 @@ def producer_bench(args, torch, synth, pk):
                    "copies_per_step": copies},
         "call_us": round(us_call, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": committed_traffic(args.workload, producer=True),
                      "kernel": "qknorm_rope_scatter_kernel", "alg_bytes_per_launch": alg},
     }), flush=True)
     return 0
@@ -336,7 +355,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.summarize:
-        return summarize_profile(args.summarize, args.workload, args.commands)
+        return summarize_profile(args.summarize, args.workload, args.commands, producer=args.producer)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
