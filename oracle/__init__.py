@@ -194,7 +194,7 @@ def attention(q, k_seqs, v_seqs, qsl, num_q_heads, num_kv_heads, scale, sinks=No
     None (causal); window: sliding window in keys, 0 = none.
     Returns float64 [total_rows, Hq, D].
     """
-    kv64 = dtype == "fp8"   # K/V come as float64 dequantized values; q is bf16
+    kv64 = dtype in ("fp8", "fp4")   # K/V come as float64 dequantized values; q is bf16
     q32 = np.ascontiguousarray(to_f32(q, "bf16" if kv64 else dtype))
     D = q32.shape[-1]
     ctxs = [int(k.shape[0]) for k in k_seqs]
@@ -241,6 +241,8 @@ def paged_attention(q, k_pool, v_pool, block_tables, context_lens, qsl, num_q_he
     for s, ctx in enumerate(context_lens):
         if dtype == "fp8":
             k, v = fp8_gather(k_pool, v_pool, block_tables[s], int(ctx), dropped)
+        elif dtype == "fp4":
+            k, v = fp4_gather(k_pool, v_pool, block_tables[s], int(ctx), dropped)
         else:
             k, v = gather(k_pool, v_pool, block_tables[s], int(ctx), dropped)
         ks.append(k)
@@ -393,6 +395,161 @@ def fp8_gather(k_pool, v_pool, block_table_row, ctx, dropped_nan=False):
         sv = v_pool[b, :, 16 * D + 4 * o:16 * D + 4 * o + 4].copy().view(np.float32)[:, 0]
         k[t] = fp8_dequantize(k_pool[b][:, offk[o]], sk)
         v[t] = fp8_dequantize(v_pool[b][:, offv[o]], sv)
+    return k, v
+
+
+# ----------------------------------------------------------------------------
+# 4-bit pools: FP4 E2M1 codes with one float32 scale per (token, KV head)
+# ----------------------------------------------------------------------------
+#
+# The same page's KV block codec also has a 4-bit (and a 2-bit) setting, which
+# brings a block to a quarter of its 16-bit size; again no format is given.
+# The 4-bit reading here takes the OCP FP4 E2M1 element format (the format of
+# the MXFP4 weights the same page lists among its native quantized types): a sign bit,
+# two exponent bits with bias 1, one mantissa bit; magnitudes 0, 0.5, 1, 1.5,
+# 2, 3, 4, 6; no infinities or NaN. As for 8 bits: s = amax / 6 (float32),
+# codes = E2M1(x / s) with x / s in float32 clamped to [-6, 6], nearest code,
+# ties to the even code; zero rows have s = 0 and zero codes.
+#
+# Tile of a (block, KV head): 8 * D code bytes (two codes a byte, the even
+# nibble index in the low half), then the 16 tokens' float32 scales. Nibble
+# index of token t, channel c:
+#   K: c = 32 j + 8 g + e  at  ((g * 16 + t) * (D / 32) + j) * 8 + e
+#   V: t = 8 h + e, c = 16 dt + n  at  ((n * 2 + h) * (D / 16) + dt) * 8 + e
+
+FP4_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """float64 value of every E2M1 code (low 4 bits)."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 1).astype(np.float64)
+    normal = (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+    sub = m * 0.5
+    return sign * np.where(e == 0, sub, normal)
+
+
+_E2M1_POS = e2m1_decode(np.arange(8))   # codes 0 .. 7, ascending magnitudes
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Codes of float values |x| <= 6 by round to nearest, ties to the even
+    code (mantissa bit 0); the sign bit follows x (negative zero keeps it)."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > FP4_MAX):
+        raise ValueError("e2m1_encode needs finite |x| <= 6")
+    a = np.abs(x)
+    hi = np.searchsorted(_E2M1_POS, a, side="left").clip(0, 7)
+    lo = (hi - 1).clip(0, 7)
+    dlo = a - _E2M1_POS[lo]
+    dhi = _E2M1_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(a == _E2M1_POS[hi], hi, np.where(pick_hi, hi, lo))
+    return (code | np.where(np.signbit(x), 0x8, 0)).astype(np.uint8)
+
+
+def fp4_quantize_rows(x_bf16):
+    """Rows [..., D] of bf16 bits -> (codes uint8 [..., D] one code each, scales float32 [...])."""
+    x = to_f32(x_bf16, "bf16")
+    amax = np.max(np.abs(x), axis=-1)
+    s = (amax.astype(np.float32) / np.float32(FP4_MAX)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    r = (x / safe[..., None]).astype(np.float32)
+    r = np.clip(r, np.float32(-FP4_MAX), np.float32(FP4_MAX))
+    codes = e2m1_encode(r)
+    codes = np.where((s > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    return codes, s
+
+
+def fp4_dequantize(codes, scales) -> np.ndarray:
+    """float64 values decode(c) * s."""
+    return e2m1_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def _fp4_k_nibbles(D):
+    """Nibble index of (token t, channel c) in the code area of a K tile: [16, D]."""
+    t = np.arange(16)[:, None]
+    c = np.arange(D)[None, :]
+    j, g, e = c // 32, (c // 8) % 4, c % 8
+    return ((g * 16 + t) * (D // 32) + j) * 8 + e
+
+
+def _fp4_v_nibbles(D):
+    """Nibble index of (token t, channel c) in the code area of a V tile: [16, D]."""
+    t = np.arange(16)[:, None]
+    c = np.arange(D)[None, :]
+    dt, n = c // 16, c % 16
+    h, e = t // 8, t % 8
+    return ((n * 2 + h) * (D // 16) + dt) * 8 + e
+
+
+def fp4_empty_pools(num_blocks, num_kv_heads, head_dim, fill=None):
+    if head_dim % 64:
+        raise ValueError("4-bit pools need head_dim a multiple of 64")
+    tile = 8 * head_dim + 64
+    kp = np.zeros((num_blocks, num_kv_heads, tile), dtype=np.uint8)
+    vp = np.zeros((num_blocks, num_kv_heads, tile), dtype=np.uint8)
+    if fill is not None:
+        kp[...] = fill
+        vp[...] = fill
+    return kp, vp
+
+
+def _put_nibbles(tile, nibbles, codes):
+    for nb, cd in zip(np.asarray(nibbles).reshape(-1), np.asarray(codes).reshape(-1)):
+        b, hi = int(nb) // 2, int(nb) % 2
+        tile[b] = (tile[b] & 0x0F) | (int(cd) << 4) if hi else (tile[b] & 0xF0) | int(cd)
+
+
+def _get_nibbles(tile, nibbles):
+    n = np.asarray(nibbles)
+    by = tile[n // 2].astype(np.int64)
+    return np.where(n % 2 == 1, by >> 4, by & 0xF)
+
+
+def fp4_scatter(k_pool, v_pool, k_new_bf16, v_new_bf16, slots):
+    """Quantize new tokens ([n, Hkv, D] bf16 bits) and write codes and scales
+    at their slots (-1 = skip)."""
+    nb, hkv, tile = k_pool.shape
+    D = (tile - 64) // 8
+    nk, nv = _fp4_k_nibbles(D), _fp4_v_nibbles(D)
+    kc, ks = fp4_quantize_rows(k_new_bf16)
+    vc, vs = fp4_quantize_rows(v_new_bf16)
+    for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
+        if slot < 0:
+            continue
+        b, o = int(slot // 16), int(slot % 16)
+        for h in range(hkv):
+            _put_nibbles(k_pool[b, h], nk[o], kc[i, h])
+            _put_nibbles(v_pool[b, h], nv[o], vc[i, h])
+            k_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4] = np.frombuffer(ks[i, h].tobytes(), np.uint8)
+            v_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4] = np.frombuffer(vs[i, h].tobytes(), np.uint8)
+
+
+def fp4_gather(k_pool, v_pool, block_table_row, ctx, dropped_nan=False):
+    """Dequantized float64 K, V [ctx, Hkv, D] of one sequence (dropped_nan as
+    for gather)."""
+    nb, hkv, tile = k_pool.shape
+    D = (tile - 64) // 8
+    nk, nv = _fp4_k_nibbles(D), _fp4_v_nibbles(D)
+    bt = np.asarray(block_table_row, dtype=np.int64)
+    k = np.zeros((ctx, hkv, D))
+    v = np.zeros((ctx, hkv, D))
+    for t in range(ctx):
+        b, o = int(bt[t // 16]), t % 16
+        if b < 0 and dropped_nan:
+            k[t] = np.nan
+            v[t] = np.nan
+            continue
+        if b < 0 or b >= nb:
+            raise ValueError("block table points outside the pool")
+        for h in range(hkv):
+            sk = k_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4].copy().view(np.float32)[0]
+            sv = v_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4].copy().view(np.float32)[0]
+            k[t, h] = e2m1_decode(_get_nibbles(k_pool[b, h], nk[o])) * np.float64(sk)
+            v[t, h] = e2m1_decode(_get_nibbles(v_pool[b, h], nv[o])) * np.float64(sv)
     return k, v
 
 
