@@ -56,6 +56,22 @@
  *   V: t = 8 h + e, c = 16 (2 d + dd) + n  at byte (((d * 16 + n) * 2 + h) * 2 + dd) * 8 + e
  * (head_dim a multiple of 64). Queries and the new K/V rows handed to
  * kv_append_scatter are bf16.
+ *
+ * 4-bit pools (KV_FP4; the same section's KV block codec has a 4-bit setting,
+ * again with no format): each (token, KV head) row is stored as OCP FP4 E2M1
+ * codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) with one
+ * float32 scale s = max|x| / 6, the codes being x / s clamped to [-6, 6] and
+ * rounded to the nearest code, ties to the even code (both divisions float32);
+ * a row of zeros stores s = 0 and zero codes. The value used is c * s. A
+ * (block, KV head) tile is 8 * head_dim code bytes, two codes a byte (the
+ * even code index in the low nibble), then the 16 tokens' float32 scales;
+ *   K_pool, V_pool [num_blocks][num_kv_heads][8 * head_dim + 64] bytes,
+ * code index (nibble) of token t, channel c:
+ *   K: c = 32 j + 8 g + e  at  ((g * 16 + t) * (head_dim / 32) + j) * 8 + e
+ *   V: t = 8 h + e, c = 16 dt + n  at  ((n * 2 + h) * (head_dim / 16) + dt) * 8 + e
+ * Two tokens share each V byte: writes of single tokens into a block update
+ * their V nibbles atomically, so tokens of one block may be written by one
+ * call or by calls on different streams.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -76,7 +92,7 @@ enum kv_status {
     KV_EINTERNAL = -5      /* unexpected internal failure */
 };
 
-enum kv_dtype { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+enum kv_dtype { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
 
 #define PAGEDKV_ABI_VERSION 1
 
@@ -257,14 +273,15 @@ int kv_accept_paths(const int32_t *parents, const int32_t *draft_tokens, const i
  *   V_pool[slot / 16][h][d][slot % 16]            = v_new[i][h][d]
  * for all h < num_kv_heads, d < head_dim: a bit copy. Slots of -1 are skipped;
  * slots outside the pool are skipped. Slots must be distinct within a call.
- * With dtype KV_FP8, k_new and v_new are bf16 and each (token, head) row is
- * quantized as described under "8-bit pools" and written with its scale.
+ * With dtype KV_FP8 or KV_FP4, k_new and v_new are bf16 and each (token,
+ * head) row is quantized as described under "8-bit pools" or "4-bit pools"
+ * and written with its scale.
  *   k_new, v_new  device [n][num_kv_heads][head_dim], element type `dtype`
- *                 (bf16 for KV_FP8)
+ *                 (bf16 for KV_FP8 and KV_FP4)
  *   slot_mapping  device int32 [n]
  *   k_pool, v_pool device pools in the layout above, num_blocks blocks
  * Supported: dtype KV_BF16 or KV_F32 with head_dim a multiple of 16 up to 256;
- * KV_FP8 with head_dim 64 or 128; block_size 16.
+ * KV_FP8 and KV_FP4 with head_dim 64 or 128; block_size 16.
  * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
  */
 int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_mapping,
@@ -339,9 +356,9 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
  * its visible keys and values, scale and sink: the same row gives the same bits
  * alone, in any batch, and inside any window (a verify window row equals the
  * same query run as a single decode row over the keys up to it).
- * Supported: head_dim 64 or 128, block_size 16, dtype KV_BF16, KV_F32 or
- * KV_FP8 (q in bf16, pools of 8-bit tiles: the keys and values are the
- * stored codes times their scales).
+ * Supported: head_dim 64 or 128, block_size 16, dtype KV_BF16, KV_F32,
+ * KV_FP8 or KV_FP4 (q in bf16, pools of 8- or 4-bit tiles: the keys and
+ * values are the stored codes times their scales).
  * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
  */
 int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
@@ -364,9 +381,10 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
  * slot_mapping, total_q_rows, ...) followed by paged_attention_forward(...) on
  * the same stream, bit for bit in `out` and in the pools. Other arguments,
  * ownership and errors are those of paged_attention_forward; k_pool and v_pool
- * are written. A bf16 batch of single-row sequences (decode) writes and uses
- * the new tokens inside the attention launch; any other batch, and every
- * KV_FP8 batch (k_new, v_new in bf16), is scattered first.
+ * are written. A bf16 batch of single-row sequences (decode) with at most 16
+ * query heads per KV head writes and uses the new tokens inside the attention
+ * launch; any other batch, and every
+ * KV_FP8 or KV_FP4 batch (k_new, v_new in bf16), is scattered first.
  */
 int paged_attention_append_forward(const void *q, const void *k_new, const void *v_new,
                                    const int32_t *slot_mapping, void *k_pool, void *v_pool, int32_t dtype,

@@ -497,35 +497,54 @@ def fp4_empty_pools(num_blocks, num_kv_heads, head_dim, fill=None):
     return kp, vp
 
 
-def _put_nibbles(tile, nibbles, codes):
-    for nb, cd in zip(np.asarray(nibbles).reshape(-1), np.asarray(codes).reshape(-1)):
-        b, hi = int(nb) // 2, int(nb) % 2
-        tile[b] = (tile[b] & 0x0F) | (int(cd) << 4) if hi else (tile[b] & 0xF0) | int(cd)
+def _fp4_put(pool, blocks, offs, nibbles, codes, scales):
+    """Write tokens' codes ([m, Hkv, D], nibble index nibbles [m, D] within
+    the tile) and scales ([m, Hkv]) into tiles pool[blocks[i], h] at token
+    offsets offs[i]. Each nibble is cleared, then set (ufunc.at applies every
+    index, repeated bytes included, so two tokens sharing a byte both land)."""
+    m, hkv, D = codes.shape
+    shape = (m, hkv, D)
+    bi = np.broadcast_to(blocks[:, None, None], shape)
+    hi = np.broadcast_to(np.arange(hkv)[None, :, None], shape)
+    by = np.broadcast_to((nibbles // 2)[:, None, :], shape)
+    sh = np.broadcast_to((4 * (nibbles % 2))[:, None, :], shape).astype(np.uint8)
+    np.bitwise_and.at(pool, (bi, hi, by), (~(np.uint8(0xF) << sh)).astype(np.uint8))
+    np.bitwise_or.at(pool, (bi, hi, by), (codes.astype(np.uint8) << sh).astype(np.uint8))
+    sb = np.ascontiguousarray(scales.astype(np.float32)).view(np.uint8).reshape(m, hkv, 4)
+    col = (8 * D + 4 * offs)[:, None, None] + np.arange(4)[None, None, :]
+    pool[blocks[:, None, None], np.arange(hkv)[None, :, None], col] = sb
 
 
-def _get_nibbles(tile, nibbles):
-    n = np.asarray(nibbles)
-    by = tile[n // 2].astype(np.int64)
-    return np.where(n % 2 == 1, by >> 4, by & 0xF)
-
-
-def fp4_scatter(k_pool, v_pool, k_new_bf16, v_new_bf16, slots):
+def fp4_scatter(k_pool, v_pool, k_new_bf16, v_new_bf16, slots, chunk=2048):
     """Quantize new tokens ([n, Hkv, D] bf16 bits) and write codes and scales
     at their slots (-1 = skip)."""
     nb, hkv, tile = k_pool.shape
     D = (tile - 64) // 8
     nk, nv = _fp4_k_nibbles(D), _fp4_v_nibbles(D)
-    kc, ks = fp4_quantize_rows(k_new_bf16)
-    vc, vs = fp4_quantize_rows(v_new_bf16)
-    for i, slot in enumerate(np.asarray(slots, dtype=np.int64)):
-        if slot < 0:
+    slots = np.asarray(slots, dtype=np.int64)
+    for a in range(0, slots.size, chunk):
+        sl = slots[a:a + chunk]
+        keep = sl >= 0
+        if not keep.any():
             continue
-        b, o = int(slot // 16), int(slot % 16)
-        for h in range(hkv):
-            _put_nibbles(k_pool[b, h], nk[o], kc[i, h])
-            _put_nibbles(v_pool[b, h], nv[o], vc[i, h])
-            k_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4] = np.frombuffer(ks[i, h].tobytes(), np.uint8)
-            v_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4] = np.frombuffer(vs[i, h].tobytes(), np.uint8)
+        kc, ks = fp4_quantize_rows(np.asarray(k_new_bf16[a:a + chunk])[keep])
+        vc, vs = fp4_quantize_rows(np.asarray(v_new_bf16[a:a + chunk])[keep])
+        b, o = sl[keep] // 16, sl[keep] % 16
+        _fp4_put(k_pool, b, o, nk[o], kc, ks)
+        _fp4_put(v_pool, b, o, nv[o], vc, vs)
+
+
+def _fp4_take(pool, blocks, offs, nibbles):
+    """Codes [m, Hkv, D] and scales [m, Hkv] (float32) of tokens at offsets
+    offs of tiles pool[blocks[i], h]."""
+    m = blocks.size
+    hkv, D = pool.shape[1], nibbles.shape[1]
+    h = np.arange(hkv)[None, :, None]
+    by = pool[blocks[:, None, None], h, (nibbles // 2)[:, None, :]].astype(np.int64)
+    codes = np.where((nibbles % 2)[:, None, :] == 1, by >> 4, by & 0xF)
+    col = (8 * D + 4 * offs)[:, None, None] + np.arange(4)[None, None, :]
+    sc = np.ascontiguousarray(pool[blocks[:, None, None], h, col]).view(np.float32).reshape(m, hkv)
+    return codes, sc
 
 
 def fp4_gather(k_pool, v_pool, block_table_row, ctx, dropped_nan=False):
@@ -535,21 +554,16 @@ def fp4_gather(k_pool, v_pool, block_table_row, ctx, dropped_nan=False):
     D = (tile - 64) // 8
     nk, nv = _fp4_k_nibbles(D), _fp4_v_nibbles(D)
     bt = np.asarray(block_table_row, dtype=np.int64)
-    k = np.zeros((ctx, hkv, D))
-    v = np.zeros((ctx, hkv, D))
-    for t in range(ctx):
-        b, o = int(bt[t // 16]), t % 16
-        if b < 0 and dropped_nan:
-            k[t] = np.nan
-            v[t] = np.nan
-            continue
-        if b < 0 or b >= nb:
-            raise ValueError("block table points outside the pool")
-        for h in range(hkv):
-            sk = k_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4].copy().view(np.float32)[0]
-            sv = v_pool[b, h, 8 * D + 4 * o:8 * D + 4 * o + 4].copy().view(np.float32)[0]
-            k[t, h] = e2m1_decode(_get_nibbles(k_pool[b, h], nk[o])) * np.float64(sk)
-            v[t, h] = e2m1_decode(_get_nibbles(v_pool[b, h], nv[o])) * np.float64(sv)
+    t = np.arange(ctx)
+    b, o = bt[t // 16], t % 16
+    gone = b < 0
+    if (gone.any() and not dropped_nan) or np.any(b >= nb):
+        raise ValueError("block table points outside the pool")
+    b = np.where(gone, 0, b)
+    k = fp4_dequantize(*_fp4_take(k_pool, b, o, nk[o]))
+    v = fp4_dequantize(*_fp4_take(v_pool, b, o, nv[o]))
+    k[gone] = np.nan
+    v[gone] = np.nan
     return k, v
 
 

@@ -10,8 +10,10 @@ fallback path.
 Pool layout (see the header): with X = 16 bytes / element size,
 ``K_pool [num_blocks, Hkv, D // X, 16, X]`` and ``V_pool [num_blocks, Hkv, D, 16]``
 for float32 and bf16 pools; 8-bit pools (E4M3 codes with a float32 scale per
-token and KV head) are ``torch.uint8 [num_blocks, Hkv, 16 * D + 64]`` each,
-with bf16 queries and bf16 new K/V rows.
+token and KV head) are ``torch.uint8 [num_blocks, Hkv, 16 * D + 64]`` each and
+4-bit pools (E2M1 codes, two a byte, with the same scales) ``torch.uint8
+[num_blocks, Hkv, 8 * D + 64]``, both with bf16 queries and bf16 new K/V rows;
+the head size the rows carry tells the two apart.
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import numpy as np
 
 __all__ = [
     "KV_OK", "KV_EINVAL", "KV_ENOMEM", "KV_EUNSUPPORTED", "KV_EDEVICE", "KV_EINTERNAL",
-    "KV_F32", "KV_BF16", "KV_FP8", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
+    "KV_F32", "KV_BF16", "KV_FP8", "KV_FP4", "KVError", "lib_path", "kv_abi_version", "kv_last_error",
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
     "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks", "kv_append_scatter",
     "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter", "paged_attention_workspace_size", "paged_attention_forward",
@@ -30,7 +32,7 @@ __all__ = [
 ]
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
-KV_F32, KV_BF16, KV_FP8 = 0, 1, 2
+KV_F32, KV_BF16, KV_FP8, KV_FP4 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -219,10 +221,14 @@ def _need(t, name, dtype=None, ndim=None):
 
 def empty_pools(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda"):
     """Allocate (K_pool, V_pool) device tensors in the library's layout;
-    dtype torch.uint8 gives 8-bit pools."""
+    dtype torch.uint8 or "fp8" gives 8-bit pools, "fp4" 4-bit pools."""
     torch = _torch()
-    if dtype == torch.uint8:
-        tile = 16 * head_dim + 64
+    if isinstance(dtype, str) or dtype == torch.uint8:
+        fmt = "fp8" if dtype == torch.uint8 else dtype
+        if fmt not in ("fp8", "fp4"):
+            raise KVError(KV_EUNSUPPORTED, f"unknown pool format {dtype!r}")
+        tile = (16 if fmt == "fp8" else 8) * head_dim + 64
+        dtype = torch.uint8
         return (torch.empty((num_blocks, num_kv_heads, tile), dtype=dtype, device=device),
                 torch.empty((num_blocks, num_kv_heads, tile), dtype=dtype, device=device))
     X = 16 // torch.empty((), dtype=dtype).element_size()
@@ -237,14 +243,16 @@ def _pools(k_pool, v_pool, elem_dtype, hkv, d):
     torch = _torch()
     if k_pool.dtype == torch.uint8:
         if elem_dtype != torch.bfloat16:
-            raise KVError(KV_EINVAL, "8-bit pools take bf16 queries and bf16 new K/V rows")
+            raise KVError(KV_EINVAL, "8- and 4-bit pools take bf16 queries and bf16 new K/V rows")
         _need(k_pool, "k_pool", dtype=torch.uint8, ndim=3)
         _need(v_pool, "v_pool", dtype=torch.uint8, ndim=3)
         nb = k_pool.shape[0]
-        want = (nb, hkv if hkv is not None else k_pool.shape[1], 16 * d + 64)
-        if tuple(k_pool.shape) != want or tuple(v_pool.shape) != want:
-            raise KVError(KV_EINVAL, f"8-bit pools must be [num_blocks, Hkv, {16 * d + 64}]")
-        return KV_FP8, nb
+        h = hkv if hkv is not None else k_pool.shape[1]
+        for code, tile in ((KV_FP8, 16 * d + 64), (KV_FP4, 8 * d + 64)):
+            if tuple(k_pool.shape) == (nb, h, tile) and tuple(v_pool.shape) == (nb, h, tile):
+                return code, nb
+        raise KVError(KV_EINVAL, f"8-bit pools must be [num_blocks, Hkv, {16 * d + 64}], "
+                                 f"4-bit pools [num_blocks, Hkv, {8 * d + 64}]")
     _need(k_pool, "k_pool", dtype=elem_dtype, ndim=5)
     _need(v_pool, "v_pool", dtype=elem_dtype, ndim=4)
     nb = k_pool.shape[0]
@@ -257,7 +265,7 @@ def _pools(k_pool, v_pool, elem_dtype, hkv, d):
 
 def kv_append_scatter(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None) -> None:
     """Scatter-write k_new/v_new [n, Hkv, D] into the pools at slot_mapping [n] (int32, -1 = skip);
-    8-bit pools quantize each (token, KV head) row."""
+    8- and 4-bit pools quantize each (token, KV head) row."""
     torch = _torch()
     _need(k_new, "k_new", ndim=3)
     _need(v_new, "v_new", dtype=k_new.dtype, ndim=3)
@@ -279,6 +287,8 @@ def kv_copy_blocks(k_pool, v_pool, src, dst, stream=None) -> None:
     if src.shape != dst.shape:
         raise KVError(KV_EINVAL, "src and dst sizes disagree")
     if k_pool.dtype == torch.uint8:
+        # a copy moves whole tiles: an 8-bit tile of (tile - 64) / 16 channels
+        # has the byte size of either format's tile
         hkv, d = k_pool.shape[1], (k_pool.shape[2] - 64) // 16
         elem = torch.bfloat16
     else:

@@ -50,6 +50,9 @@ constexpr int kMaxHeadDim = 128;
 constexpr int kParRows = 32;   // rows per (sequence, KV head) the parallel shape takes
 constexpr int kSeqRows = 64;   // rows per workgroup in the sequential shape
 
+// Tile formats of the MFMA paths: bf16 values, 8-bit codes, 4-bit codes.
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2;
+
 // ---------------------------------------------------------------------------
 // Fixed partition of absolute key positions: 256-key splits below 1024,
 // 1024-key splits from there on; each split has four equal quarters. (Short
@@ -624,13 +627,13 @@ __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r
         ksc, vsc, qop, kc, rv, g, scale_log2);
 }
 
-// Pool access of the parallel and sequential shapes for bf16 (Q8 = false)
-// and 8-bit (Q8 = true) tiles; pointers are byte addresses of tiles.
-template <int D, bool Q8>
+// Pool access of the parallel and sequential shapes for each tile format
+// (kKvBf16, kKvFp8, kKvFp4); pointers are byte addresses of tiles.
+template <int D, int KF>
 struct Pool;
 
 template <int D>
-struct Pool<D, false> {
+struct Pool<D, kKvBf16> {
     using Regs = StepRegs<D>;
     static constexpr size_t tile_bytes = (size_t)kBlock * D * 2;
     __device__ static void load(Regs &r, const uint8_t *k0, const uint8_t *v0, const uint8_t *k1, const uint8_t *v1,
@@ -652,7 +655,7 @@ struct Pool<D, false> {
 };
 
 template <int D>
-struct Pool<D, true> {
+struct Pool<D, kKvFp8> {
     using Regs = StepRegs8<D>;
     static constexpr size_t tile_bytes = (size_t)q8_tile_bytes<D>();
     __device__ static void load(Regs &r, const uint8_t *k0, const uint8_t *v0, const uint8_t *k1, const uint8_t *v1,
@@ -669,6 +672,156 @@ struct Pool<D, true> {
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
                                    const RowVis (&rv)[2], int g, float sl2) {
         step_update8x2<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// 4-bit pools: FP4 E2M1 codes (OCP) with one float32 scale per (token, KV
+// head); the stored value is code * scale. Tile of a (block, KV head): 8 * D
+// code bytes, two codes a byte (the first in the low nibble), then the 16
+// tokens' scales. Code (nibble) index of token t, channel c:
+//   K: c = 32 j + 8 g + e  at  ((g*16 + t) * (D/32) + j) * 8 + e
+//   V: t = 8 h + e, c = 16 dt + n  at  ((n*2 + h) * (D/16) + dt) * 8 + e
+// so that a lane's K operands for a key are one run of D/8 bytes (a dword
+// per MFMA k-step) and its V^T operands one run of D/4 bytes (a dword per
+// d-tile). Two keys share each V byte, which is why a token written alone
+// takes atomic nibble updates (scatter4_kernel).
+// ---------------------------------------------------------------------------
+template <int D>
+constexpr int q4_tile_bytes() { return 8 * D + 64; }
+
+template <int D>
+struct StepRegs4 {
+    uint32_t k[2][D / 32];  // tile tau: dword j = channels 32j+8g..+7 of the lane's key
+    uint32_t v[D / 16];     // dword dt = channel 16dt+n at the lane's eight keys
+    f32x4_t ks[2], vs[2];   // scales of the lane's keys 0-3 and 4-7
+};
+
+// eight codes (one dword, low nibble first) -> eight bf16 values, exact
+__device__ inline bf16x8_t fp4x8_to_bf16(uint32_t w) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ inline void load_dw2(uint32_t *d, const uint8_t *src) {
+    const u32x2_t w = *reinterpret_cast<const u32x2_t *>(src);
+    d[0] = w.x;
+    d[1] = w.y;
+}
+__device__ inline void load_dw4(uint32_t *d, const uint8_t *src) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t *>(src);
+    d[0] = w.x;
+    d[1] = w.y;
+    d[2] = w.z;
+    d[3] = w.w;
+}
+
+// Staged copies in LDS (attn_sequential) permute 16-byte pieces so that each
+// group of 8 lanes reads 128 distinct bytes: at D = 128 a K piece is one
+// token's run, kept in lds_k_pos order; a V piece q of channel row m's run
+// of half h (piece 4m + 2h + q at D = 128, 2m + h at D = 64) swaps with its
+// neighbours by bits of m.
+template <int D>
+__device__ inline int lds_v4_piece(int pc) {
+    if constexpr (D == 128) return (pc & ~3) | ((pc & 3) ^ ((pc >> 3) & 3));
+    else return (pc & ~1) | ((pc & 1) ^ ((pc >> 3) & 1));
+}
+
+// Operands of one chunk from 4-bit tiles kt0/vt0 and kt1/vt1 (blocks 0, 1),
+// in the pools (LDS = false) or staged in LDS.
+template <int D, bool LDS>
+__device__ inline void load_step4(StepRegs4<D> &r, const uint8_t *kt0, const uint8_t *vt0, const uint8_t *kt1,
+                                  const uint8_t *vt1, int g, int n) {
+    constexpr int KB = D / 8, VB = D / 4;  // bytes of a K run, of a V run
+    const uint8_t *k = n >= 8 ? kt1 : kt0;
+    const int tk = 8 * ((n >> 2) & 1) + (n & 3);
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+        const int t = tk + 4 * tau;
+        if constexpr (D == 128) load_dw4(r.k[tau], k + (g * kBlock + (LDS ? lds_k_pos(t) : t)) * KB);
+        else load_dw2(r.k[tau], k + (g * kBlock + t) * KB);
+    }
+    const uint8_t *v = (g >> 1) ? vt1 : vt0;
+    const int h = g & 1;
+#pragma unroll
+    for (int q = 0; q < VB / 16; ++q) {
+        const int pc = (2 * n + h) * (VB / 16) + q;
+        load_dw4(r.v + 4 * q, v + (LDS ? lds_v4_piece<D>(pc) : pc) * 16);
+    }
+    const uint8_t *kss = ((g >> 1) ? kt1 : kt0) + 8 * D + 32 * h;
+    const uint8_t *vss = v + 8 * D + 32 * h;
+    r.ks[0] = *reinterpret_cast<const f32x4_t *>(kss);
+    r.ks[1] = *reinterpret_cast<const f32x4_t *>(kss + 16);
+    r.vs[0] = *reinterpret_cast<const f32x4_t *>(vss);
+    r.vs[1] = *reinterpret_cast<const f32x4_t *>(vss + 16);
+}
+
+// Zero the V scales of keys at or past ctx, so that a zero weight never meets
+// a NaN (codes are always finite; the scores of those keys are masked by select).
+template <int D>
+__device__ inline void mask_tail4(StepRegs4<D> &r, int kc, int ctx, int g) {
+    if (kc + kStep <= ctx) return;
+    const int nv = ctx - (kc + key_off(g));  // the lane's keys 0 .. nv-1 exist
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r.vs[0][i] = i < nv ? r.vs[0][i] : 0.f;
+        r.vs[1][i] = i + 4 < nv ? r.vs[1][i] : 0.f;
+    }
+}
+
+template <int D>
+__device__ inline void scales4(const StepRegs4<D> &r, float (&ksc)[8], float (&vsc)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ksc[i] = r.ks[0][i];
+        ksc[4 + i] = r.ks[1][i];
+        vsc[i] = r.vs[0][i];
+        vsc[4 + i] = r.vs[1][i];
+    }
+}
+
+template <int D, bool MASKED>
+__device__ inline void step_update4(TileState<D / 16> &st, const StepRegs4<D> &r, const u32x4_t (&qop)[D / 32],
+                                    int kc, const RowVis &rv, int g, float scale_log2) {
+    float ksc[8], vsc[8];
+    scales4<D>(r, ksc, vsc);
+    step_core<D, true, MASKED>(
+        st, [&](int tau, int j) { return fp4x8_to_bf16(r.k[tau][j]); }, [&](int dt) { return fp4x8_to_bf16(r.v[dt]); },
+        ksc, vsc, qop, kc, rv, g, scale_log2);
+}
+
+template <int D, bool MASKED>
+__device__ inline void step_update4x2(TileState<D / 16> (&st)[2], const StepRegs4<D> &r,
+                                      const u32x4_t (&qop)[2][D / 32], int kc, const RowVis (&rv)[2], int g,
+                                      float scale_log2) {
+    float ksc[8], vsc[8];
+    scales4<D>(r, ksc, vsc);
+    step_core2<D, true, MASKED>(
+        st, [&](int tau, int j) { return fp4x8_to_bf16(r.k[tau][j]); }, [&](int dt) { return fp4x8_to_bf16(r.v[dt]); },
+        ksc, vsc, qop, kc, rv, g, scale_log2);
+}
+
+template <int D>
+struct Pool<D, kKvFp4> {
+    using Regs = StepRegs4<D>;
+    static constexpr size_t tile_bytes = (size_t)q4_tile_bytes<D>();
+    __device__ static void load(Regs &r, const uint8_t *k0, const uint8_t *v0, const uint8_t *k1, const uint8_t *v1,
+                                int g, int n) {
+        load_step4<D, false>(r, k0, v0, k1, v1, g, n);
+    }
+    __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail4<D>(r, kc, ctx, g); }
+    template <bool MASKED>
+    __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
+                                  const RowVis &rv, int g, float sl2) {
+        step_update4<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+    }
+    template <bool MASKED>
+    __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
+                                   const RowVis (&rv)[2], int g, float sl2) {
+        step_update4x2<D, MASKED>(st, r, qop, kc, rv, g, sl2);
     }
 };
 
@@ -766,9 +919,9 @@ struct ParLds {
     float2 ml[3][NT][64];
 };
 
-template <int D, int NT, bool PF, bool APPEND, bool Q8, bool MASKED>
+template <int D, int NT, bool PF, bool APPEND, int KF, bool MASKED>
 __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnParams P) {
-    using PoolT = Pool<D, Q8>;
+    using PoolT = Pool<D, KF>;
     using Regs = typename PoolT::Regs;
     constexpr int DT = D / 16, KJ = D / 32;
     const int tid = threadIdx.x;
@@ -841,10 +994,10 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                   : -1;
         // appending decode step: the wave whose quarter holds the new key
         const int pn = ctx - 1;
-        const bool fused = APPEND && !Q8 && kq0 <= pn && pn < kq1;
+        const bool fused = APPEND && KF == kKvBf16 && kq0 <= pn && pn < kq1;
         u32x4_t knew[KJ];
         uint32_t vnew[DT];
-        if (APPEND && !Q8 && fused) {
+        if (APPEND && KF == kKvBf16 && fused) {
             const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
 #pragma unroll
             for (int jj = 0; jj < KJ; ++jj)
@@ -879,7 +1032,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                         g, n);
         };
         auto compute = [&](Regs &r, int kc) {
-            if constexpr (APPEND && !Q8)
+            if constexpr (APPEND && KF == kKvBf16)
                 if (fused && kc <= pn && pn < kc + kStep) patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
             PoolT::mask(r, kc, ctx, g);
             if constexpr (NT == 2) {
@@ -1065,9 +1218,9 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
 // Two workgroups per CU (the LDS staging allows no more): bounding the
 // registers to that occupancy keeps the MFMA accumulators in VGPRs, where the
 // per-step rescale and select use them without copies.
-template <int D, bool Q8, bool MASKED>
+template <int D, int KF, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
-    using PoolT = Pool<D, Q8>;
+    using PoolT = Pool<D, KF>;
     using Regs = typename PoolT::Regs;
     constexpr int DT = D / 16, KJ = D / 32;
     constexpr int TB = (int)PoolT::tile_bytes;  // bytes of one (block, head) tile
@@ -1115,15 +1268,18 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     // step's blocks 0, 1; parts 2, 3 their V. Lane l stages pieces l + 64 v.
     const int blk = wave & 1;
     const bool is_v = wave >= 2;
-    // LDS position of piece pc of the wave's part (see load_step_lds and
-    // load_step8: K token order 0-3, 8-11, 4-7, 12-15; V halves swapped on
-    // rows with bit 2 set; 8-bit tiles keep their scales in place)
+    // LDS position of piece pc of the wave's part (see load_step_lds,
+    // load_step8 and load_step4: K token order 0-3, 8-11, 4-7, 12-15; V
+    // pieces of a channel row permuted by the row's bits; scales in place)
     auto lds_pos = [&](int pc) {
-        if constexpr (Q8) {
-            if (pc >= D) return pc;                                   // scales
-            return is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
-                        : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
+        if constexpr (KF == kKvFp4) {
+            if (pc >= D / 2) return pc;  // scales
+            if constexpr (D == 128)
+                return is_v ? lds_v4_piece<D>(pc) : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
+            else
+                return is_v ? lds_v4_piece<D>(pc) : pc;
         } else {
+            if (KF == kKvFp8 && pc >= D) return pc;  // scales
             return is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
                         : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
         }
@@ -1175,9 +1331,11 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
         __syncthreads();
         if (kc <= wave_pmax && (!MASKED || kc + kStep > wave_lo)) {
             Regs r;
-            if constexpr (Q8)
+            if constexpr (KF == kKvFp8)
                 load_step8<D>(r, buf, buf + 2 * TB, buf + TB, buf + 3 * TB, g, n, [](int t) { return lds_k_pos(t); },
                               [](int row, int h) { return lds_v_half(row, h); });
+            else if constexpr (KF == kKvFp4)
+                load_step4<D, true>(r, buf, buf + 2 * TB, buf + TB, buf + 3 * TB, g, n);
             else
                 load_step_lds<D>(r, reinterpret_cast<const uint16_t *>(buf), reinterpret_cast<const uint16_t *>(buf + 2 * TB),
                                  reinterpret_cast<const uint16_t *>(buf + TB),
@@ -1569,6 +1727,142 @@ __global__ __launch_bounds__(256) void scatter8_kernel(const uint16_t *__restric
 }
 
 // ---------------------------------------------------------------------------
+// Scatter-write into 4-bit pools: the grid of scatter8_kernel. Each (token,
+// head) row is quantized: s = amax / 6, codes = E2M1 of x / s clamped to
+// [-6, 6], rounded to nearest with ties to the even code by the conversion
+// instruction (both divisions IEEE float32); a zero row stores s = 0 and zero
+// codes. A whole block written in order goes out as 16-byte pieces built in
+// LDS. A token written alone owns its K run and its scales, but shares each
+// V byte with the neighbouring key, which another workgroup may be writing
+// at the same time: its V codes go in by atomic nibble updates (clear, then
+// set), which commute with the neighbour's.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restrict__ kn, const uint16_t *__restrict__ vn,
+                                                      const int32_t *__restrict__ slots, int n, uint8_t *kp,
+                                                      uint8_t *vp, int num_blocks, int Hkv) {
+    constexpr int TB = q4_tile_bytes<D>();
+    constexpr int CPT = D / 16;  // channels per lane
+    constexpr int KJ = D / 32, DT = D / 16;
+    const int tid = threadIdx.x;
+    const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
+    __shared__ int s_slot[kBlock];
+    __shared__ int s_full;
+    __shared__ __attribute__((aligned(16))) uint8_t kc[kBlock][D], vc[kBlock][D];  // one code a byte
+    __shared__ float ksc[kBlock], vsc[kBlock];
+    if (tid < kBlock) {
+        const int i = i0 + tid;
+        const int sl = i < n ? slots[i] : -1;
+        s_slot[tid] = (sl >= 0 && sl < num_blocks * kBlock) ? sl : -1;
+    }
+    const int t = tid >> 4, part = tid & 15;  // token of the group, channel group
+    const int i = i0 + t;
+    const bool have = i < n;
+    float xk[CPT], xv[CPT];
+    {
+        const uint16_t *rk = kn + ((size_t)i * Hkv + h) * D + part * CPT;
+        const uint16_t *rv = vn + ((size_t)i * Hkv + h) * D + part * CPT;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            xk[c] = have ? __builtin_bit_cast(float, (uint32_t)rk[c] << 16) : 0.f;
+            xv[c] = have ? __builtin_bit_cast(float, (uint32_t)rv[c] << 16) : 0.f;
+        }
+    }
+    auto quantize = [&](float (&x)[CPT], uint8_t *codes_row, float *scale_slot) {
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) amax = fmaxf(amax, fabsf(x[c]));
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float sc = __fdiv_rn(amax, 6.f);
+        const float safe = sc > 0.f ? sc : 1.f;
+#pragma unroll
+        for (int c = 0; c < CPT; c += 2) {
+            const float r0 = fminf(fmaxf(__fdiv_rn(x[c], safe), -6.f), 6.f);
+            const float r1 = fminf(fmaxf(__fdiv_rn(x[c + 1], safe), -6.f), 6.f);
+            const uint32_t w = sc > 0.f ? __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, r0, r1, 1.0f, 0) : 0u;
+            codes_row[part * CPT + c] = (uint8_t)(w & 0xF);
+            codes_row[part * CPT + c + 1] = (uint8_t)((w >> 4) & 0xF);
+        }
+        if (part == 0) *scale_slot = sc;
+    };
+    quantize(xk, kc[t], &ksc[t]);
+    quantize(xv, vc[t], &vsc[t]);
+    __syncthreads();
+    if (tid < 64) {
+        const int sl0 = s_slot[0];
+        const bool ok = tid >= kBlock || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlock == 0);
+        const bool full = __all(ok);
+        if (tid == 0) s_full = full;
+    }
+    __syncthreads();
+    // eight codes into a dword, the first in the low nibble
+    auto pack8 = [](const uint8_t (&c)[8]) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= (uint32_t)c[e] << (4 * e);
+        return w;
+    };
+    if (s_full) {
+        const int blk = s_slot[0] / kBlock;
+        uint32_t *kt = reinterpret_cast<uint32_t *>(kp + ((size_t)blk * Hkv + h) * TB);
+        uint32_t *vt = reinterpret_cast<uint32_t *>(vp + ((size_t)blk * Hkv + h) * TB);
+        // 16-byte piece pc holds dwords 4 pc .. 4 pc + 3 of the code area
+        for (int pc = tid; pc < D / 2; pc += 256) {
+            u32x4_t wk, wv;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int w = 4 * pc + q;
+                // K dword (g*16 + o) * KJ + j: token o, channels 32 j + 8 g + e
+                const int j = w % KJ, go = w / KJ, g = go >> 4, o = go & 15;
+                uint8_t ck[8], cv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ck[e] = kc[o][32 * j + 8 * g + e];
+                // V dword (nn*2 + hh) * DT + dt: channel 16 dt + nn, tokens 8 hh + e
+                const int dt = w % DT, nh = w / DT, nn = nh >> 1, hh = nh & 1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cv[e] = vc[8 * hh + e][16 * dt + nn];
+                wk[q] = pack8(ck);
+                wv[q] = pack8(cv);
+            }
+            *reinterpret_cast<u32x4_t *>(kt + 4 * pc) = wk;
+            *reinterpret_cast<u32x4_t *>(vt + 4 * pc) = wv;
+        }
+        if (tid < kBlock) {
+            reinterpret_cast<float *>(kt + 2 * D)[tid] = ksc[tid];
+            reinterpret_cast<float *>(vt + 2 * D)[tid] = vsc[tid];
+        }
+        return;
+    }
+    const int sl = s_slot[t];
+    if (!have || sl < 0) return;
+    const int blk = sl / kBlock, o = sl % kBlock;
+    uint32_t *kt = reinterpret_cast<uint32_t *>(kp + ((size_t)blk * Hkv + h) * TB);
+    uint32_t *vt = reinterpret_cast<uint32_t *>(vp + ((size_t)blk * Hkv + h) * TB);
+    // K: the token's own runs, KJ dwords for each g
+    for (int w = part; w < 4 * KJ; w += 16) {
+        const int g = w / KJ, j = w % KJ;
+        uint8_t ck[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ck[e] = kc[t][32 * j + 8 * g + e];
+        kt[(g * kBlock + o) * KJ + j] = pack8(ck);
+    }
+    // V: nibble o & 7 of one dword per channel
+    const int hh = o >> 3, sh = 4 * (o & 7);
+#pragma unroll
+    for (int c = part * CPT; c < part * CPT + CPT; ++c) {
+        const int dt = c >> 4, nn = c & 15;
+        uint32_t *w = vt + (nn * 2 + hh) * DT + dt;
+        atomicAnd(w, ~(0xFu << sh));
+        atomicOr(w, (uint32_t)vc[t][c] << sh);
+    }
+    if (part == 0) {
+        reinterpret_cast<float *>(kt + 2 * D)[o] = ksc[t];
+        reinterpret_cast<float *>(vt + 2 * D)[o] = vsc[t];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 // Workspace: the split maxima and sums, then the split accumulators.
@@ -1606,50 +1900,52 @@ static int device_cus() {
     return cus;
 }
 
-template <int D, int NT, bool APPEND, bool Q8, bool MASKED>
+template <int D, int NT, bool APPEND, int KF, bool MASKED>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
     const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.grid_splits;
     // Two prefetch stages: always for bf16 single tiles (measured 3 % faster on
-    // large decode grids); for 8-bit tiles, whose conversions need the
+    // large decode grids); for 8- and 4-bit tiles, whose conversions need the
     // registers, only on grids that leave CUs free.
     if constexpr (NT == 1) {
-        if (!Q8 || nwg <= device_cus()) {
-            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, Q8, MASKED>), dim3((unsigned)nwg), dim3(256), 0,
+        if (KF == kKvBf16 || nwg <= device_cus()) {
+            hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, KF, MASKED>), dim3((unsigned)nwg), dim3(256), 0,
                                st, P);
             return;
         }
     }
-    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND, Q8, MASKED>), dim3((unsigned)nwg), dim3(256), 0, st, P);
+    hipLaunchKernelGGL((attn_parallel<D, NT, false, APPEND, KF, MASKED>), dim3((unsigned)nwg), dim3(256), 0, st, P);
 }
 
-template <int D, int NT, bool Q8, bool MASKED>
+// The appending variant exists for single-tile rows only (forward_impl fuses
+// no other batch).
+template <int D, int NT, int KF, bool MASKED>
 static void launch_parallel(const AttnParams &P, hipStream_t st) {
-    if constexpr (Q8 || MASKED) launch_parallel_as<D, NT, false, Q8, MASKED>(P, st);
-    else if (P.k_new) launch_parallel_as<D, NT, true, false, false>(P, st);
-    else launch_parallel_as<D, NT, false, false, false>(P, st);
+    if constexpr (KF != kKvBf16 || MASKED || NT != 1) launch_parallel_as<D, NT, false, KF, MASKED>(P, st);
+    else if (P.k_new) launch_parallel_as<D, NT, true, kKvBf16, false>(P, st);
+    else launch_parallel_as<D, NT, false, kKvBf16, false>(P, st);
 }
 
-template <int D, bool Q8, bool MASKED>
+template <int D, int KF, bool MASKED>
 static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
     const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
-        launch_parallel<D, 1, Q8, MASKED>(P, st);
+        launch_parallel<D, 1, KF, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P);
     } else {
-        launch_parallel<D, 2, Q8, MASKED>(P, st);
+        launch_parallel<D, 2, KF, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
-        hipLaunchKernelGGL((attn_sequential<D, Q8, MASKED>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
+        hipLaunchKernelGGL((attn_sequential<D, KF, MASKED>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
     }
 }
 
-template <int D, bool Q8>
+template <int D, int KF>
 static void launch_mfma_vis(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
-    if (P.tree_mask || P.window > 0) launch_mfma<D, Q8, true>(P, max_q_len, total_rows, st);
-    else launch_mfma<D, Q8, false>(P, max_q_len, total_rows, st);
+    if (P.tree_mask || P.window > 0) launch_mfma<D, KF, true>(P, max_q_len, total_rows, st);
+    else launch_mfma<D, KF, false>(P, max_q_len, total_rows, st);
 }
 
 }  // namespace pkv
@@ -1684,7 +1980,7 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                         float scale, const float *sinks, float *out, void *workspace, size_t workspace_bytes,
                         void *hip_stream, const AppendArgs *app, const MaskArgs *mk) {
-    if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8)
+    if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8 && dtype != KV_FP4)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: dtype %d not supported", dtype);
     if (head_dim != 64 && head_dim != 128)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: head_dim %d not supported (64, 128)", head_dim);
@@ -1770,10 +2066,10 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
 
     if (app) {
-        // One new token per row, at the row's own position. A decode batch in
-        // the parallel shape takes them inside the attention launch; any other
-        // batch is scattered first, as two calls would.
-        const bool fused = dtype == KV_BF16 && P.decode_only && max_q_len * P.G <= kParRows;
+        // One new token per row, at the row's own position. A decode batch
+        // whose rows fit one tile takes them inside the attention launch; any
+        // other batch is scattered first, as two calls would.
+        const bool fused = dtype == KV_BF16 && P.decode_only && max_q_len * P.G <= 16;
         if (fused) {
             P.k_new = static_cast<const uint16_t *>(app->k_new);
             P.v_new = static_cast<const uint16_t *>(app->v_new);
@@ -1790,11 +2086,14 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
 
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
-        if (head_dim == 64) launch_mfma_vis<64, false>(P, max_q_len, total_q_rows, st);
-        else launch_mfma_vis<128, false>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, kKvBf16>(P, max_q_len, total_q_rows, st);
+        else launch_mfma_vis<128, kKvBf16>(P, max_q_len, total_q_rows, st);
     } else if (dtype == KV_FP8) {
-        if (head_dim == 64) launch_mfma_vis<64, true>(P, max_q_len, total_q_rows, st);
-        else launch_mfma_vis<128, true>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, kKvFp8>(P, max_q_len, total_q_rows, st);
+        else launch_mfma_vis<128, kKvFp8>(P, max_q_len, total_q_rows, st);
+    } else if (dtype == KV_FP4) {
+        if (head_dim == 64) launch_mfma_vis<64, kKvFp4>(P, max_q_len, total_q_rows, st);
+        else launch_mfma_vis<128, kKvFp4>(P, max_q_len, total_q_rows, st);
     } else {
         const dim3 grid(total_q_rows, num_q_heads);
         if (head_dim == 64) hipLaunchKernelGGL((attn_f32<64>), grid, dim3(64), 0, st, P);
@@ -1868,10 +2167,10 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
                       void *k_pool, void *v_pool, int32_t num_blocks, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int32_t dtype, void *hip_stream) {
     using namespace pkv;
-    if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8)
+    if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8 && dtype != KV_FP4)
         PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: dtype %d not supported", dtype);
-    if (dtype == KV_FP8 && head_dim != 64 && head_dim != 128)
-        PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: 8-bit pools need head_dim 64 or 128, not %d", head_dim);
+    if ((dtype == KV_FP8 || dtype == KV_FP4) && head_dim != 64 && head_dim != 128)
+        PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: 8- and 4-bit pools need head_dim 64 or 128, not %d", head_dim);
     if (block_size != kBlock)
         PKV_FAIL(KV_EUNSUPPORTED, "kv_append_scatter: block_size %d not supported (16)", block_size);
     if (head_dim <= 0 || head_dim % 16 || head_dim > 256)
@@ -1889,7 +2188,18 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     const dim3 grid((unsigned)groups, (unsigned)num_kv_heads);
-    if (dtype == KV_FP8) {
+    if (dtype == KV_FP4) {
+        auto kn = static_cast<const uint16_t *>(k_new);
+        auto vn = static_cast<const uint16_t *>(v_new);
+        auto kpp = static_cast<uint8_t *>(k_pool);
+        auto vpp = static_cast<uint8_t *>(v_pool);
+        if (head_dim == 64)
+            hipLaunchKernelGGL(scatter4_kernel<64>, grid, dim3(256), 0, st, kn, vn, slot_mapping, n, kpp, vpp, num_blocks,
+                               num_kv_heads);
+        else
+            hipLaunchKernelGGL(scatter4_kernel<128>, grid, dim3(256), 0, st, kn, vn, slot_mapping, n, kpp, vpp,
+                               num_blocks, num_kv_heads);
+    } else if (dtype == KV_FP8) {
         auto kn = static_cast<const uint16_t *>(k_new);
         auto vn = static_cast<const uint16_t *>(v_new);
         auto kpp = static_cast<uint8_t *>(k_pool);

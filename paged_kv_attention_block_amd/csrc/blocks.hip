@@ -84,6 +84,7 @@ int kv_copy_blocks(void *k_pool, void *v_pool, const int32_t *src, const int32_t
     if (dtype == KV_BF16) tile = 16LL * head_dim * 2;
     else if (dtype == KV_F32) tile = 16LL * head_dim * 4;
     else if (dtype == KV_FP8) tile = 16LL * head_dim + 64;
+    else if (dtype == KV_FP4) tile = 8LL * head_dim + 64;
     else PKV_FAIL(KV_EUNSUPPORTED, "kv_copy_blocks: dtype %d not supported", dtype);
     if (n == 0) return KV_OK;
     if (!k_pool || !v_pool || !src || !dst) PKV_FAIL(KV_EINVAL, "kv_copy_blocks: required pointer is NULL");

@@ -40,15 +40,17 @@ class Staged:
 
 
 def _torch_dtype(name):
-    """Element type of the pools for a workload dtype ("fp8": 8-bit pools)."""
+    """Element type of the pools for a workload dtype ("fp8", "fp4": 8- and
+    4-bit pools)."""
     import torch
-    return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[name]
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": "fp8", "fp4": "fp4"}[name]
 
 
 def _to_device(a, dtype_name, device):
-    """Rows (queries, new K/V) to the device; "fp8" workloads carry bf16 rows."""
+    """Rows (queries, new K/V) to the device; "fp8" and "fp4" workloads carry
+    bf16 rows."""
     import torch
-    if dtype_name in ("bf16", "fp8"):
+    if dtype_name in ("bf16", "fp8", "fp4"):
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
         return t.view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
@@ -79,7 +81,7 @@ def stage(w, device="cuda", copies: int = 1, poison: bool = True, scatter_step: 
     dt = _torch_dtype(w.dtype)
     Hkv, D = w.num_kv_heads, w.head_dim
     k0, v0 = empty_pools(w.num_blocks, Hkv, D, dt, device)
-    if poison and w.dtype == "fp8":
+    if poison and w.dtype in ("fp8", "fp4"):
         k0.fill_(0xFF)   # code 0xFF is NaN in E4M3FN, four 0xFF bytes a NaN scale
         v0.fill_(0xFF)
     elif poison:

@@ -55,7 +55,7 @@ class Seq:
 @dataclass
 class Workload:
     name: str
-    dtype: str               # 'bf16' | 'f32' (storage and Q type) | 'fp8' (bf16 rows, 8-bit pools)
+    dtype: str               # 'bf16' | 'f32' (storage and Q type) | 'fp8' / 'fp4' (bf16 rows, 8- / 4-bit pools)
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
@@ -89,10 +89,10 @@ class Workload:
 
 
 def _normal(rng, shape, dtype):
-    """N(0, 1) values; bf16 bits for bf16 workloads and for 8-bit-pool ("fp8")
-    workloads, whose queries and new K/V rows arrive in bf16."""
+    """N(0, 1) values; bf16 bits for bf16 workloads and for 8- and 4-bit-pool
+    ("fp8", "fp4") workloads, whose queries and new K/V rows arrive in bf16."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return f32_to_bf16_bits(x) if dtype in ("bf16", "fp8") else x
+    return f32_to_bf16_bits(x) if dtype in ("bf16", "fp8", "fp4") else x
 
 
 def _pool_size(unique_blocks: int, exact: Optional[int] = None) -> int:
@@ -205,8 +205,10 @@ def verify_window(seed=1005, n=16, lo=4096, hi=16384, window=8, dtype="bf16"):
 
 
 def by_name(name, **kw):
-    """A named workload; the suffix "_fp8" selects 8-bit pools for the same rows."""
-    if name.endswith("_fp8") and name != "tiny_decode_fp8":
-        return by_name(name[:-4], dtype="fp8", **kw)
+    """A named workload; the suffix "_fp8" or "_fp4" selects 8- or 4-bit pools
+    for the same rows."""
+    for fmt in ("fp8", "fp4"):
+        if name.endswith("_" + fmt):
+            return by_name(name[:-4], dtype=fmt, **kw)
     return {"tiny_decode": tiny_decode, "mid_decode": mid_decode, "sink_decode": sink_decode,
             "mixed_step": mixed_step, "verify_window": verify_window}[name](**kw)

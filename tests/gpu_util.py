@@ -7,7 +7,7 @@ import numpy as np
 import oracle
 import synth
 
-TOL = {"bf16": 2e-3, "f32": 1e-5, "fp8": 2e-3}
+TOL = {"bf16": 2e-3, "f32": 1e-5, "fp8": 2e-3, "fp4": 2e-3}
 
 
 def oracle_side(w, fill_nan=True, tree_mask=None, window=0, drop=None):
@@ -29,6 +29,10 @@ def oracle_side(w, fill_nan=True, tree_mask=None, window=0, drop=None):
         kp, vp = oracle.fp8_empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim,
                                         fill=np.uint8(0xFF) if fill_nan else None)
         put = oracle.fp8_scatter
+    elif w.dtype == "fp4":
+        kp, vp = oracle.fp4_empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim,
+                                        fill=np.uint8(0xFF) if fill_nan else None)
+        put = oracle.fp4_scatter
     else:
         nan = np.uint16(0x7FC0) if w.dtype == "bf16" else np.float32(np.nan)
         kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype,
@@ -49,10 +53,12 @@ def oracle_side(w, fill_nan=True, tree_mask=None, window=0, drop=None):
 
 
 def _dense(rows, dtype):
-    """Dense K or V rows as the attention sees them: for 8-bit pools the
-    oracle's quantize-then-dequantize of each (token, KV head) row."""
+    """Dense K or V rows as the attention sees them: for 8- and 4-bit pools
+    the oracle's quantize-then-dequantize of each (token, KV head) row."""
     if dtype == "fp8":
         return oracle.fp8_dequantize(*oracle.fp8_quantize_rows(rows))
+    if dtype == "fp4":
+        return oracle.fp4_dequantize(*oracle.fp4_quantize_rows(rows))
     return rows
 
 

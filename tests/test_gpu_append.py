@@ -83,16 +83,17 @@ def test_sink_decode_large_grid(pk):
     _check(pk, synth.sink_decode(), oracle_sample=[0, 7, 31])
 
 
-def test_decode_into_8bit_pools(pk):
-    """Decode rows into 8-bit pools: the new tokens are quantized by the
-    scatter launch, then attended."""
-    _check(pk, synth.sink_decode(dtype="fp8"), oracle_sample=[0, 7, 31])
+@pytest.mark.parametrize("dtype", ["fp8", "fp4"])
+def test_decode_into_quantized_pools(pk, dtype):
+    """Decode rows into 8- and 4-bit pools: the new tokens are quantized by
+    the scatter launch, then attended."""
+    _check(pk, synth.sink_decode(dtype=dtype), oracle_sample=[0, 7, 31])
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(8, 2, 64), (40, 2, 128), (4, 4, 128)])
 def test_block_and_split_boundaries(pk, Hq, Hkv, D):
     """New tokens at every offset class in a block and next to split edges;
-    40/2 heads take the two-tile rows."""
+    40/2 heads take the two-tile rows, which scatter first."""
     ctxs = [1, 2, 15, 16, 17, 31, 32, 33, 255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049, 3072, 4097]
     w = custom("bf16", Hq, Hkv, D, ctxs, [1] * len(ctxs), seed=Hq * 100 + Hkv * 10 + D, sinks=(Hq % 8 == 0))
     _check(pk, w)
@@ -105,9 +106,9 @@ def test_resident_token_slot_minus_one(pk):
     _check(pk, w, resident_slots=(1, 3))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp4"])
 def test_other_batches_scatter_first(pk, dtype):
-    """Verify windows, prefill chunks, fp32 and 8-bit pools take the scatter
+    """Verify windows, prefill chunks, fp32, 8- and 4-bit pools take the scatter
     launch first; the result is the same as two calls."""
     w = custom(dtype, 16, 4, 64, [300, 1100, 70, 40], [8, 130, 1, 40], seed=99)
     _check(pk, w)

@@ -50,7 +50,8 @@ def alone(pk, st, w, i):
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("bf16", 64, 8, 64), ("f32", 4, 2, 64),
-                                             ("bf16", 8, 8, 64), ("fp8", 32, 8, 128), ("fp8", 64, 8, 64)])
+                                             ("bf16", 8, 8, 64), ("fp8", 32, 8, 128), ("fp8", 64, 8, 64),
+                                             ("fp4", 32, 8, 128), ("fp4", 64, 8, 64)])
 def test_window_rows_equal_rows_alone(pk, dtype, Hq, Hkv, D):
     import torch
     from paged_kv_attention_block_amd.staging import stage

@@ -16,7 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, custom, max_err, oracle_side
+from gpu_util import TOL, _dense, custom, max_err, oracle_side
 
 pytestmark = pytest.mark.gpu
 
@@ -82,7 +82,7 @@ def check(pk, w, tree_mask=None, window=0, drop=None):
                        set(int(b) for r in rows for b in r if b >= 0))
         if freed:
             idx = torch.tensor(freed, dtype=torch.long, device="cuda")
-            fill = 0xFF if w.dtype == "fp8" else float("nan")
+            fill = 0xFF if w.dtype in ("fp8", "fp4") else float("nan")
             st.k_pools[0][idx] = fill
             st.v_pools[0][idx] = fill
     out = masked(pk, st, w, tree_mask, window, tables)
@@ -98,7 +98,7 @@ def check(pk, w, tree_mask=None, window=0, drop=None):
     return st, out
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp4"])
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 2, 64), (8, 8, 64)])
 def test_tree_windows(pk, dtype, Hq, Hkv, D):
     """Tree windows of up to 16 rows (both tile counts), next to decode rows,
@@ -123,7 +123,7 @@ def test_chain_mask_equals_causal_bitwise(pk):
     np.testing.assert_array_equal(bits(a), bits(b))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 def test_tree_row_equals_window_cut_after_it(pk, dtype):
     """Row r of a tree window gives the same bits as the last row of the same
     window cut after row r (context base + r + 1, masks of rows 0 .. r)."""
@@ -145,14 +145,14 @@ def test_tree_row_equals_window_cut_after_it(pk, dtype):
         np.testing.assert_array_equal(bits(out)[r], full[r])
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp4"])
 @pytest.mark.parametrize("window", [1, 100, 128, 1000, 4096])
 def test_sliding_window_decode(pk, dtype, window):
     w = custom(dtype, 64, 8, 64, [1024, 5000, 8192, 3000, 130, 2049], [1] * 6, seed=700 + window, sinks=True)
     check(pk, w, window=window)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 @pytest.mark.parametrize("window", [7, 128, 700])
 def test_sliding_window_verify_and_prefill(pk, dtype, window):
     """Verify windows (8 rows), a long prefill chunk (the sequential shape)
@@ -161,7 +161,7 @@ def test_sliding_window_verify_and_prefill(pk, dtype, window):
     check(pk, w, window=window)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 def test_sliding_window_with_freed_blocks(pk, dtype):
     """Blocks below every row's window freed on the host (table entries -1)
     and poisoned in the pool: nothing changes."""
@@ -217,15 +217,15 @@ def test_masked_rejects_bad_arguments(pk):
 # block copies, accept walk, rollback
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp4"])
 def test_copy_blocks_bit_exact(pk, dtype):
     import torch
     rng = np.random.default_rng(12)
     nb, hkv, D = 40, 3, 128 if dtype != "f32" else 64
     announce(f"copy blocks {dtype}")
-    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[dtype]
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": "fp8", "fp4": "fp4"}[dtype]
     kp, vp = pk.empty_pools(nb, hkv, D, tdt, "cuda")
-    if dtype == "fp8":
+    if dtype in ("fp8", "fp4"):
         kp.copy_(torch.randint(0, 256, kp.shape, dtype=torch.uint8))
         vp.copy_(torch.randint(0, 256, vp.shape, dtype=torch.uint8))
     else:
@@ -277,7 +277,7 @@ def test_accept_paths_match_oracle(pk):
     assert max(lens) >= 3
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 def test_rollback_round(pk, dtype):
     """One speculative round end to end on two sequences with a 12-row draft
     tree each. Sequence 1 allocates the prompt and its first 8 drafts (the
@@ -291,7 +291,7 @@ def test_rollback_round(pk, dtype):
     import synth
     rng = np.random.default_rng(14 + len(dtype))
     B, Hq, Hkv, D, nb = 16, 32, 8, 128, 64
-    tdt = torch.uint8 if dtype == "fp8" else torch.bfloat16
+    tdt = dtype if dtype in ("fp8", "fp4") else torch.bfloat16
     t = lambda a: torch.tensor(np.asarray(a, dtype=np.int32), device="cuda")
 
     def rows(*shape):
@@ -305,8 +305,8 @@ def test_rollback_round(pk, dtype):
 
     pool = pk.kv_pool_create(nb, B, rng.permutation(nb))
     kp, vp = pk.empty_pools(nb, Hkv, D, tdt, "cuda")
-    kp.fill_(0xFF if dtype == "fp8" else float("nan"))
-    vp.fill_(0xFF if dtype == "fp8" else float("nan"))
+    kp.fill_(0xFF if dtype in ("fp8", "fp4") else float("nan"))
+    vp.fill_(0xFF if dtype in ("fp8", "fp4") else float("nan"))
     prompt = [int(x) for x in rng.integers(0, 50, 40)]          # 2 full blocks + 8 tokens
     kr, vr = rows(40, Hkv, D), rows(40, Hkv, D)
     parents = [-1, 0, 0, 1, 2, 3, -1, 6, 4, 8, 9, 10]
@@ -365,9 +365,9 @@ def test_rollback_round(pk, dtype):
     torch.cuda.synchronize()
     ks = [np.concatenate([kr, kw[s][acc[s]], kn[s:s + 1]]) for s in (0, 1)]
     vs = [np.concatenate([vr, vw[s][acc[s]], vn[s:s + 1]]) for s in (0, 1)]
-    if dtype == "fp8":
-        ks = [oracle.fp8_dequantize(*oracle.fp8_quantize_rows(k)) for k in ks]
-        vs = [oracle.fp8_dequantize(*oracle.fp8_quantize_rows(v)) for v in vs]
+    if dtype in ("fp8", "fp4"):
+        ks = [_dense(k, dtype) for k in ks]
+        vs = [_dense(v, dtype) for v in vs]
     want = oracle.attention(q, ks, vs, np.array([0, 1, 2], np.int32), Hq, Hkv, 1.0 / np.sqrt(D), None, dtype)
     err = max_err(out.cpu().numpy(), want)
     print(f"[case] rollback round {dtype}: max abs err {err:.3e}", flush=True)

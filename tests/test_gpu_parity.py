@@ -3,7 +3,7 @@
 Every test compares the library's output, produced through the C ABI
 (kv_pool_alloc, kv_append_scatter, paged_attention_forward), with the fp64
 oracle on the same seeded inputs: max-abs error <= 2e-3 for bf16 K/V and for
-8-bit pools (against the oracle's attention over its own dequantized codes),
+8- and 4-bit pools (against the oracle's attention over its own dequantized codes),
 <= 1e-5 for fp32 K/V, and bit-exact pools after the scatter-write.
 """
 import sys
@@ -64,17 +64,18 @@ def check_workload(pk, w, compare_pools=True, sample_rows=None):
 
 
 @pytest.mark.parametrize("name", ["tiny_decode", "mid_decode", "sink_decode", "verify_window",
-                                  "mid_decode_fp8", "sink_decode_fp8", "verify_window_fp8"])
+                                  "mid_decode_fp8", "sink_decode_fp8", "verify_window_fp8",
+                                  "mid_decode_fp4", "sink_decode_fp4", "verify_window_fp4"])
 def test_named_workloads_full(pk, name):
     check_workload(pk, synth.by_name(name))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 def test_mixed_step_full(pk, dtype):
     check_workload(pk, synth.mixed_step(dtype=dtype))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp4"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 1), (8, 8), (16, 2), (12, 4)])
 def test_small_shapes(pk, dtype, D, Hq, Hkv):
@@ -90,7 +91,7 @@ def test_small_shapes(pk, dtype, D, Hq, Hkv):
     check_workload(pk, w)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8", "fp4"])
 def test_prefill_chunks_and_decode_mixed(pk, dtype):
     """Long prefill windows (multi-rowblock path) next to decode rows."""
     w = custom(dtype, 8, 2, 128, [300, 1100, 70, 2500, 5], [300, 130, 1, 1, 5], seed=77, sinks=True)
@@ -102,7 +103,7 @@ def test_prefill_from_zero_full_causal(pk):
     check_workload(pk, w)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_prefill_chunk_on_long_context(pk, D, dtype):
     """Prefill chunks whose rows see thousands of keys: the prefill shape walks
@@ -111,13 +112,13 @@ def test_prefill_chunk_on_long_context(pk, D, dtype):
     check_workload(pk, w)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 def test_long_context(pk, dtype):
     w = custom(dtype, 16, 2, 128, [20000, 9000], [1, 4], seed=79, sinks=True)
     check_workload(pk, w)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
 def test_shared_prefix_sequences(pk, dtype):
     w = custom(dtype, 16, 4, 64, [700, 650, 901, 64], [1, 1, 3, 1], seed=80, shared_prefix=600, n_shared=3)
     check_workload(pk, w)

@@ -101,10 +101,39 @@ def test_scatter_then_gather_gives_the_dequantized_rows(D):
     np.testing.assert_array_equal(gv, oracle.fp4_dequantize(vc, vs))
     assert np.all(kp[perm[5:]] == 0xFF)
     # the codes of one block, read back nibble by nibble by hand
-    b, h, t, c = int(table[1]), 2, 5, 37
-    nib = int(oracle._fp4_k_nibbles(D)[t, c])
-    byte = int(kp[b, h, nib // 2])
-    assert (byte >> 4 if nib % 2 else byte & 0xF) == kc[16 + t, h, c]
+    # every code and scale read back nibble by nibble, byte by byte, by hand
+    nk, nv = oracle._fp4_k_nibbles(D), oracle._fp4_v_nibbles(D)
+    for tok in range(0, ctx, 3):
+        blk, off = int(table[tok // 16]), tok % 16
+        for h in range(hkv):
+            for pool, nib, codes, sc in ((kp, nk, kc, ks), (vp, nv, vc, vs)):
+                for c in range(D):
+                    n_ = int(nib[off, c])
+                    byte = int(pool[blk, h, n_ // 2])
+                    assert (byte >> 4 if n_ % 2 else byte & 0xF) == codes[tok, h, c]
+                raw = bytes(int(x) for x in pool[blk, h, 8 * D + 4 * off:8 * D + 4 * off + 4])
+                assert np.frombuffer(raw, np.float32)[0] == sc[tok, h]
+
+
+def test_scatter_of_interleaved_tokens_keeps_both_nibbles():
+    """Two tokens sharing V bytes, written by separate calls and in one call
+    in either order, give the same tiles as one whole-block write."""
+    rng = np.random.default_rng(21)
+    D, hkv = 64, 2
+    k = synth.f32_to_bf16_bits(rng.standard_normal((16, hkv, D), dtype=np.float32))
+    v = synth.f32_to_bf16_bits(rng.standard_normal((16, hkv, D), dtype=np.float32))
+    whole = oracle.fp4_empty_pools(2, hkv, D, fill=0xFF)
+    oracle.fp4_scatter(*whole, k, v, np.arange(16) + 16)
+    odd_even = oracle.fp4_empty_pools(2, hkv, D, fill=0xFF)
+    order = np.r_[np.arange(1, 16, 2), np.arange(0, 16, 2)]
+    for half in (order[:8], order[8:]):
+        oracle.fp4_scatter(*odd_even, k[half], v[half], half + 16)
+    mixed = oracle.fp4_empty_pools(2, hkv, D, fill=0xFF)
+    perm = rng.permutation(16)
+    oracle.fp4_scatter(*mixed, k[perm], v[perm], perm + 16)
+    for got in (odd_even, mixed):
+        np.testing.assert_array_equal(got[0][1], whole[0][1])
+        np.testing.assert_array_equal(got[1][1], whole[1][1])
 
 
 def test_paged_attention_on_4bit_pools_matches_dense_brute_force():
