@@ -35,8 +35,10 @@ MIN_FOOTPRINT = 1 << 30        # bytes of pool touched per step
 
 def row_bytes(w):
     """Bytes one token's K (or V) row of one KV head occupies in the pool:
-    head_dim elements, or for 8-bit pools head_dim codes and a float32 scale."""
-    return {"bf16": 2 * w.head_dim, "f32": 4 * w.head_dim, "fp8": w.head_dim + 4}[w.dtype]
+    head_dim elements, or for 8- and 4-bit pools head_dim codes (one or half
+    a byte each) and a float32 scale."""
+    return {"bf16": 2 * w.head_dim, "f32": 4 * w.head_dim, "fp8": w.head_dim + 4,
+            "fp4": w.head_dim // 2 + 4}[w.dtype]
 
 
 def elem_bytes(w):
@@ -104,6 +106,9 @@ def cpu_baseline(w, kv_bytes, rows, seconds, tree_mask=None, window=0):
     if w.dtype == "fp8":
         kp, vp = oracle.fp8_empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim)
         put = oracle.fp8_scatter
+    elif w.dtype == "fp4":
+        kp, vp = oracle.fp4_empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim)
+        put = oracle.fp4_scatter
     else:
         kp, vp = oracle.empty_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, w.dtype)
         put = oracle.scatter
@@ -177,7 +182,7 @@ def _short(name):
 
 def _appending(kernel):
     """True for attn_parallel instances with the appending path: template
-    arguments <head_dim, tiles, prefetch, append, 8-bit pools, masked>."""
+    arguments <head_dim, tiles, prefetch, append, tile format, masked>."""
     if not kernel.startswith("attn_parallel<"):
         return False
     args = [a.strip() for a in kernel[kernel.index("<") + 1:kernel.rindex(">")].split(",")]
