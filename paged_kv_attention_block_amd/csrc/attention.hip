@@ -283,6 +283,33 @@ __device__ inline void patch_new_key(StepRegs<D> &r, const u32x4_t (&knew)[D / 3
     }
 }
 
+// Reductions over the four lanes n, n + 16, n + 32, n + 48 that hold one
+// row. The gfx950 lane swaps exchange rows 0/1 and 2/3 (16) or the two
+// halves (32) of two copies of x, after which every lane holds the lower and
+// the upper value of its pair: no trip through LDS. max and + are
+// commutative, so both lanes of a pair get the same bits, the bits a
+// lane-own + partner order gives.
+__device__ inline float2 lane_pair16(float x) {
+    const int v = __builtin_bit_cast(int, x);
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return make_float2(__builtin_bit_cast(float, (int)s[0]), __builtin_bit_cast(float, (int)s[1]));
+}
+__device__ inline float2 lane_pair32(float x) {
+    const int v = __builtin_bit_cast(int, x);
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return make_float2(__builtin_bit_cast(float, (int)s[0]), __builtin_bit_cast(float, (int)s[1]));
+}
+__device__ inline float row_max4(float x) {
+    float2 p = lane_pair16(x);
+    p = lane_pair32(fmaxf(p.x, p.y));
+    return fmaxf(p.x, p.y);
+}
+__device__ inline float row_sum4(float x) {
+    float2 p = lane_pair16(x);
+    p = lane_pair32(p.x + p.y);
+    return p.x + p.y;
+}
+
 // One online-softmax step over the MFMA operands kop(tau, j) (K, tile tau,
 // k-step j) and vop(dt) (V^T, d-tile dt). SCALED: 8-bit pools, whose scores
 // take the keys' K scales (ksc, the lane's 8 keys) and whose probabilities
@@ -343,9 +370,8 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
             sc[4 + i] = vis(i + 4) ? s1[i] * scale_log2 : -INFINITY;
         }
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mx =
+        row_max4(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))));
     // the row sees at least one key of the chunk (with a restricted
     // visibility: its maximum over the chunk is a score)
     const bool has = MASKED ? mx != -INFINITY : kc <= prow;
@@ -355,9 +381,7 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     float pv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
-    float rs = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
+    const float rs = row_sum4(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
     bf16x8_t phi, plo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -367,19 +391,23 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
         phi[e] = x;
         plo[e] = (__bf16)(w - (float)x);
     }
-    // Rows with no visible key in the chunk keep their state exactly; the
-    // rescale by alpha is skipped when it is 1 in every lane (x * 1 == x).
-    const bool rescale = __any(alpha != 1.f);
-    const bool all_has = __all(has);
+    // The rescale is exact where alpha is 1 (denormals are kept). Rows with
+    // no visible key in the chunk keep their state exactly; padding rows
+    // (prow < 0) are never stored, so only real rows decide which path runs.
+    f32x4_t a[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        f32x4_t a = st.acc[dt];
-        if (rescale) a *= alpha;
         const bf16x8_t va = vop(dt);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a, 0, 0, 0);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a, 0, 0, 0);
-        st.acc[dt] = (all_has || has) ? a : st.acc[dt];
+        a[dt] = st.acc[dt] * alpha;
+        a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a[dt], 0, 0, 0);
+        a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a[dt], 0, 0, 0);
     }
+    if (!__all(has || prow < 0)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) a[dt] = has ? a[dt] : st.acc[dt];
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = a[dt];
     const float l_new = fmaf(alpha, st.l, rs);
     st.l = has ? l_new : st.l;
     st.m = has ? m_new : st.m;
@@ -409,7 +437,7 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
     }
     bf16x8_t phi[2], plo[2];
     float alpha[2], m_new[2], rs[2];
-    bool has[2], rescale[2], all_has[2];
+    bool has[2], fast = true;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int prow = rv[t].prow;
@@ -428,10 +456,8 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
                 sc[4 + i] = vis(i + 4) ? s1[t][i] * scale_log2 : -INFINITY;
             }
         }
-        float mx =
-            fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mx = row_max4(
+            fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))));
         has[t] = MASKED ? mx != -INFINITY : kc <= prow;
         m_new[t] = fmaxf(st[t].m, mx);
         const float m_use = m_new[t] == -INFINITY ? 0.f : m_new[t];
@@ -439,10 +465,7 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
-        float r = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-        r += __shfl_xor(r, 16, 64);
-        r += __shfl_xor(r, 32, 64);
-        rs[t] = r;
+        rs[t] = row_sum4(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float w = pv[e];
@@ -451,21 +474,30 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
             phi[t][e] = x;
             plo[t][e] = (__bf16)(w - (float)x);
         }
-        rescale[t] = __any(alpha[t] != 1.f);
-        all_has[t] = __all(has[t]);
+        fast = fast && __all(has[t] || prow < 0);
     }
+    // as in step_core, for both tiles at once
+    f32x4_t a[2][DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const bf16x8_t va = vop(dt);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            f32x4_t a = st[t].acc[dt];
-            if (rescale[t]) a *= alpha[t];
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], a, 0, 0, 0);
-            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], a, 0, 0, 0);
-            st[t].acc[dt] = (all_has[t] || has[t]) ? a : st[t].acc[dt];
+            a[t][dt] = st[t].acc[dt] * alpha[t];
+            a[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], a[t][dt], 0, 0, 0);
+            a[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], a[t][dt], 0, 0, 0);
         }
     }
+    if (!fast) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) a[t][dt] = has[t] ? a[t][dt] : st[t].acc[dt];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st[t].acc[dt] = a[t][dt];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float l_new = fmaf(alpha[t], st[t].l, rs[t]);
@@ -995,25 +1027,29 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
         // appending decode step: the wave whose quarter holds the new key
         const int pn = ctx - 1;
         const bool fused = APPEND && KF == kKvBf16 && kq0 <= pn && pn < kq1;
-        u32x4_t knew[KJ];
-        uint32_t vnew[DT];
+        // The new token's K and V rows wait in LDS (this wave's slot) for the
+        // step that holds pn, rather than in registers through the loop.
+        __shared__ __attribute__((aligned(16))) uint16_t s_new[APPEND ? 4 : 1][2][D];
         if (APPEND && KF == kKvBf16 && fused) {
             const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
-#pragma unroll
-            for (int jj = 0; jj < KJ; ++jj)
-                knew[jj] = *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + (4 * jj + g) * 8);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) vnew[dt] = P.v_new[rowoff + 16 * dt + n];
-            // and writes it to its pool slot, as the scatter-write would
             const int slot = P.slots[s];
+            if (lane < D / 8) {
+                const u32x4_t kq = *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + lane * 8);
+                *reinterpret_cast<u32x4_t *>(&s_new[wave][0][lane * 8]) = kq;
+                *reinterpret_cast<u32x4_t *>(&s_new[wave][1][lane * 8]) =
+                    *reinterpret_cast<const u32x4_t *>(P.v_new + rowoff + lane * 8);
+                // and writes it to its pool slot, as the scatter-write would
+                if (slot >= 0 && slot < P.num_blocks * kBlock) {
+                    const size_t tb = ((size_t)(slot / kBlock) * P.Hkv + kvh) * D;  // element offset of the tile
+                    *reinterpret_cast<u32x4_t *>(P.kp_w + tb * kBlock + ((size_t)lane * kBlock + slot % kBlock) * 8) =
+                        kq;
+                }
+            }
             if (slot >= 0 && slot < P.num_blocks * kBlock) {
-                const int b = slot / kBlock, o = slot % kBlock;
-                const size_t tb = ((size_t)b * P.Hkv + kvh) * D;  // element offset of the (block, head) tile
-                if (lane < D / 8)
-                    *reinterpret_cast<u32x4_t *>(P.kp_w + tb * kBlock + ((size_t)lane * kBlock + o) * 8) =
-                        *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + lane * 8);
+                const size_t tb = ((size_t)(slot / kBlock) * P.Hkv + kvh) * D;
 #pragma unroll
-                for (int c = lane; c < D; c += 64) P.vp_w[tb * kBlock + (size_t)c * kBlock + o] = P.v_new[rowoff + c];
+                for (int c = lane; c < D; c += 64)
+                    P.vp_w[tb * kBlock + (size_t)c * kBlock + slot % kBlock] = P.v_new[rowoff + c];
             }
         }
         const size_t tile = PoolT::tile_bytes;
@@ -1032,8 +1068,20 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
                         g, n);
         };
         auto compute = [&](Regs &r, int kc) {
-            if constexpr (APPEND && KF == kKvBf16)
-                if (fused && kc <= pn && pn < kc + kStep) patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
+            if constexpr (APPEND && KF == kKvBf16) {
+                if (fused && kc <= pn && pn < kc + kStep) {
+                    // LDS operations of one wave complete in order: the rows
+                    // written above are there
+                    u32x4_t knew[KJ];
+                    uint32_t vnew[DT];
+#pragma unroll
+                    for (int jj = 0; jj < KJ; ++jj)
+                        knew[jj] = *reinterpret_cast<const u32x4_t *>(&s_new[wave][0][(4 * jj + g) * 8]);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) vnew[dt] = s_new[wave][1][16 * dt + n];
+                    patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
+                }
+            }
             PoolT::mask(r, kc, ctx, g);
             if constexpr (NT == 2) {
                 if (rows_total > 16)  // uniform: both tiles in one pass over the operands
