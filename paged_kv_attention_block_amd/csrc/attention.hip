@@ -43,6 +43,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 16;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -150,7 +151,10 @@ __device__ inline void fold_state(TileState<DT> &a, const TileState<DT> &b) {
 }
 
 // out = acc / (l + sink term); the sink logit (log2 units, -inf if none)
-// takes part in the max.
+// takes part in the max. A zero output is written as +0 (x + 0 turns -0 into
+// +0 and keeps every other value): a row's accumulators carry its values
+// exactly through steps in which it sees no key, but not always the sign of
+// a zero (see step_core).
 template <int DT>
 __device__ inline void finalize(const TileState<DT> &s, float sink2, f32x4_t *o) {
     float l = s.l;
@@ -163,7 +167,7 @@ __device__ inline void finalize(const TileState<DT> &s, float sink2, f32x4_t *o)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[dt][i] = (s.acc[dt][i] * al) / l;
+        for (int i = 0; i < 4; ++i) o[dt][i] = (s.acc[dt][i] * al) / l + 0.0f;
 }
 
 // ---------------------------------------------------------------------------
@@ -283,6 +287,23 @@ __device__ inline void patch_new_key(StepRegs<D> &r, const u32x4_t (&knew)[D / 3
     }
 }
 
+// P as bf16 hi + lo pairs: hi = w rounded to bf16 (nearest even), lo = the
+// rest rounded to bf16; two values per conversion instruction.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ inline void split_hi_lo(const float (&w)[8], bf16x8_t &phi, bf16x8_t &plo) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const auto h = __builtin_convertvector(f32x2_t{w[e], w[e + 1]}, bf16x2_t);
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+        const float h0 = __builtin_bit_cast(float, hb << 16), h1 = __builtin_bit_cast(float, hb & 0xFFFF0000u);
+        const auto l = __builtin_convertvector(f32x2_t{w[e] - h0, w[e + 1] - h1}, bf16x2_t);
+        phi[e] = h[0];
+        phi[e + 1] = h[1];
+        plo[e] = l[0];
+        plo[e + 1] = l[1];
+    }
+}
+
 // Reductions over the four lanes n, n + 16, n + 32, n + 48 that hold one
 // row. The gfx950 lane swaps exchange rows 0/1 and 2/3 (16) or the two
 // halves (32) of two copies of x, after which every lane holds the lower and
@@ -383,31 +404,27 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
     const float rs = row_sum4(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
     bf16x8_t phi, plo;
+    {
+        float w[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float w = pv[e];
-        if constexpr (SCALED) w = w * vsc[e];
-        const __bf16 x = (__bf16)w;
-        phi[e] = x;
-        plo[e] = (__bf16)(w - (float)x);
+        for (int e = 0; e < 8; ++e) w[e] = SCALED ? pv[e] * vsc[e] : pv[e];
+        split_hi_lo(w, phi, plo);
     }
-    // The rescale is exact where alpha is 1 (denormals are kept). Rows with
-    // no visible key in the chunk keep their state exactly; padding rows
-    // (prow < 0) are never stored, so only real rows decide which path runs.
-    f32x4_t a[DT];
+    // A row with no visible key in the chunk keeps m and l (selects), and
+    // its accumulators keep their values: alpha is 1 (x * 1 == x, denormals
+    // are kept) or the accumulators are still zero, and its weights are 0
+    // against finite V (masked tails are zeroed), so the products add zeros.
+    // Only a zero's sign can change (-0 + 0 = +0), which finalize removes.
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const bf16x8_t va = vop(dt);
-        a[dt] = st.acc[dt] * alpha;
-        a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, a[dt], 0, 0, 0);
-        a[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, a[dt], 0, 0, 0);
+        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, st.acc[dt], 0, 0, 0);
+        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, st.acc[dt], 0, 0, 0);
     }
-    if (!__all(has || prow < 0)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) a[dt] = has ? a[dt] : st.acc[dt];
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) st.acc[dt] = a[dt];
     const float l_new = fmaf(alpha, st.l, rs);
     st.l = has ? l_new : st.l;
     st.m = has ? m_new : st.m;
@@ -437,7 +454,7 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
     }
     bf16x8_t phi[2], plo[2];
     float alpha[2], m_new[2], rs[2];
-    bool has[2], fast = true;
+    bool has[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const int prow = rv[t].prow;
@@ -466,38 +483,28 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(sc[e] - m_use);
         rs[t] = row_sum4(((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7])));
+        float w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float w = pv[e];
-            if constexpr (SCALED) w = w * vsc[e];
-            const __bf16 x = (__bf16)w;
-            phi[t][e] = x;
-            plo[t][e] = (__bf16)(w - (float)x);
-        }
-        fast = fast && __all(has[t] || prow < 0);
+        for (int e = 0; e < 8; ++e) w[e] = SCALED ? pv[e] * vsc[e] : pv[e];
+        split_hi_lo(w, phi[t], plo[t]);
     }
     // as in step_core, for both tiles at once
-    f32x4_t a[2][DT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (__any(alpha[t] != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) st[t].acc[dt] *= alpha[t];
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const bf16x8_t va = vop(dt);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            a[t][dt] = st[t].acc[dt] * alpha[t];
-            a[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], a[t][dt], 0, 0, 0);
-            a[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], a[t][dt], 0, 0, 0);
+            st[t].acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], st[t].acc[dt], 0, 0, 0);
+            st[t].acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], st[t].acc[dt], 0, 0, 0);
         }
     }
-    if (!fast) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) a[t][dt] = has[t] ? a[t][dt] : st[t].acc[dt];
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st[t].acc[dt] = a[t][dt];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const float l_new = fmaf(alpha[t], st[t].l, rs[t]);
@@ -534,7 +541,6 @@ __device__ inline void step_update2(TileState<D / 16> (&st)[2], const StepRegs<D
 // or its V^T operands of two d-tiles. Codes become bf16 exactly; scales act
 // in float32 on the scores (K) and on the probabilities (V).
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <int D>
 constexpr int q8_tile_bytes() { return 16 * D + 64; }
