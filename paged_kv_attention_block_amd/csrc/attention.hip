@@ -210,13 +210,15 @@ __device__ inline void load_step(StepRegs<D> &r, const uint16_t *kb0, const uint
 }
 
 // The same operands from a step staged in LDS by attn_sequential, whose
-// layout permutes 16-byte pieces so that each group of 8 lanes reads 128
-// distinct bytes (no bank conflicts): in a K tile the 16 tokens of a channel
-// chunk sit in the order 0-3, 8-11, 4-7, 12-15 (lds_k_pos), and in a V tile
-// the two 16-byte halves of channel row r swap when bit 2 of r is set
-// (lds_v_half). K tiles of blocks 0, 1 at k0, k1; V tiles at v0, v1.
+// layout permutes 16-byte pieces so that the lanes of one LDS cycle read
+// distinct banks, whether a cycle serves 8 lanes (128 bytes) or 16 (256):
+// in a K tile the 16 tokens of a channel chunk sit in the order 0-3, 8-11,
+// 4-7, 12-15 (lds_k_pos), the K tiles of the two blocks start 128 bytes
+// apart modulo 256, and in a V tile the two 16-byte halves of channel row r
+// swap when bit 2 xor bit 3 of r is set (lds_v_half). K tiles of blocks 0, 1
+// at k0, k1; V tiles at v0, v1.
 __device__ inline int lds_k_pos(int token) { return (token & 3) + ((token >> 3) << 2) + (((token >> 2) & 1) << 3); }
-__device__ inline int lds_v_half(int row, int half) { return half ^ ((row >> 2) & 1); }
+__device__ inline int lds_v_half(int row, int half) { return half ^ ((row >> 2) & 1) ^ ((row >> 3) & 1); }
 
 template <int D>
 __device__ inline void load_step_lds(StepRegs<D> &r, const uint16_t *k0, const uint16_t *v0, const uint16_t *k1,
@@ -757,15 +759,18 @@ __device__ inline void load_dw4(uint32_t *d, const uint8_t *src) {
     d[3] = w.w;
 }
 
-// Staged copies in LDS (attn_sequential) permute 16-byte pieces so that each
-// group of 8 lanes reads 128 distinct bytes: at D = 128 a K piece is one
-// token's run, kept in lds_k_pos order; a V piece q of channel row m's run
-// of half h (piece 4m + 2h + q at D = 128, 2m + h at D = 64) swaps with its
-// neighbours by bits of m.
+// Staged copies in LDS (attn_sequential) permute 16-byte pieces so that the
+// 8 or 16 lanes of one LDS cycle read distinct banks: at D = 128 a K piece is
+// one token's run, kept in lds_k_pos order; a V piece c of channel row m's
+// run (piece 4m + c, c = 2h + q, at D = 128; 2m + h at D = 64) moves within
+// the row to c ^ f(m), f(m) = 2 b2 + (b1 ^ b3) at D = 128 and b2 ^ b3 at
+// D = 64 (b_i = bit i of m). For every 8 consecutive rows, and for every 16,
+// each piece column then lands in distinct 16-byte bank groups.
 template <int D>
 __device__ inline int lds_v4_piece(int pc) {
-    if constexpr (D == 128) return (pc & ~3) | ((pc & 3) ^ ((pc >> 3) & 3));
-    else return (pc & ~1) | ((pc & 1) ^ ((pc >> 3) & 1));
+    if constexpr (D == 128)
+        return (pc & ~3) | ((pc & 3) ^ ((((pc >> 4) & 1) << 1) | (((pc >> 3) ^ (pc >> 5)) & 1)));
+    else return (pc & ~1) | ((pc & 1) ^ (((pc >> 3) ^ (pc >> 4)) & 1));
 }
 
 // Operands of one chunk from 4-bit tiles kt0/vt0 and kt1/vt1 (blocks 0, 1),
@@ -1309,7 +1314,11 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     const int wave_lo = MASKED ? seq_lowest_key(P, ctx - q_len + wave_row0 / P.G) : 0;
     const int blk_lo = MASKED ? seq_lowest_key(P, ctx - q_len + row0 / P.G) : 0;
 
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * TB];
+    // Staged parts sit PS bytes apart, PS = 128 modulo 256: the K tiles of a
+    // step's two blocks then start 128 bytes apart modulo 256, so that the 16
+    // lanes of one 256-byte LDS cycle that read both blocks hit distinct banks.
+    constexpr int PS = (TB + 255) / 256 * 256 + 128;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * PS];
     // the row state of each wave's tile, touched only at split ends
     __shared__ f32x4_t fin_acc[4][DT][64];
     __shared__ float2 fin_ml[4][64];
@@ -1322,22 +1331,29 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     // step's blocks 0, 1; parts 2, 3 their V. Lane l stages pieces l + 64 v.
     const int blk = wave & 1;
     const bool is_v = wave >= 2;
-    // LDS position of piece pc of the wave's part (see load_step_lds,
-    // load_step8 and load_step4: K token order 0-3, 8-11, 4-7, 12-15; V
-    // pieces of a channel row permuted by the row's bits; scales in place)
-    auto lds_pos = [&](int pc) {
+    // LDS layout of the staged tiles (see load_step_lds, load_step8 and
+    // load_step4): K keeps the token order 0-3, 8-11, 4-7, 12-15 within each
+    // 16-piece chunk, V pieces of a channel row are permuted by the row's
+    // bits, scales stay in place. Staged index i = lane + 64 v: a V part
+    // loads piece i and writes it to its position; a K part writes position
+    // i and loads the piece that belongs there (the token order swaps bits 2
+    // and 3 of the token, so it is its own inverse). Either way each group of
+    // 8 lanes writes 128 contiguous bytes, free of bank conflicts.
+    auto k_piece_at = [&](int i) {
         if constexpr (KF == kKvFp4) {
-            if (pc >= D / 2) return pc;  // scales
-            if constexpr (D == 128)
-                return is_v ? lds_v4_piece<D>(pc) : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
-            else
-                return is_v ? lds_v4_piece<D>(pc) : pc;
-        } else {
-            if (KF == kKvFp8 && pc >= D) return pc;  // scales
-            return is_v ? (pc >> 1) * 2 + lds_v_half(pc >> 1, pc & 1)
-                        : (pc >> 4) * kBlock + lds_k_pos(pc & 15);
+            if (D != 128 || i >= D / 2) return i;  // 8-byte runs in order; scales
+        } else if constexpr (KF == kKvFp8) {
+            if (i >= D) return i;  // scales
         }
+        return (i >> 4) * kBlock + lds_k_pos(i & 15);
     };
+    auto v_pos_of = [&](int i) {
+        if constexpr (KF == kKvFp4) return i >= D / 2 ? i : lds_v4_piece<D>(i);
+        else if constexpr (KF == kKvFp8) return i >= D ? i : (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
+        else return (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
+    };
+    auto src_piece = [&](int i) { return is_v ? i : k_piece_at(i); };
+    auto lds_pos = [&](int i) { return is_v ? v_pos_of(i) : i; };
 
     // Block ids in register windows of 64 blocks (32 steps): lane i of bcur
     // holds table entry 64 bw + i, bnxt the next window, loaded a window
@@ -1364,7 +1380,7 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             if (NP % 64 == 0 || lane + 64 * v < NP)
-                dst[v] = *reinterpret_cast<const u32x4_t *>(src + (size_t)(lane + 64 * v) * 16);
+                dst[v] = *reinterpret_cast<const u32x4_t *>(src + (size_t)src_piece(lane + 64 * v) * 16);
     };
 
     TileState<DT> spl, qtr;
@@ -1380,20 +1396,20 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             if (NP % 64 == 0 || lane + 64 * v < NP)
-                *reinterpret_cast<u32x4_t *>(buf + wave * TB + lds_pos(lane + 64 * v) * 16) = pre[v];
+                *reinterpret_cast<u32x4_t *>(buf + wave * PS + lds_pos(lane + 64 * v) * 16) = pre[v];
         fetch(pre, c + 2);
         __syncthreads();
         if (kc <= wave_pmax && (!MASKED || kc + kStep > wave_lo)) {
             Regs r;
             if constexpr (KF == kKvFp8)
-                load_step8<D>(r, buf, buf + 2 * TB, buf + TB, buf + 3 * TB, g, n, [](int t) { return lds_k_pos(t); },
+                load_step8<D>(r, buf, buf + 2 * PS, buf + PS, buf + 3 * PS, g, n, [](int t) { return lds_k_pos(t); },
                               [](int row, int h) { return lds_v_half(row, h); });
             else if constexpr (KF == kKvFp4)
-                load_step4<D, true>(r, buf, buf + 2 * TB, buf + TB, buf + 3 * TB, g, n);
+                load_step4<D, true>(r, buf, buf + 2 * PS, buf + PS, buf + 3 * PS, g, n);
             else
-                load_step_lds<D>(r, reinterpret_cast<const uint16_t *>(buf), reinterpret_cast<const uint16_t *>(buf + 2 * TB),
-                                 reinterpret_cast<const uint16_t *>(buf + TB),
-                                 reinterpret_cast<const uint16_t *>(buf + 3 * TB), g, n);
+                load_step_lds<D>(r, reinterpret_cast<const uint16_t *>(buf), reinterpret_cast<const uint16_t *>(buf + 2 * PS),
+                                 reinterpret_cast<const uint16_t *>(buf + PS),
+                                 reinterpret_cast<const uint16_t *>(buf + 3 * PS), g, n);
             PoolT::mask(r, kc, ctx, g);
             PoolT::template update<MASKED>(qtr, r, qop, kc, rv, g, P.scale_log2);
         }
