@@ -101,8 +101,9 @@ struct AttnParams {
     // window of `window` keys ending at each row's position.
     const uint32_t *tree_mask;
     int32_t window;
-    // The parallel shape skips sequences with at most min_rows rows (another
-    // launch of it takes them), 0 = none.
+    // The two-tile parallel instance skips sequences with at most min_rows
+    // rows (the one-tile launch takes them), 0 = none. Last, so that it moves
+    // no other field; the one-tile instances never read it.
     int32_t min_rows;
 };
 
@@ -1003,8 +1004,8 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     const int p_max = ctx - q_len + (rows_total - 1) / P.G;
     const int ns_item = min(num_splits(p_max + 1), P.max_splits);
     // (uniform over the workgroup)
-    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT && rows_total > P.min_rows &&
-          p_max >= 0))
+    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT &&
+          (NT == 1 || rows_total > P.min_rows) && p_max >= 0))
         return;
     const int wbase = ctx - q_len;                              // position of the first query row
     const int lo_seq = MASKED ? seq_lowest_key(P, wbase) : 0;  // no row sees a key below it
