@@ -1181,18 +1181,21 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
 }
 
 // ---------------------------------------------------------------------------
-// Split fold of the parallel shape: grid (sequence, KV head, tile); wave w
-// owns the d-tiles w, w + 4, ... of the tile's rows (the fold is elementwise
-// in d) and folds the split states left to right, then finalizes.
+// Split fold of the parallel shape: grid (sequence, KV head, tile x group
+// of four d-tiles); wave w owns d-tile 4 * group + w of the tile's rows (the
+// fold is elementwise in d; every workgroup repeats the same m, l fold) and
+// folds the split states left to right, sixteen loads in flight, then
+// finalizes.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
-    constexpr int DT = D / 16, DW = DT / 4;
-    static_assert(DT % 4 == 0, "head_dim must be a multiple of 64");
+    constexpr int DG = D / 64;  // groups of four d-tiles, one workgroup each
+    static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int g = lane >> 4, n = lane & 15;
-    const int s = blockIdx.x, kvh = blockIdx.y, t = blockIdx.z;
+    const int s = blockIdx.x, kvh = blockIdx.y, t = blockIdx.z / DG;
+    const int dt = (blockIdx.z % DG) * 4 + wave;  // the wave's d-tile
     int q0, q_len;
     if (P.decode_only) {
         q0 = s;
@@ -1207,7 +1210,7 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
     const int rho = min(16 * t + n, rows_total - 1);  // padding lanes repeat a real row and store nothing
     const int r = rho / P.G, hl = rho - r * P.G;
     const size_t base0 = ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * P.max_splits;
-    TileState<DW> acc;
+    TileState<1> acc;
     state_clear(acc);
     // the slots the parallel grid wrote (all, or a sliding window's run)
     int j0 = 0, j1 = P.max_splits;
@@ -1215,10 +1218,10 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
         j0 = split_index(max(P.ctx_lens[s] - q_len - P.window + 1, 0));
         j1 = min(j0 + P.grid_splits, P.max_splits);
     }
-    // eight split states per round trip
-    constexpr int U = 8;
+    // sixteen split states per round trip
+    constexpr int U = 16;
     for (int j = j0; j < j1; j += U) {
-        TileState<DW> x[U];
+        TileState<1> x[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             state_clear(x[u]);
@@ -1226,21 +1229,17 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
                 const float2 ml = P.ws_ml[base0 + j + u];
                 x[u].m = ml.x;
                 x[u].l = ml.y;
-#pragma unroll
-                for (int e = 0; e < DW; ++e)
-                    x[u].acc[e] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j + u) * D +
-                                                                      16 * (wave + 4 * e) + 4 * g);
+                x[u].acc[0] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j + u) * D + 16 * dt + 4 * g);
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) fold_state(acc, x[u]);
     }
     if (16 * t + n >= rows_total) return;
-    f32x4_t o[DW];
+    f32x4_t o[1];
     finalize(acc, sink_log2(P, kvh, hl), o);
     float *dst = P.out + ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * D + 4 * g;
-#pragma unroll
-    for (int e = 0; e < DW; ++e) *reinterpret_cast<f32x4_t *>(dst + 16 * (wave + 4 * e)) = o[e];
+    *reinterpret_cast<f32x4_t *>(dst + 16 * dt) = o[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -2007,7 +2006,7 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
     const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
         launch_parallel<D, 1, KF, MASKED>(P, st);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 1), dim3(256), 0, st, P);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, D / 64), dim3(256), 0, st, P);
     } else if (KF != kKvBf16 && rows_per_seq > kParRows) {
         // A batch with prefill chunks: its sequences of up to 16 rows (decode
         // rows) take the one-tile instance, which holds twice the waves per
@@ -2017,10 +2016,10 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
         AttnParams P2 = P;
         P2.min_rows = 16;
         launch_parallel<D, 2, KF, MASKED>(P2, st);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2 * (D / 64)), dim3(256), 0, st, P);
     } else {
         launch_parallel<D, 2, KF, MASKED>(P, st);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2), dim3(256), 0, st, P);
+        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2 * (D / 64)), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
