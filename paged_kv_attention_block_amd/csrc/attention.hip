@@ -101,10 +101,6 @@ struct AttnParams {
     // window of `window` keys ending at each row's position.
     const uint32_t *tree_mask;
     int32_t window;
-    // The two-tile parallel instance skips sequences with at most min_rows
-    // rows (the one-tile launch takes them), 0 = none. Last, so that it moves
-    // no other field; the one-tile instances never read it.
-    int32_t min_rows;
 };
 
 // A zero (block, head) tile: loads of blocks past the end of a sequence read it.
@@ -966,8 +962,12 @@ struct ParLds {
     float2 ml[3][NT][64];
 };
 
-template <int D, int NT, bool PF, bool APPEND, int KF, bool MASKED>
-__global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnParams P) {
+// TWO: one-tile instances that also take sequences of 17 to 32 rows, in two
+// passes of 16 rows over the same keys (quantized batches with prefill
+// chunks, so that one launch covers decode and verify rows).
+template <int D, int NT, bool PF, bool APPEND, int KF, bool MASKED, bool TWO = false>
+__global__ __launch_bounds__(256, par_waves(D, NT, PF) - (TWO && D == 64 ? 1 : 0)) void attn_parallel(AttnParams P) {
+    constexpr int NPASS = TWO ? 2 : 1;
     using PoolT = Pool<D, KF>;
     using Regs = typename PoolT::Regs;
     constexpr int DT = D / 16, KJ = D / 32;
@@ -1004,8 +1004,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
     const int p_max = ctx - q_len + (rows_total - 1) / P.G;
     const int ns_item = min(num_splits(p_max + 1), P.max_splits);
     // (uniform over the workgroup)
-    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT &&
-          (NT == 1 || rows_total > P.min_rows) && p_max >= 0))
+    if (!(q0 >= 0 && q_len > 0 && q0 + q_len <= P.total_rows && rows_total <= 16 * NT * NPASS && p_max >= 0))
         return;
     const int wbase = ctx - q_len;                              // position of the first query row
     const int lo_seq = MASKED ? seq_lowest_key(P, wbase) : 0;  // no row sees a key below it
@@ -1014,7 +1013,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
         // fold reads every slot without first learning the context length.
         if (wave == 0) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
+            for (int t = 0; t < NT * NPASS; ++t) {
                 const int rho = 16 * t + n;
                 if (g != 0 || rho >= rows_total) continue;
                 const int r = rho / P.G, hl = rho - r * P.G;
@@ -1023,160 +1022,168 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF)) void attn_parallel(AttnP
         }
         return;
     }
-    RowInfo ri[NT];
-    RowVis rv[NT];
-    u32x4_t qop[NT][KJ];
-    TileState<DT> st[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        state_clear(st[t]);
-        ri[t] = row_info(16 * t + n, rows_total, P.G, ctx, q_len);
-        rv[t] = row_vis<MASKED>(P, ri[t], q0, wbase);
-    }
-    {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) load_q<D>(qop[t], P, q0, ri[t], kvh, g);
-        const int kq1 = min(kq0 + ql, p_max + 1);
-        bid = (lane < ql / kBlock && jb < (ctx + kBlock - 1) / kBlock && jb < P.max_blocks_per_seq && bid >= 0 &&
-               bid < P.num_blocks)
-                  ? bid
-                  : -1;
-        // appending decode step: the wave whose quarter holds the new key
-        const int pn = ctx - 1;
-        const bool fused = APPEND && KF == kKvBf16 && kq0 <= pn && pn < kq1;
-        // The new token's K and V rows wait in LDS (this wave's slot) for the
-        // step that holds pn, rather than in registers through the loop.
-        __shared__ __attribute__((aligned(16))) uint16_t s_new[APPEND ? 4 : 1][2][D];
-        if (APPEND && KF == kKvBf16 && fused) {
-            const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
-            const int slot = P.slots[s];
-            if (lane < D / 8) {
-                const u32x4_t kq = *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + lane * 8);
-                *reinterpret_cast<u32x4_t *>(&s_new[wave][0][lane * 8]) = kq;
-                *reinterpret_cast<u32x4_t *>(&s_new[wave][1][lane * 8]) =
-                    *reinterpret_cast<const u32x4_t *>(P.v_new + rowoff + lane * 8);
-                // and writes it to its pool slot, as the scatter-write would
-                if (slot >= 0 && slot < P.num_blocks * kBlock) {
-                    const size_t tb = ((size_t)(slot / kBlock) * P.Hkv + kvh) * D;  // element offset of the tile
-                    *reinterpret_cast<u32x4_t *>(P.kp_w + tb * kBlock + ((size_t)lane * kBlock + slot % kBlock) * 8) =
-                        kq;
-                }
-            }
-            if (slot >= 0 && slot < P.num_blocks * kBlock) {
-                const size_t tb = ((size_t)(slot / kBlock) * P.Hkv + kvh) * D;
-#pragma unroll
-                for (int c = lane; c < D; c += 64)
-                    P.vp_w[tb * kBlock + (size_t)c * kBlock + slot % kBlock] = P.v_new[rowoff + c];
-            }
-        }
-        const size_t tile = PoolT::tile_bytes;
-        const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * tile;
-        const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * tile;
-        const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_zero_tile);
-        const size_t bstride = (size_t)P.Hkv * tile;
-        // Step at key kc; lanes past the quarter's blocks hold -1, so a fetch
-        // one step past the end reads the zero tile.
-        auto fetch = [&](Regs &r, int kc) {
-            const int li = (kc - kq0) / kBlock;
-            const int b0 = __builtin_amdgcn_readlane(bid, li);
-            const int b1 = __builtin_amdgcn_readlane(bid, li + 1);
-            PoolT::load(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : zero, b0 >= 0 ? vbase + (size_t)b0 * bstride : zero,
-                        b1 >= 0 ? kbase + (size_t)b1 * bstride : zero, b1 >= 0 ? vbase + (size_t)b1 * bstride : zero,
-                        g, n);
-        };
-        auto compute = [&](Regs &r, int kc) {
-            if constexpr (APPEND && KF == kKvBf16) {
-                if (fused && kc <= pn && pn < kc + kStep) {
-                    // LDS operations of one wave complete in order: the rows
-                    // written above are there
-                    u32x4_t knew[KJ];
-                    uint32_t vnew[DT];
-#pragma unroll
-                    for (int jj = 0; jj < KJ; ++jj)
-                        knew[jj] = *reinterpret_cast<const u32x4_t *>(&s_new[wave][0][(4 * jj + g) * 8]);
-#pragma unroll
-                    for (int dt = 0; dt < DT; ++dt) vnew[dt] = s_new[wave][1][16 * dt + n];
-                    patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
-                }
-            }
-            PoolT::mask(r, kc, ctx, g);
-            if constexpr (NT == 2) {
-                if (rows_total > 16)  // uniform: both tiles in one pass over the operands
-                    PoolT::template update2<MASKED>(st, r, qop, kc, rv, g, P.scale_log2);
-                else
-                    PoolT::template update<MASKED>(st[0], r, qop[0], kc, rv[0], g, P.scale_log2);
-            } else {
-#pragma unroll
-                for (int t = 0; t < NT; ++t)
-                    if (16 * t < rows_total)
-                        PoolT::template update<MASKED>(st[t], r, qop[t], kc, rv[t], g, P.scale_log2);
-            }
-        };
-        // Steps wholly below every row's lowest visible key change no state:
-        // the wave starts at the step holding lo_seq.
-        const int kstart = (MASKED && lo_seq > kq0) ? kq0 + (lo_seq - kq0) / kStep * kStep : kq0;
-        if constexpr (PF) {
-            // Two register stages, each refilled as soon as it is consumed,
-            // so that two steps are in flight; unrolled so that each stage
-            // keeps fixed registers (a copy between stages would wait for the
-            // loads it copies).
-            Regs r0, r1;
-            if (!MASKED || kstart < kq1) fetch(r0, kstart);
-            if (kstart + kStep < kq1) fetch(r1, kstart + kStep);
-            for (int kc = kstart; kc < kq1; kc += 2 * kStep) {
-                compute(r0, kc);
-                if (kc + 2 * kStep < kq1) fetch(r0, kc + 2 * kStep);
-                if (kc + kStep < kq1) {
-                    compute(r1, kc + kStep);
-                    if (kc + 3 * kStep < kq1) fetch(r1, kc + 3 * kStep);
-                }
-            }
-        } else {
-            for (int kc = kstart; kc < kq1; kc += kStep) {
-                Regs r;
-                fetch(r, kc);
-                compute(r, kc);
-            }
-        }
-    }
-    __shared__ ParLds<D, NT> lds;
-    if (wave > 0) {
+    for (int pass = 0; pass < NPASS; ++pass) {
+        if (TWO && 16 * NT * pass >= rows_total) break;  // uniform
+        RowInfo ri[NT];
+        RowVis rv[NT];
+        u32x4_t qop[NT][KJ];
+        TileState<DT> st[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            lds.ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) lds.acc[wave - 1][t][dt][lane] = st[t].acc[dt];
+            state_clear(st[t]);
+            ri[t] = row_info(16 * (NT * pass + t) + n, rows_total, P.G, ctx, q_len);
+            rv[t] = row_vis<MASKED>(P, ri[t], q0, wbase);
         }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    // quarter states -> split state (left fold in quarter order); with one
-    // split slot there is no fold launch and the rows are finished here
-    const bool whole = P.max_splits == 1;
+        {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        if (ri[t].prow < 0) continue;
+            for (int t = 0; t < NT; ++t) load_q<D>(qop[t], P, q0, ri[t], kvh, g);
+            const int kq1 = min(kq0 + ql, p_max + 1);
+            bid = (lane < ql / kBlock && jb < (ctx + kBlock - 1) / kBlock && jb < P.max_blocks_per_seq && bid >= 0 &&
+                   bid < P.num_blocks)
+                      ? bid
+                      : -1;
+            // appending decode step: the wave whose quarter holds the new key
+            const int pn = ctx - 1;
+            const bool fused = APPEND && KF == kKvBf16 && kq0 <= pn && pn < kq1;
+            // The new token's K and V rows wait in LDS (this wave's slot) for the
+            // step that holds pn, rather than in registers through the loop.
+            __shared__ __attribute__((aligned(16))) uint16_t s_new[APPEND ? 4 : 1][2][D];
+            if (APPEND && KF == kKvBf16 && fused) {
+                const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
+                const int slot = P.slots[s];
+                if (lane < D / 8) {
+                    const u32x4_t kq = *reinterpret_cast<const u32x4_t *>(P.k_new + rowoff + lane * 8);
+                    *reinterpret_cast<u32x4_t *>(&s_new[wave][0][lane * 8]) = kq;
+                    *reinterpret_cast<u32x4_t *>(&s_new[wave][1][lane * 8]) =
+                        *reinterpret_cast<const u32x4_t *>(P.v_new + rowoff + lane * 8);
+                    // and writes it to its pool slot, as the scatter-write would
+                    if (slot >= 0 && slot < P.num_blocks * kBlock) {
+                        const size_t tb = ((size_t)(slot / kBlock) * P.Hkv + kvh) * D;  // element offset of the tile
+                        *reinterpret_cast<u32x4_t *>(P.kp_w + tb * kBlock + ((size_t)lane * kBlock + slot % kBlock) * 8) =
+                            kq;
+                    }
+                }
+                if (slot >= 0 && slot < P.num_blocks * kBlock) {
+                    const size_t tb = ((size_t)(slot / kBlock) * P.Hkv + kvh) * D;
 #pragma unroll
-        for (int w = 0; w < 3; ++w) {
-            TileState<DT> o;
-            const float2 ml = lds.ml[w][t][lane];
-            o.m = ml.x;
-            o.l = ml.y;
+                    for (int c = lane; c < D; c += 64)
+                        P.vp_w[tb * kBlock + (size_t)c * kBlock + slot % kBlock] = P.v_new[rowoff + c];
+                }
+            }
+            const size_t tile = PoolT::tile_bytes;
+            const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * tile;
+            const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * tile;
+            const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_zero_tile);
+            const size_t bstride = (size_t)P.Hkv * tile;
+            // Step at key kc; lanes past the quarter's blocks hold -1, so a fetch
+            // one step past the end reads the zero tile.
+            auto fetch = [&](Regs &r, int kc) {
+                const int li = (kc - kq0) / kBlock;
+                const int b0 = __builtin_amdgcn_readlane(bid, li);
+                const int b1 = __builtin_amdgcn_readlane(bid, li + 1);
+                PoolT::load(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : zero, b0 >= 0 ? vbase + (size_t)b0 * bstride : zero,
+                            b1 >= 0 ? kbase + (size_t)b1 * bstride : zero, b1 >= 0 ? vbase + (size_t)b1 * bstride : zero,
+                            g, n);
+            };
+            auto compute = [&](Regs &r, int kc) {
+                if constexpr (APPEND && KF == kKvBf16) {
+                    if (fused && kc <= pn && pn < kc + kStep) {
+                        // LDS operations of one wave complete in order: the rows
+                        // written above are there
+                        u32x4_t knew[KJ];
+                        uint32_t vnew[DT];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds.acc[w][t][dt][lane];
-            fold_state(st[t], o);
+                        for (int jj = 0; jj < KJ; ++jj)
+                            knew[jj] = *reinterpret_cast<const u32x4_t *>(&s_new[wave][0][(4 * jj + g) * 8]);
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) vnew[dt] = s_new[wave][1][16 * dt + n];
+                        patch_new_key<D>(r, knew, vnew, kc, pn, g, n);
+                    }
+                }
+                PoolT::mask(r, kc, ctx, g);
+                if constexpr (NT == 2) {
+                    if (rows_total > 16)  // uniform: both tiles in one pass over the operands
+                        PoolT::template update2<MASKED>(st, r, qop, kc, rv, g, P.scale_log2);
+                    else
+                        PoolT::template update<MASKED>(st[0], r, qop[0], kc, rv[0], g, P.scale_log2);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        if (16 * t < rows_total)
+                            PoolT::template update<MASKED>(st[t], r, qop[t], kc, rv[t], g, P.scale_log2);
+                }
+            };
+            // Steps wholly below every row's lowest visible key change no state:
+            // the wave starts at the step holding lo_seq.
+            const int kstart = (MASKED && lo_seq > kq0) ? kq0 + (lo_seq - kq0) / kStep * kStep : kq0;
+            if constexpr (PF) {
+                // Two register stages, each refilled as soon as it is consumed,
+                // so that two steps are in flight; unrolled so that each stage
+                // keeps fixed registers (a copy between stages would wait for the
+                // loads it copies).
+                Regs r0, r1;
+                if (!MASKED || kstart < kq1) fetch(r0, kstart);
+                if (kstart + kStep < kq1) fetch(r1, kstart + kStep);
+                for (int kc = kstart; kc < kq1; kc += 2 * kStep) {
+                    compute(r0, kc);
+                    if (kc + 2 * kStep < kq1) fetch(r0, kc + 2 * kStep);
+                    if (kc + kStep < kq1) {
+                        compute(r1, kc + kStep);
+                        if (kc + 3 * kStep < kq1) fetch(r1, kc + 3 * kStep);
+                    }
+                }
+            } else {
+                for (int kc = kstart; kc < kq1; kc += kStep) {
+                    Regs r;
+                    fetch(r, kc);
+                    compute(r, kc);
+                }
+            }
         }
-        if (whole) {
-            f32x4_t o[DT];
-            finalize(st[t], sink_log2(P, kvh, ri[t].hl), o);
-            store_out<DT>(P, q0, ri[t], kvh, g, o);
-        } else {
-            const size_t base = ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + j;
-            if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
+        __shared__ ParLds<D, NT> lds;
+        if (wave > 0) {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
+            for (int t = 0; t < NT; ++t) {
+                lds.ml[wave - 1][t][lane] = make_float2(st[t].m, st[t].l);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lds.acc[wave - 1][t][dt][lane] = st[t].acc[dt];
+            }
         }
+        __syncthreads();
+        if (wave != 0) {
+            if constexpr (!TWO) return;
+            __syncthreads();  // wave 0 has read the LDS states before the next pass writes them
+            continue;
+        }
+        // quarter states -> split state (left fold in quarter order); with one
+        // split slot there is no fold launch and the rows are finished here
+        const bool whole = P.max_splits == 1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (ri[t].prow < 0) continue;
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                TileState<DT> o;
+                const float2 ml = lds.ml[w][t][lane];
+                o.m = ml.x;
+                o.l = ml.y;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds.acc[w][t][dt][lane];
+                fold_state(st[t], o);
+            }
+            if (whole) {
+                f32x4_t o[DT];
+                finalize(st[t], sink_log2(P, kvh, ri[t].hl), o);
+                store_out<DT>(P, q0, ri[t], kvh, g, o);
+            } else {
+                const size_t base = ((size_t)(q0 + ri[t].r) * P.Hq + kvh * P.G + ri[t].hl) * P.max_splits + j;
+                if (g == 0) P.ws_ml[base] = make_float2(st[t].m, st[t].l);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st[t].acc[dt];
+            }
+        }
+        if constexpr (TWO) __syncthreads();
     }
 }
 
@@ -2007,18 +2014,21 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
     if (rows_per_seq <= 16) {
         launch_parallel<D, 1, KF, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, D / 64), dim3(256), 0, st, P);
-    } else if (KF != kKvBf16 && rows_per_seq > kParRows) {
-        // A batch with prefill chunks: its sequences of up to 16 rows (decode
-        // rows) take the one-tile instance, which holds twice the waves per
-        // SIMD for quantized tiles (measured 14 % faster on a mixed step), and
-        // the two-tile instance takes those of 17 to 32 rows.
-        launch_parallel<D, 1, KF, MASKED>(P, st);
-        AttnParams P2 = P;
-        P2.min_rows = 16;
-        launch_parallel<D, 2, KF, MASKED>(P2, st);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2 * (D / 64)), dim3(256), 0, st, P);
     } else {
-        launch_parallel<D, 2, KF, MASKED>(P, st);
+        bool done = false;
+        if constexpr (KF != kKvBf16) {
+            if (rows_per_seq > kParRows) {
+                // A batch with prefill chunks: the one-tile instance, which
+                // holds twice the waves per SIMD for quantized tiles (measured
+                // 14 % faster on a mixed step), takes its decode rows, and
+                // sequences of 17 to 32 rows in two passes, in one launch.
+                const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.grid_splits;
+                hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, MASKED, true>), dim3((unsigned)nwg), dim3(256),
+                                   0, st, P);
+                done = true;
+            }
+        }
+        if (!done) launch_parallel<D, 2, KF, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2 * (D / 64)), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
@@ -2148,7 +2158,6 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     P.kp_w = P.vp_w = nullptr;
     P.tree_mask = mk ? mk->tree_mask : nullptr;
     P.window = mk ? mk->window : 0;
-    P.min_rows = 0;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
 
     if (app) {
