@@ -22,12 +22,14 @@
 //    enters the PV product as a hi + lo pair of bf16 values;
 //  * the four quarter states fold left to right into a split state, the split
 //    states fold left to right into the row state (fold_state), and the sink
-//    and the one division come last (finalize);
+//    and the one division come last (finalize), which writes +0 for every
+//    zero output;
 //  * fp32: one wave per (row, head), one online state over all keys in order.
 // Two bf16 launch shapes compute exactly that: "parallel" (one workgroup per
 // split, a wave per quarter, then a fold launch over the split states) for
 // decode and verify rows, and "sequential" (one workgroup per 64 rows walking
-// every split, folds kept in registers) for prefill chunks.
+// every split: quarter and split states in registers, the row state in LDS)
+// for prefill chunks.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -618,11 +620,9 @@ __device__ inline void mask_tail8(StepRegs8<D> &r, int kc, int ctx, int g) {
     }
 }
 
-template <int D, bool MASKED>
-__device__ inline void step_update8x2(TileState<D / 16> (&st)[2], const StepRegs8<D> &r,
-                                      const u32x4_t (&qop)[2][D / 32], int kc, const RowVis (&rv)[2], int g,
-                                      float scale_log2) {
-    float ksc[8], vsc[8];
+// The K and V scales of the lane's eight keys (8- and 4-bit operands).
+template <class R>
+__device__ inline void step_scales(const R &r, float (&ksc)[8], float (&vsc)[8]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         ksc[i] = r.ks[0][i];
@@ -630,6 +630,14 @@ __device__ inline void step_update8x2(TileState<D / 16> (&st)[2], const StepRegs
         vsc[i] = r.vs[0][i];
         vsc[4 + i] = r.vs[1][i];
     }
+}
+
+template <int D, bool MASKED>
+__device__ inline void step_update8x2(TileState<D / 16> (&st)[2], const StepRegs8<D> &r,
+                                      const u32x4_t (&qop)[2][D / 32], int kc, const RowVis (&rv)[2], int g,
+                                      float scale_log2) {
+    float ksc[8], vsc[8];
+    step_scales(r, ksc, vsc);
     step_core2<D, true, MASKED>(
         st,
         [&](int tau, int j) {
@@ -647,13 +655,7 @@ template <int D, bool MASKED>
 __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r, const u32x4_t (&qop)[D / 32],
                                     int kc, const RowVis &rv, int g, float scale_log2) {
     float ksc[8], vsc[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ksc[i] = r.ks[0][i];
-        ksc[4 + i] = r.ks[1][i];
-        vsc[i] = r.vs[0][i];
-        vsc[4 + i] = r.vs[1][i];
-    }
+    step_scales(r, ksc, vsc);
     step_core<D, true, MASKED>(
         st,
         [&](int tau, int j) {
@@ -815,22 +817,11 @@ __device__ inline void mask_tail4(StepRegs4<D> &r, int kc, int ctx, int g) {
     }
 }
 
-template <int D>
-__device__ inline void scales4(const StepRegs4<D> &r, float (&ksc)[8], float (&vsc)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ksc[i] = r.ks[0][i];
-        ksc[4 + i] = r.ks[1][i];
-        vsc[i] = r.vs[0][i];
-        vsc[4 + i] = r.vs[1][i];
-    }
-}
-
 template <int D, bool MASKED>
 __device__ inline void step_update4(TileState<D / 16> &st, const StepRegs4<D> &r, const u32x4_t (&qop)[D / 32],
                                     int kc, const RowVis &rv, int g, float scale_log2) {
     float ksc[8], vsc[8];
-    scales4<D>(r, ksc, vsc);
+    step_scales(r, ksc, vsc);
     step_core<D, true, MASKED>(
         st, [&](int tau, int j) { return fp4x8_to_bf16(r.k[tau][j]); }, [&](int dt) { return fp4x8_to_bf16(r.v[dt]); },
         ksc, vsc, qop, kc, rv, g, scale_log2);
@@ -841,7 +832,7 @@ __device__ inline void step_update4x2(TileState<D / 16> (&st)[2], const StepRegs
                                       const u32x4_t (&qop)[2][D / 32], int kc, const RowVis (&rv)[2], int g,
                                       float scale_log2) {
     float ksc[8], vsc[8];
-    scales4<D>(r, ksc, vsc);
+    step_scales(r, ksc, vsc);
     step_core2<D, true, MASKED>(
         st, [&](int tau, int j) { return fp4x8_to_bf16(r.k[tau][j]); }, [&](int dt) { return fp4x8_to_bf16(r.v[dt]); },
         ksc, vsc, qop, kc, rv, g, scale_log2);
@@ -1288,7 +1279,7 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
 
 // Two workgroups per CU (the LDS staging allows no more): bounding the
 // registers to that occupancy keeps the MFMA accumulators in VGPRs, where the
-// per-step rescale and select use them without copies.
+// per-step rescale and MFMA accumulation use them without copies.
 template <int D, int KF, bool MASKED>
 __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     using PoolT = Pool<D, KF>;
