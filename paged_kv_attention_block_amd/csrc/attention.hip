@@ -388,12 +388,18 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (SCALED) {
-            sc[i] = vis(i) ? (s0[i] * ksc[i]) * scale_log2 : -INFINITY;
-            sc[4 + i] = vis(i + 4) ? (s1[i] * ksc[4 + i]) * scale_log2 : -INFINITY;
+            sc[i] = (s0[i] * ksc[i]) * scale_log2;
+            sc[4 + i] = (s1[i] * ksc[4 + i]) * scale_log2;
         } else {
-            sc[i] = vis(i) ? s0[i] * scale_log2 : -INFINITY;
-            sc[4 + i] = vis(i + 4) ? s1[i] * scale_log2 : -INFINITY;
+            sc[i] = s0[i] * scale_log2;
+            sc[4 + i] = s1[i] * scale_log2;
         }
+    }
+    // Masking only in steps where some lane does not see all its keys (the
+    // diagonal, the tail, a window or tree edge); elsewhere it changes nothing.
+    if (!__all(MASKED ? vm == 0xFFu : lim >= 7)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sc[i] = vis(i) ? sc[i] : -INFINITY;
     }
     const float mx =
         row_max4(fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))));
@@ -470,12 +476,16 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (SCALED) {
-                sc[i] = vis(i) ? (s0[t][i] * ksc[i]) * scale_log2 : -INFINITY;
-                sc[4 + i] = vis(i + 4) ? (s1[t][i] * ksc[4 + i]) * scale_log2 : -INFINITY;
+                sc[i] = (s0[t][i] * ksc[i]) * scale_log2;
+                sc[4 + i] = (s1[t][i] * ksc[4 + i]) * scale_log2;
             } else {
-                sc[i] = vis(i) ? s0[t][i] * scale_log2 : -INFINITY;
-                sc[4 + i] = vis(i + 4) ? s1[t][i] * scale_log2 : -INFINITY;
+                sc[i] = s0[t][i] * scale_log2;
+                sc[4 + i] = s1[t][i] * scale_log2;
             }
+        }
+        if (!__all(MASKED ? vm == 0xFFu : lim >= 7)) {  // as in step_core
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sc[i] = vis(i) ? sc[i] : -INFINITY;
         }
         const float mx = row_max4(
             fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7]))));
