@@ -64,6 +64,21 @@ def test_window_rows_equal_rows_alone(pk, dtype, Hq, Hkv, D):
         np.testing.assert_array_equal(got[0], full[i], err_msg=f"row {i}")
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "fp4"])
+def test_quantized_mixed_batch_rows_equal_rows_alone(pk, dtype):
+    """8- and 4-bit batches with a prefill chunk take a one-tile split launch
+    that covers windows of 17-32 rows in two passes: those rows, the decode
+    rows and the prefill rows each equal themselves alone."""
+    from paged_kv_attention_block_amd.staging import stage
+    # Hq/Hkv = 4: windows of 5 and 8 rows are 20 and 32 rows per KV head
+    w = custom(dtype, 16, 4, 128, [2600, 1300, 900, 5000], [5, 300, 1, 8], seed=99, sinks=True)
+    announce(f"quantized mixed-batch invariance {dtype}")
+    st = stage(w)
+    full = bits(run_forward(pk, st, w))
+    for i in [0, 2, 4, 5, 6, 150, 304, 305, 306, 308, 312]:
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i}")
+
+
 def test_prefill_rows_equal_rows_alone(pk):
     from paged_kv_attention_block_amd.staging import stage
     w = custom("bf16", 16, 4, 128, [1500, 300], [200, 300], seed=95, sinks=True)
