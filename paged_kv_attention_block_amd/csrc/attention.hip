@@ -90,7 +90,9 @@ struct AttnParams {
     // visible key on (no more can hold a visible key)
     int32_t grid_splits;
     int32_t decode_only;  // every sequence has q_len == 1 (rows packed in sequence order)
-    int32_t seq_stride;   // sequence slots per split slot in the parallel grid (>= num_seqs)
+    // sequence slots per split slot in the parallel grid (>= num_seqs), or 0:
+    // the grid is dealt in the balanced order of balanced_item
+    int32_t seq_stride;
     float scale_log2;
     // Appending decode step (paged_attention_append_forward), else all null:
     // row s's own token sits at position ctx - 1; its K/V rows, and the pool
@@ -936,7 +938,7 @@ __device__ inline void store_out(const AttnParams &P, int q0, const RowInfo &ri,
 // Parallel shape: one workgroup per (KV head, sequence, split), in a flat
 // grid whose fastest index is the KV head and whose split slots run the
 // 1024-key splits before the 256-key ones, so that short workgroups fill the
-// end. 4 waves; wave w streams quarter w of the split in 32-key steps for all
+// end (decode batches whose grid queues: the balanced order below). 4 waves; wave w streams quarter w of the split in 32-key steps for all
 // NT tiles (up to 16 NT rows per sequence and KV head). The quarter states
 // meet in LDS and wave 0 folds them in order. A sequence whose rows see one
 // split only is finished here; otherwise the split state goes to the
@@ -947,6 +949,73 @@ __device__ inline void store_out(const AttnParams &P, int q0, const RowInfo &ri,
 __device__ inline int split_of_slot(int z, int max_splits) {
     if (max_splits <= kSplitsA) return z;
     return z + kSplitsA < max_splits ? z + kSplitsA : z - (max_splits - kSplitsA);
+}
+
+// Balanced order (decode batches whose grid queues: at most 64 sequences,
+// max_splits below 1024, no restricted visibility). The dispatcher deals a
+// die's workgroups to its shader engines in turn, by count; a slot order
+// fixed in advance hands some engines more keys than others, and slots of
+// splits a sequence does not have still take their turn among the busy
+// ones. Here every workgroup reads the batch's context lengths (lane l:
+// sequence l) and ranks the items by class: the full 1024-key splits (in
+// sequence order; a split-major order measured 7-10 % slower), then each
+// sequence's partial last split, then the full 256-key splits, then the
+// slots past each sequence's splits (which only record an empty state for
+// the fold), so that neighbours in dispatch order carry about the same
+// number of keys and the short items come last. The price is a round trip:
+// the block ids wait for the context lengths. Returns false for a slot past
+// all of them. The item computed is the same whichever workgroup takes it.
+__device__ inline bool balanced_item(const AttnParams &P, int rank, int cap_rows, int lane, int &s, int &j, int &ctx,
+                                     int &qa, int &qb) {
+    const bool in = lane < P.num_seqs;
+    const int c = in ? P.ctx_lens[lane] : 0;
+    const int a = P.decode_only ? lane : (in ? P.qsl[lane] : 0);
+    const int b = P.decode_only ? lane + 1 : (in ? P.qsl[lane + 1] : 0);
+    const int ql = b - a, rows = ql * P.G;
+    const int pmax = c - ql + (rows - 1) / P.G;
+    // the sequences the parallel shape takes (the same test as its items')
+    const bool ok = in && a >= 0 && ql > 0 && b <= P.total_rows && rows <= cap_rows && pmax >= 0;
+    const int ns = ok ? min(num_splits(pmax + 1), P.max_splits) : 0;
+    const int part = ns > 0 && split_begin(ns) > pmax + 1;  // its last split is partial
+    const int nA = max(ns - kSplitsA, 0) - (part && ns > kSplitsA ? 1 : 0);
+    const int nB = min(ns, kSplitsA) - (part && ns <= kSplitsA ? 1 : 0);
+    const int nE = ok ? P.max_splits - ns : 0;
+    // inclusive scans over the lanes, two 16-bit counts per word
+    const int v0 = nA | (nE << 16), v1 = part | (nB << 16);
+    int i0 = v0, i1 = v1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u0 = __shfl_up(i0, o, 64), u1 = __shfl_up(i1, o, 64);
+        if (lane >= o) {
+            i0 += u0;
+            i1 += u1;
+        }
+    }
+    const int t0 = __builtin_amdgcn_readlane(i0, 63), t1 = __builtin_amdgcn_readlane(i1, 63);
+    const int NA = t0 & 0xffff, NE = t0 >> 16, NP = t1 & 0xffff, NB = t1 >> 16;
+    int r = rank, cls, hi, cnt;
+    if (r < NA) {
+        cls = 0, hi = i0 & 0xffff, cnt = nA;
+    } else if ((r -= NA) < NP) {
+        cls = 1, hi = i1 & 0xffff, cnt = part;
+    } else if ((r -= NP) < NB) {
+        cls = 2, hi = i1 >> 16, cnt = nB;
+    } else if ((r -= NB) < NE) {
+        cls = 3, hi = i0 >> 16, cnt = nE;
+    } else {
+        return false;
+    }
+    const unsigned long long hit = __ballot(cnt > 0 && hi - cnt <= r && r < hi);  // one lane
+    if (!hit) return false;
+    const int l = __ffsll((long long)hit) - 1;
+    const int off = r - __builtin_amdgcn_readlane(hi - cnt, l);
+    const int ns_l = __builtin_amdgcn_readlane(ns, l);
+    s = l;
+    j = cls == 0 ? kSplitsA + off : cls == 1 ? ns_l - 1 : cls == 2 ? off : ns_l + off;
+    ctx = __builtin_amdgcn_readlane(c, l);
+    qa = __builtin_amdgcn_readlane(a, l);
+    qb = __builtin_amdgcn_readlane(b, l);
+    return true;
 }
 
 // Waves per SIMD the parallel shape is built for: the register budget that
@@ -977,22 +1046,28 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - (TWO && D == 64 ? 1 : 0
     const int g = lane >> 4, n = lane & 15;
     const int kvh = blockIdx.x % P.Hkv;
     const int rest = blockIdx.x / P.Hkv;
-    const int s = rest % P.seq_stride;
-    int j = split_of_slot(rest / P.seq_stride, P.max_splits);
-    if (s >= P.num_seqs) return;  // padding slot
-
-    // Loads that need nothing but the grid position go out together: the context
-    // length, the row offsets, and the block ids of the wave's quarter
-    // [kq0, kq0 + ql), lane i holding block kq0/16 + i.
-    // (no branches among them, so that none waits for another)
-    const int ctx = P.ctx_lens[s];
-    const int qa = P.qsl[s], qb = P.qsl[s + 1];
+    int s, j, ctx, qa, qb;
+    if (!MASKED && P.seq_stride == 0) {
+        if (!balanced_item(P, rest, 16 * NT * NPASS, lane, s, j, ctx, qa, qb)) return;
+    } else {
+        s = rest % P.seq_stride;
+        j = split_of_slot(rest / P.seq_stride, P.max_splits);
+        if (s >= P.num_seqs) return;  // padding slot
+        // Loads that need nothing but the grid position go out together: the
+        // context length, the row offsets, and the block ids of the wave's
+        // quarter (below). (no branches among them, so that none waits for another)
+        ctx = P.ctx_lens[s];
+        qa = P.qsl[s];
+        qb = P.qsl[s + 1];
+    }
     if constexpr (MASKED) {
         if (P.grid_splits < P.max_splits) {  // grid slot z: the z-th split from the lowest visible key's
             j = split_index(max(ctx - (P.decode_only ? 1 : qb - qa) - P.window + 1, 0)) + rest / P.seq_stride;
             if (j >= P.max_splits) return;
         }
     }
+    // the block ids of the wave's quarter [kq0, kq0 + ql), lane i holding
+    // block kq0/16 + i
     const int ks = split_begin(j);
     const int ql = (split_begin(j + 1) - ks) >> 2;
     const int kq0 = ks + wave * ql;
@@ -1983,9 +2058,14 @@ static int device_cus() {
     return cus;
 }
 
+// workgroups of the parallel grid
+static int64_t par_grid(const AttnParams &P) {
+    return (int64_t)P.Hkv * (P.seq_stride ? P.seq_stride : P.num_seqs) * P.grid_splits;
+}
+
 template <int D, int NT, bool APPEND, int KF, bool MASKED>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
-    const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.grid_splits;
+    const int64_t nwg = par_grid(P);
     // Two prefetch stages: always for bf16 single tiles (measured 3 % faster on
     // large decode grids); for 8- and 4-bit tiles, whose conversions need the
     // registers, only on grids that leave CUs free.
@@ -2023,7 +2103,7 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
                 // holds twice the waves per SIMD for quantized tiles (measured
                 // 14 % faster on a mixed step), takes its decode rows, and
                 // sequences of 17 to 32 rows in two passes, in one launch.
-                const int64_t nwg = (int64_t)P.Hkv * P.seq_stride * P.grid_splits;
+                const int64_t nwg = par_grid(P);
                 hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, MASKED, true>), dim3((unsigned)nwg), dim3(256),
                                    0, st, P);
                 done = true;
@@ -2141,9 +2221,11 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     P.max_splits = max_splits;
     P.decode_only = max_q_len == 1 && total_q_rows == num_seqs;
     // The dispatcher deals workgroups to the shader engines of a die in turn,
-    // by count, not by work. A sequence stride of 1 mod 4 (padding slots exit
-    // at once) moves each sequence to the next engine at every split slot,
-    // so that no engine gets all the splits of the same long sequences.
+    // by count, not by work. A grid that queues takes the balanced order of
+    // balanced_item where it applies; otherwise a sequence stride of 1 mod 4
+    // (padding slots exit at once) moves each sequence to the next engine at
+    // every split slot, so that no engine gets all the splits of the same
+    // long sequences.
     // Under a sliding window, the keys some row of a sequence sees span at most
     // window + max_q_len - 1 positions, which meet at most that many keys / 256
     // (rounded up) + 1 splits.
@@ -2152,7 +2234,13 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
         P.grid_splits = (int32_t)std::min<int64_t>(
             max_splits, ((int64_t)mk->window + max_q_len - 1 + kSplitA - 1) / kSplitA + 1);
     P.seq_stride = num_seqs;
-    if ((int64_t)num_kv_heads * num_seqs * P.grid_splits > device_cus()) P.seq_stride += (5 - num_seqs % 4) % 4;
+    if ((int64_t)num_kv_heads * num_seqs * P.grid_splits > device_cus()) {
+        // (measured: decode batches gain 2-5 %; batches with longer windows,
+        // whose items are alike, lose up to 3 % to the extra round trip)
+        const bool restricted = mk && (mk->tree_mask || mk->window > 0);
+        if (P.decode_only && !restricted && num_seqs <= 64 && max_splits < 1024) P.seq_stride = 0;
+        else P.seq_stride += (5 - num_seqs % 4) % 4;
+    }
     P.scale_log2 = scale * kLog2e;
     P.k_new = P.v_new = nullptr;
     P.slots = nullptr;

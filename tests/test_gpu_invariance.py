@@ -145,3 +145,32 @@ def test_run_to_run_determinism(pk):
     a = bits(run_forward(pk, st, w)).copy()
     for _ in range(3):
         np.testing.assert_array_equal(bits(run_forward(pk, st, w)), a)
+
+
+@pytest.mark.parametrize("dtype,S,D,maxctx", [("bf16", 40, 128, 6000), ("bf16", 64, 64, 6000), ("bf16", 65, 64, 6000),
+                                              ("fp8", 64, 64, 2500), ("fp4", 48, 64, 2500)])
+def test_decode_batch_dispatch_orders(pk, dtype, S, D, maxctx):
+    """Decode batches large enough that workgroups queue are dealt in an order
+    computed from the context lengths (up to 64 sequences; 65 take the fixed
+    slot order): split-aligned lengths, one-key last splits, contexts below
+    one large split and long ones. Every row matches the oracle and equals
+    itself alone (a grid too small to queue, in the fixed order)."""
+    from gpu_util import TOL, max_err, oracle_side
+    from paged_kv_attention_block_amd.staging import stage
+    rng = np.random.default_rng(300 + S + D)
+    edge = [c for c in [1, 2, 255, 256, 257, 1023, 1024, 1025, 2048, 2049, 3072, 4096, 5000] if c <= maxctx]
+    ctxs = (edge + [int(x) for x in rng.integers(1, maxctx, size=S)])[:S]
+    rng.shuffle(ctxs)
+    w = custom(dtype, 32, 8, D, ctxs, [1] * S, seed=310 + S, sinks=True)
+    announce(f"decode dispatch order {dtype} S={S} D={D}")
+    st = stage(w)
+    out = run_forward(pk, st, w)
+    got = out.cpu().numpy()
+    want = oracle_side(w)[3]
+    err = max_err(got, want)
+    print(f"[case] max abs err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and err <= TOL[dtype]
+    full = bits(out)
+    for i in sorted(set([0, S - 1] + [ctxs.index(c) for c in edge if c in ctxs] +
+                        [int(x) for x in rng.integers(0, S, size=6)])):
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i} ctx {ctxs[i]}")
