@@ -64,6 +64,8 @@ constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvFp4 = 2;
 // ---------------------------------------------------------------------------
 constexpr int kEdge = 1024, kSplitA = 256, kSplitB = 1024;
 constexpr int kSplitsA = kEdge / kSplitA;
+static_assert((kSplitA & (kSplitA - 1)) == 0 && (kSplitB & (kSplitB - 1)) == 0 && kEdge % kSplitB == 0,
+              "split sizes are powers of two and the edge falls on a large-split boundary");
 
 __host__ __device__ inline int split_index(int pos) {
     return pos < kEdge ? pos / kSplitA : kSplitsA + (pos - kEdge) / kSplitB;
@@ -1380,6 +1382,10 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
 
     int s = 0, rb = 0;
     if (!find_seq_item(P.qsl, P.num_seqs, P.G, blockIdx.x / P.Hkv, lane, s, rb)) return;
+    // uniform (a ballot's lane and values broadcast from it): in scalar
+    // registers, the walk below and its boundary tests stay scalar too
+    s = __builtin_amdgcn_readfirstlane(s);
+    rb = __builtin_amdgcn_readfirstlane(rb);
     const int q0 = P.qsl[s];
     const int q_len = P.qsl[s + 1] - q0;
     const int ctx = P.ctx_lens[s];
@@ -1501,12 +1507,14 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
             PoolT::mask(r, kc, ctx, g);
             PoolT::template update<MASKED>(qtr, r, qop, kc, rv, g, P.scale_log2);
         }
-        // quarter and split boundaries fall on step boundaries
+        // quarter and split boundaries fall on step boundaries; quarters are
+        // kSplitA / 4 keys up to the edge and kSplitB / 4 after it, both
+        // powers of two that divide every split start
         const int next = kc + kStep;
-        const int sj = split_index(kc);
-        const int sb = split_begin(sj), se = split_begin(sj + 1);
+        const int se = split_begin(split_index(kc) + 1);
+        const int qmask = (next <= kEdge ? kSplitA / 4 : kSplitB / 4) - 1;
         const bool last = c + 1 == nsteps;
-        if ((next - sb) % ((se - sb) >> 2) == 0 || last) {
+        if ((next & qmask) == 0 || last) {
             fold_state(spl, qtr);
             state_clear(qtr);
         }
