@@ -2104,20 +2104,17 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
         launch_parallel<D, 1, KF, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, D / 64), dim3(256), 0, st, P);
     } else {
-        bool done = false;
-        if constexpr (KF != kKvBf16) {
-            if (rows_per_seq > kParRows) {
-                // A batch with prefill chunks: the one-tile instance, which
-                // holds twice the waves per SIMD for quantized tiles (measured
-                // 14 % faster on a mixed step), takes its decode rows, and
-                // sequences of 17 to 32 rows in two passes, in one launch.
-                const int64_t nwg = par_grid(P);
-                hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, MASKED, true>), dim3((unsigned)nwg), dim3(256),
-                                   0, st, P);
-                done = true;
-            }
+        if (rows_per_seq > kParRows) {
+            // A batch with prefill chunks: the one-tile instance, which holds
+            // more waves per SIMD (measured on a mixed step: 14 % faster for
+            // quantized tiles, 5 % for bf16; its two-stage variant was slower),
+            // takes its decode rows, and sequences of 17 to 32 rows in two
+            // passes, in one launch.
+            hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, MASKED, true>), dim3((unsigned)par_grid(P)),
+                               dim3(256), 0, st, P);
+        } else {
+            launch_parallel<D, 2, KF, MASKED>(P, st);
         }
-        if (!done) launch_parallel<D, 2, KF, MASKED>(P, st);
         if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2 * (D / 64)), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
