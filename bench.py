@@ -266,6 +266,52 @@ def summarize_profile(d, workload, commands, producer=False):
     return 0
 
 
+MFMA_COUNTERS = ("SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU",
+                 "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", "SQ_WAVES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4                # MI355X: 256 compute units of 4 SIMDs
+XCDS = 8
+
+
+def summarize_mfma(d, workload, commands):
+    """Write profiles/mfma_<workload>.md from one rocprofv3 --pmc run over the
+    bench with MFMA_COUNTERS. MFMA utilisation follows rocprofv3's own
+    MfmaUtil: summed SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE of the
+    busiest die x SIMDs); the counter as collected sums the eight dies, so
+    its per-die maximum is taken as that sum / 8. A 16x16x32 bf16 MFMA is
+    16384 FLOP."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        k = _short(r["Kernel_Name"])
+        if not k.startswith(ATTN_KERNELS):
+            continue
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# MFMA and VALU counters, workload {workload}", "",
+             f"Source digest (sha256/16 of {os.path.basename(ATTN_SOURCE)}): `{source_digest()}`", "",
+             "Command (repository root, rocprofv3 output under gpurun_out/):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "Per dispatch, averaged over the run's dispatches of each kernel. MFMA utilisation:",
+              "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), as rocprofv3's MfmaUtil;",
+              "MFMA TFLOP/s: SQ_INSTS_MFMA x 16384 FLOP over the dispatch's GRBM_GUI_ACTIVE / 8 cycles at 2.4 GHz.",
+              "", "| kernel | dispatches | SQ_INSTS_MFMA | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | SQ_INSTS_VALU "
+              "| VALU per MFMA | MFMA util % | issued MFMA TFLOP/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(acc):
+        m = {c: sum(v) / len(v) for c, v in acc[k].items()}
+        if not all(c in m for c in MFMA_COUNTERS):
+            continue
+        n = len(acc[k]["SQ_INSTS_MFMA"])
+        die_cycles = m["GRBM_GUI_ACTIVE"] / XCDS
+        util = 100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (die_cycles * SIMDS) if die_cycles else 0.0
+        tflops = m["SQ_INSTS_MFMA"] * 16384 / (die_cycles / 2.4e9) / 1e12 if die_cycles else 0.0
+        vpm = f"{m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.1f}" if m["SQ_INSTS_MFMA"] else "—"
+        lines.append(f"| {k} | {n} | {m['SQ_INSTS_MFMA']:.0f} | {m['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} | "
+                     f"{m['GRBM_GUI_ACTIVE']:.0f} | {m['SQ_INSTS_VALU']:.0f} | {vpm} | {util:.1f} | {tflops:.0f} |")
+    out = os.path.join(ROOT, "profiles", f"mfma_{workload}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+    return 0
+
+
 def committed_traffic(workload, producer=False):
     """HBM bytes per call from the committed summary, or None when there is
     none or the kernels changed since it was taken."""
@@ -354,6 +400,8 @@ def main(argv=None):
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (for counter calibration) and exit")
     ap.add_argument("--summarize", metavar="DIR", help="only write the profile summary from rocprofv3 output")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="only write the MFMA/VALU counter summary from one rocprofv3 --pmc run")
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the summary")
     ap.add_argument("--producer", action="store_true",
                     help="time kv_qknorm_rope_scatter on the workload's step tokens instead of the attention step")
@@ -361,6 +409,8 @@ def main(argv=None):
 
     if args.summarize:
         return summarize_profile(args.summarize, args.workload, args.commands, producer=args.producer)
+    if args.summarize_mfma:
+        return summarize_mfma(args.summarize_mfma, args.workload, args.commands)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
