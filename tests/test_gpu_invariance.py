@@ -174,3 +174,37 @@ def test_decode_batch_dispatch_orders(pk, dtype, S, D, maxctx):
     for i in sorted(set([0, S - 1] + [ctxs.index(c) for c in edge if c in ctxs] +
                         [int(x) for x in rng.integers(0, S, size=6)])):
         np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i} ctx {ctxs[i]}")
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("bf16", 64, 8, 64), ("bf16", 16, 8, 64),
+                                             ("fp8", 32, 8, 128), ("fp4", 32, 8, 128)])
+def test_shared_prefix_batch_rows(pk, dtype, Hq, Hkv, D):
+    """A decode batch in which sequences 0-9 share a 2100-token prefix (five
+    whole splits read through the same blocks) and 10-13 have private
+    blocks. Every row matches the oracle, equals itself alone, and equals
+    the same batch with private copies of the prefix blocks."""
+    from gpu_util import TOL, max_err, oracle_side
+    from paged_kv_attention_block_amd.staging import stage
+    rng = np.random.default_rng(400 + D + Hq)
+    ctxs = [2100 + int(x) for x in rng.integers(1, 900, size=12)] + [3000, 1500]
+    w = custom(dtype, Hq, Hkv, D, ctxs, [1] * len(ctxs), seed=410 + Hq, sinks=True, shared_prefix=2100, n_shared=10)
+    announce(f"shared-prefix batch {dtype} {Hq}/{Hkv} D{D}")
+    st = stage(w)
+    assert (st.tables_np[0, :131] == st.tables_np[9, :131]).all()
+    out = run_forward(pk, st, w)
+    got = out.cpu().numpy()
+    err = max_err(got, oracle_side(w)[3])
+    print(f"[case] max abs err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got)) and err <= TOL[dtype]
+    full = bits(out)
+    for i in range(len(ctxs)):
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i}")
+    w2 = copy.deepcopy(w)
+    r2 = np.random.default_rng(7)
+    for seq in w2.seqs:                      # distinct token ids, same K/V bytes: no sharing
+        seq.tokens = r2.integers(0, 1 << 30, size=seq.ctx).astype(np.int32)
+    w2.num_blocks = 4 * w.num_blocks
+    w2.free_order = r2.permutation(w2.num_blocks).astype(np.int32)
+    st2 = stage(w2)
+    assert not (st2.tables_np[0, :131] == st2.tables_np[1, :131]).any()
+    np.testing.assert_array_equal(full, bits(run_forward(pk, st2, w2)))
