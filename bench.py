@@ -120,20 +120,47 @@ def cpu_baseline(w, kv_bytes, rows, seconds, tree_mask=None, window=0):
     tables = np.array(tables, dtype=np.int32)
     threads = oracle.default_threads()
     times = []
+    want = None
     t_end = time.perf_counter() + seconds
     while time.perf_counter() < t_end or len(times) < 2:
         t1 = time.perf_counter()
-        oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
-                               w.num_kv_heads, w.scale, w.sinks, w.dtype, threads, tree_mask=tree_mask,
-                               window=window)
+        out = oracle.paged_attention(w.q, kp, vp, tables, w.context_lens, w.qsl, w.num_q_heads,
+                                     w.num_kv_heads, w.scale, w.sinks, w.dtype, threads, tree_mask=tree_mask,
+                                     window=window)
         times.append(time.perf_counter() - t1)
+        if want is None:
+            want = out
         if len(times) >= 500:
             break
     med = float(np.median(times))
     return {"value": round(kv_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} calls over one layer's batch ({rows} rows, {kv_bytes / 1e6:.1f} MB of "
                       f"K/V), median {med * 1e3:.2f} ms per call (gather + fp64 attention); "
-                      f"seq-tokens/s {rows / med:.1f}"}
+                      f"seq-tokens/s {rows / med:.1f}"}, want
+
+
+# max-abs tolerance against the fp64 oracle, per pool format (8- and 4-bit
+# pools against the oracle's attention over its own dequantized codes)
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8": 2e-3, "fp4": 2e-3}
+
+
+def rows_alone_equal(pk, torch, st, w, rows):
+    """Bitwise: each listed query row, submitted by itself as one decode row
+    over the keys up to its position through the same block table, against
+    the same row in the batch output held in st.out."""
+    batch = st.out.contiguous().view(torch.int32).cpu().numpy()
+    dev = st.q.device
+    for i in rows:
+        s = int(np.searchsorted(w.qsl, i, side="right") - 1)
+        seq = w.seqs[s]
+        p = seq.ctx - seq.q_len + (i - int(w.qsl[s]))
+        one = pk.paged_attention_forward(
+            st.q[i:i + 1].contiguous(), st.k_pools[0], st.v_pools[0], st.tables[s:s + 1].contiguous(),
+            torch.tensor([p + 1], dtype=torch.int32, device=dev), torch.tensor([0, 1], dtype=torch.int32, device=dev),
+            1, p + 1, w.scale, sinks=st.sinks)
+        if not np.array_equal(one.contiguous().view(torch.int32).cpu().numpy()[0], batch[i]):
+            return False
+    return True
 
 
 def copy_calibrate(nbytes, reps):
@@ -548,9 +575,19 @@ def main(argv=None):
     att_alg_bytes = kv_bytes + q_bytes + out_bytes
     achieved = att_alg_bytes / (att_ms * 1e-3) / 1e9
 
-    cpu = None
+    # Checks on the same inputs, outside the timed regions, with the oracle
+    # leg (runs that skip it, such as the profiler's, launch nothing more):
+    # the batch output of the last call against the oracle's, and, without
+    # tree masks or a window, the first and last rows computed alone, bit
+    # for bit.
+    cpu = parity = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, kv_bytes, rows, args.cpu_seconds, tree_mask_words(w) if tree else None, window)
+        got = st.out.cpu().numpy()
+        cpu, want = cpu_baseline(w, kv_bytes, rows, args.cpu_seconds, tree_mask_words(w) if tree else None, window)
+        err = float(np.max(np.abs(got.astype(np.float64) - want))) if got.size else 0.0
+        parity = {"max_abs_err": err, "tol": TOL[w.dtype], "ok": bool(np.all(np.isfinite(got)) and err <= TOL[w.dtype])}
+        if not masked and rows:
+            parity["rows_alone_bitwise"] = rows_alone_equal(pk, torch, st, w, sorted({0, rows - 1}))
 
     line = {
         "metric": METRIC,
@@ -585,8 +622,12 @@ def main(argv=None):
             "alg_bytes_per_launch": att_alg_bytes,
         },
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(line), flush=True)
+    if parity and (not parity.get("ok", True) or not parity.get("rows_alone_bitwise", True)):
+        print(f"bench.py: output check failed: {parity}", file=sys.stderr)
+        return 1
     return 0
 
 
