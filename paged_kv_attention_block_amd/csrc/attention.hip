@@ -2074,11 +2074,14 @@ static int64_t par_grid(const AttnParams &P) {
 template <int D, int NT, bool APPEND, int KF, bool MASKED>
 static void launch_parallel_as(const AttnParams &P, hipStream_t st) {
     const int64_t nwg = par_grid(P);
-    // Two prefetch stages: always for bf16 single tiles (measured 3 % faster on
-    // large decode grids); for 8- and 4-bit tiles, whose conversions need the
-    // registers, only on grids that leave CUs free.
+    // Two prefetch stages only on grids that leave CUs free. On grids that
+    // queue, the one-stage variant keeps more workgroups resident: for 8- and
+    // 4-bit tiles the conversions need the registers; for bf16 tiles the
+    // extra slots measured 1 % faster on sink_decode's appending step and
+    // even on its attention calls (whose fixed order had favoured two stages
+    // by 3 % before the balanced order).
     if constexpr (NT == 1) {
-        if (KF == kKvBf16 || nwg <= device_cus()) {
+        if (nwg <= device_cus()) {
             hipLaunchKernelGGL((attn_parallel<D, NT, true, APPEND, KF, MASKED>), dim3((unsigned)nwg), dim3(256), 0,
                                st, P);
             return;
