@@ -93,6 +93,25 @@ def tree_mask_words(w, seed=1234):
     return np.array(words, dtype=np.uint32)
 
 
+def visible_keys(w, window=0, tree_words=None):
+    """Keys attended per layer, summed over query rows: row r of a sequence
+    sits at p = ctx - q_len + r and sees keys 0..p, or the last `window` of
+    them, or (a draft tree) every key before the window plus its ancestors."""
+    total, i = 0, 0
+    for seq in w.seqs:
+        base = seq.ctx - seq.q_len
+        for r in range(seq.q_len):
+            p = base + r
+            if tree_words is not None:
+                total += base + bin(int(tree_words[i]) & ((1 << (r + 1)) - 1)).count("1")
+            elif window:
+                total += min(p + 1, window)
+            else:
+                total += p + 1
+            i += 1
+    return total
+
+
 def logical_kv_bytes(w):
     return sum(seq.ctx for seq in w.seqs) * w.num_kv_heads * row_bytes(w) * 2
 
@@ -611,6 +630,8 @@ def main(argv=None):
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "seq_tokens_per_s": round(rows / (ms_per_step * 1e-3), 1),
+        "ctx_tokens_per_s": round(visible_keys(w, window, tree_mask_words(w) if tree else None)
+                                  / (ms_per_step * 1e-3), 1),
         "attention_call_us": round(att_ms * 1e3, 3),
         "eager_ms_per_step": round(eager_ms, 4),
         "layer_us": round(ms_per_step * 1e3 / layers, 3),
