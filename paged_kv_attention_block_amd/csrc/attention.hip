@@ -1266,21 +1266,22 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - (TWO && D == 64 ? 1 : 0
 }
 
 // ---------------------------------------------------------------------------
-// Split fold of the parallel shape: grid (sequence, KV head, tile x group
-// of four d-tiles); wave w owns d-tile 4 * group + w of the tile's rows (the
-// fold is elementwise in d; every workgroup repeats the same m, l fold) and
-// folds the split states left to right, sixteen loads in flight, then
-// finalizes.
+// Split fold of the parallel shape: grid (sequence, KV head, group of cells),
+// a cell being one (query row, query head) of the sequence's rows for that KV
+// head. D / 4 lanes hold a cell's accumulator, four consecutive channels each,
+// so every load and store covers whole cache lines; the fold is elementwise in
+// d and every lane of a cell repeats the same m, l fold. The split states are
+// folded left to right, sixteen per round trip, then finalized.
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
-    constexpr int DG = D / 64;  // groups of four d-tiles, one workgroup each
+    constexpr int LPC = D / 4;         // lanes per cell
+    constexpr int CPG = 256 / LPC;     // cells per workgroup
     static_assert(D % 64 == 0, "head_dim must be a multiple of 64");
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
-    const int g = lane >> 4, n = lane & 15;
-    const int s = blockIdx.x, kvh = blockIdx.y, t = blockIdx.z / DG;
-    const int dt = (blockIdx.z % DG) * 4 + wave;  // the wave's d-tile
+    const int s = blockIdx.x, kvh = blockIdx.y;
+    const int cell = blockIdx.z * CPG + tid / LPC;  // rho = r * G + hl within the sequence
+    const int e = (tid % LPC) * 4;                  // the lane's first channel
     int q0, q_len;
     if (P.decode_only) {
         q0 = s;
@@ -1290,13 +1291,12 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
         q_len = P.qsl[s + 1] - q0;
     }
     const int rows_total = q_len * P.G;
-    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT || 16 * t >= rows_total) return;
+    if (q0 < 0 || q_len <= 0 || q0 + q_len > P.total_rows || rows_total > 16 * NT || cell >= rows_total) return;
     // every slot holds a state (empty past the row's keys): no context length needed
-    const int rho = min(16 * t + n, rows_total - 1);  // padding lanes repeat a real row and store nothing
-    const int r = rho / P.G, hl = rho - r * P.G;
+    const int r = cell / P.G, hl = cell - r * P.G;
     const size_t base0 = ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * P.max_splits;
-    TileState<1> acc;
-    state_clear(acc);
+    float m = -INFINITY, l = 0.f;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     // the slots the parallel grid wrote (all, or a sliding window's run)
     int j0 = 0, j1 = P.max_splits;
     if (P.grid_splits < P.max_splits) {
@@ -1306,25 +1306,43 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
     // sixteen split states per round trip
     constexpr int U = 16;
     for (int j = j0; j < j1; j += U) {
-        TileState<1> x[U];
+        float2 xml[U];
+        f32x4_t xacc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            state_clear(x[u]);
+            xml[u] = make_float2(-INFINITY, 0.f);
+            xacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (j + u < j1) {
-                const float2 ml = P.ws_ml[base0 + j + u];
-                x[u].m = ml.x;
-                x[u].l = ml.y;
-                x[u].acc[0] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j + u) * D + 16 * dt + 4 * g);
+                xml[u] = P.ws_ml[base0 + j + u];
+                xacc[u] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j + u) * D + e);
             }
         }
+        // the fold of two states (as fold_state, element by element)
 #pragma unroll
-        for (int u = 0; u < U; ++u) fold_state(acc, x[u]);
+        for (int u = 0; u < U; ++u) {
+            if (xml[u].x == -INFINITY) continue;
+            if (m == -INFINITY) {
+                m = xml[u].x;
+                l = xml[u].y;
+                acc = xacc[u];
+                continue;
+            }
+            const float M = fmaxf(m, xml[u].x);
+            const float al = fast_exp2(m - M);
+            const float be = fast_exp2(xml[u].x - M);
+            l = fmaf(l, al, xml[u].y * be);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(acc[i], al, xacc[u][i] * be);
+            m = M;
+        }
     }
-    if (16 * t + n >= rows_total) return;
+    TileState<1> st;
+    st.m = m;
+    st.l = l;
+    st.acc[0] = acc;
     f32x4_t o[1];
-    finalize(acc, sink_log2(P, kvh, hl), o);
-    float *dst = P.out + ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * D + 4 * g;
-    *reinterpret_cast<f32x4_t *>(dst + 16 * dt) = o[0];
+    finalize(st, sink_log2(P, kvh, hl), o);
+    *reinterpret_cast<f32x4_t *>(P.out + ((size_t)(q0 + r) * P.Hq + kvh * P.G + hl) * D + e) = o[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -2105,7 +2123,8 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
     const bool fold = P.max_splits > 1;
     if (rows_per_seq <= 16) {
         launch_parallel<D, 1, KF, MASKED>(P, st);
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, D / 64), dim3(256), 0, st, P);
+        if (fold)
+            hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 16 * D / 4 / 256), dim3(256), 0, st, P);
     } else {
         if (rows_per_seq > kParRows) {
             // A batch with prefill chunks: the one-tile instance, which holds
@@ -2118,7 +2137,8 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
         } else {
             launch_parallel<D, 2, KF, MASKED>(P, st);
         }
-        if (fold) hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 2 * (D / 64)), dim3(256), 0, st, P);
+        if (fold)
+            hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 32 * D / 4 / 256), dim3(256), 0, st, P);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
