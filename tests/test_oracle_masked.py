@@ -221,7 +221,8 @@ def invariants(a):
         assert len(st["blocks"]) == -(-len(st["tokens"]) // a.B)
         assert len(st["hashes"]) == len(st["tokens"]) // a.B
         for b in st["blocks"]:
-            refs[b] += 1
+            if b >= 0:                         # -1: freed by drop_prefix, no reference held
+                refs[b] += 1
     assert refs == a.ref
     free = list(a.free)
     assert len(set(free)) == len(free)
@@ -333,3 +334,149 @@ def test_rollback_after_a_tree_round_matches_serial_appends():
     k_got, v_got = oracle.gather(kp, vp, row, ctx)
     np.testing.assert_array_equal(k_got, np.concatenate([kr, kw[path]]))
     np.testing.assert_array_equal(v_got, np.concatenate([vr, vw[path]]))
+
+
+# ----------------------------------------------------------------------------
+# Allocator.drop_prefix: freeing the blocks a sliding window has passed
+# (TensorSharp "高级功能" page, "性能优化": sliding-window layers; prefix
+# reuse bounded by the window). Every expectation below is worked out by hand
+# from the rule "block j is freed when (j + 1) * B <= first_kept; freed blocks
+# go to the back of the free list, highest j first, and keep their hash".
+# ----------------------------------------------------------------------------
+
+def _fresh_seq_of_14(B=4):
+    """12 blocks in identity order; sequence 1 holds tokens 1..14 in blocks
+    0, 1, 2 (full) and 3 (two slots)."""
+    a = oracle.Allocator(12, B)
+    row, nb, ctx, _ = a.alloc(1, list(range(1, 15)), 6)
+    assert row == [0, 1, 2, 3, -1, -1] and nb == 4 and ctx == 14
+    assert list(a.free) == list(range(4, 12))
+    return a
+
+
+@pytest.mark.parametrize("first_kept,freed", [(8, [1, 0]), (7, [0]), (9, [1, 0]), (3, []), (0, []),
+                                              (12, [2, 1, 0]), (14, [2, 1, 0]), (100, [2, 1, 0])])
+def test_drop_prefix_frees_whole_blocks_below_first_kept(first_kept, freed):
+    a = _fresh_seq_of_14()
+    a.drop_prefix(1, first_kept)
+    invariants(a)
+    # freed blocks join the back of the free list, the highest block index j first
+    assert list(a.free) == list(range(4, 12)) + freed
+    assert a.table_row(1, 6) == [-1 if b in freed else b for b in [0, 1, 2, 3]] + [-1, -1]
+    for b in freed:
+        assert a.ref[b] == 0 and a.in_free[b]
+        assert a.blk_hash[b] is not None          # hash kept: LRU reuse stays possible
+    assert a.seqs[1]["dropped"] == bool(freed)
+    assert len(a.seqs[1]["tokens"]) == 14         # positions keep their meaning
+
+
+def test_drop_prefix_of_a_shared_block_only_drops_a_reference():
+    a = _fresh_seq_of_14()
+    row2, _, _, slots = a.alloc(2, list(range(1, 9)), 6)   # shares blocks 0 and 1
+    assert row2[:2] == [0, 1] and slots == [-1] * 8
+    assert a.ref[0] == 2 and a.ref[1] == 2
+    a.drop_prefix(1, 8)
+    invariants(a)
+    assert a.ref[0] == 1 and a.ref[1] == 1
+    assert list(a.free) == list(range(4, 12))      # nothing went back to the pool
+    assert a.table_row(1, 6)[:4] == [-1, -1, 2, 3]
+    assert a.table_row(2, 6)[:2] == [0, 1]         # the other sequence keeps them
+
+
+def test_dropped_blocks_stay_hash_addressable_for_other_sequences():
+    a = _fresh_seq_of_14()
+    a.drop_prefix(1, 8)
+    assert list(a.free)[-2:] == [1, 0]
+    row2, _, _, slots = a.alloc(2, list(range(1, 9)), 6)
+    invariants(a)
+    assert row2[:2] == [0, 1] and slots == [-1] * 8   # revived from the free list
+    assert list(a.free) == list(range(4, 12))
+
+
+def test_a_dropped_sequence_neither_registers_nor_looks_up():
+    a = _fresh_seq_of_14()
+    a.drop_prefix(1, 8)
+    # block 3 fills up after the drop: it must not be registered ...
+    _, _, _, s = a.alloc(1, [15, 16], 6)
+    assert s == [14, 15]                            # block 3, slots 2 and 3
+    assert a.blk_hash[3] is None
+    # ... so a new sequence with the same 16 tokens shares blocks 0-2 only
+    row3, _, _, slots3 = a.alloc(3, list(range(1, 17)), 6)
+    invariants(a)
+    assert row3[:3] == [0, 1, 2] and row3[3] not in (3, -1)
+    assert slots3[:12] == [-1] * 12 and -1 not in slots3[12:]
+    # and a full block that another sequence registered is not looked up by
+    # the dropped sequence: it gets a fresh block for the same four tokens
+    a.alloc(3, [17, 18, 19, 20], 6)
+    ref4 = a.table_row(3, 6)[4]
+    assert a.blk_hash[ref4] is not None
+    row1, _, _, s1 = a.alloc(1, [17, 18, 19, 20], 6)
+    invariants(a)
+    assert row1[4] != ref4 and -1 not in s1
+
+
+def test_drop_prefix_errors():
+    a = _fresh_seq_of_14()
+    with pytest.raises(KeyError):
+        a.drop_prefix(7, 4)
+    with pytest.raises(ValueError):
+        a.drop_prefix(1, -1)
+    a.drop_prefix(1, 8)
+    a.drop_prefix(1, 8)                             # a second drop frees nothing more
+    invariants(a)
+    assert list(a.free) == list(range(4, 12)) + [1, 0]
+
+
+# ----------------------------------------------------------------------------
+# copy_blocks: the device copy a truncate into a shared block asks for
+# (TensorFold page, section on the GPU accept kernel: a rollback restores the
+# KV cache after the accepted path). Pinned on hand-built pools whose every
+# element names its own (block, head, element) position.
+# ----------------------------------------------------------------------------
+
+def _labelled_pool(nb, Hkv, tile, offset):
+    return (offset + np.arange(nb * Hkv * tile, dtype=np.int64).reshape(nb, Hkv, tile)).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "fp4"])
+def test_copy_blocks_direction_and_whole_tiles(fmt):
+    nb, Hkv, D = 6, 3, 64
+    if fmt == "bf16":
+        kp, vp = oracle.empty_pools(nb, Hkv, D, 16, "bf16")
+        kp[...] = np.arange(kp.size, dtype=np.uint16).reshape(kp.shape)
+        vp[...] = (np.arange(vp.size) + 40000).astype(np.uint16).reshape(vp.shape)
+    else:
+        mk = oracle.fp8_empty_pools if fmt == "fp8" else oracle.fp4_empty_pools
+        kp, vp = mk(nb, Hkv, D)
+        kp[...] = (np.arange(kp.size) % 251).astype(np.uint8).reshape(kp.shape)
+        vp[...] = (np.arange(vp.size) % 241).astype(np.uint8).reshape(vp.shape)
+    k0, v0 = kp.copy(), vp.copy()
+    oracle.copy_blocks(kp, vp, [4, 0], [1, 5])
+    # destination blocks hold the source blocks' full tiles, every head and slot
+    np.testing.assert_array_equal(kp[1], k0[4])
+    np.testing.assert_array_equal(vp[1], v0[4])
+    np.testing.assert_array_equal(kp[5], k0[0])
+    np.testing.assert_array_equal(vp[5], v0[0])
+    # sources and all other blocks are untouched (direction: src -> dst)
+    for b in (0, 2, 3, 4):
+        np.testing.assert_array_equal(kp[b], k0[b])
+        np.testing.assert_array_equal(vp[b], v0[b])
+    # the tiles really differ, so a copy the other way would have shown
+    assert not np.array_equal(k0[1], k0[4]) and not np.array_equal(v0[5], v0[0])
+
+
+def test_copy_blocks_then_retarget_gathers_the_same_keys():
+    """A truncate's copy-on-write: copy the shared block, point the table at
+    the copy, and the sequence gathers exactly the keys it had."""
+    rng = np.random.default_rng(44)
+    B, Hkv, D = 16, 2, 8
+    kp, vp = oracle.empty_pools(8, Hkv, D, B, "f32", fill=np.float32(np.nan))
+    k = rng.standard_normal((40, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((40, Hkv, D)).astype(np.float32)
+    row = [6, 2, 3]
+    slots = [row[t // B] * B + t % B for t in range(40)]
+    oracle.scatter(kp, vp, k, v, slots)
+    oracle.copy_blocks(kp, vp, [2], [7])
+    kg, vg = oracle.gather(kp, vp, [6, 7, 3], 40)
+    np.testing.assert_array_equal(kg, k)
+    np.testing.assert_array_equal(vg, v)
