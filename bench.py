@@ -116,6 +116,19 @@ def logical_kv_bytes(w):
     return sum(seq.ctx for seq in w.seqs) * w.num_kv_heads * row_bytes(w) * 2
 
 
+def host_cpu_model():
+    """The host CPU's model name (the "model name" field of /proc/cpuinfo,
+    which lscpu also reports), or None where the file has none."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, kv_bytes, rows, seconds, tree_mask=None, window=0):
     """The oracle, as it stands, on the host cores: its own allocation and
     scatter build the pools once; each timed call is gather + fp64 attention
@@ -138,6 +151,7 @@ def cpu_baseline(w, kv_bytes, rows, seconds, tree_mask=None, window=0):
         tables.append(row)
     tables = np.array(tables, dtype=np.int32)
     threads = oracle.default_threads()
+    cpu_model = host_cpu_model()
     times = []
     want = None
     t_end = time.perf_counter() + seconds
@@ -153,6 +167,7 @@ def cpu_baseline(w, kv_bytes, rows, seconds, tree_mask=None, window=0):
             break
     med = float(np.median(times))
     return {"value": round(kv_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{len(times)} calls over one layer's batch ({rows} rows, {kv_bytes / 1e6:.1f} MB of "
                       f"K/V), median {med * 1e3:.2f} ms per call (gather + fp64 attention); "
                       f"seq-tokens/s {rows / med:.1f}"}, want
@@ -438,9 +453,12 @@ def producer_bench(args, torch, synth, pk):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mid_decode")
+    ap.add_argument("--loops", type=int, default=5, help="timed loops of --steps steps; the median is reported")
+    # the largest decode workload is the default: 32 sequences of 1024-8192
+    # keys, 64 q / 8 KV heads, D 64, with sinks (226 MB of K/V per layer)
+    ap.add_argument("--workload", default="sink_decode")
     ap.add_argument("--layers", type=int, default=0, help="pool copies per step (0: reach 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample budget (0: skip)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="BYTES",
@@ -568,20 +586,35 @@ def main(argv=None):
 
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        g_step.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    def timed(graph, n):
+        """Milliseconds per replay of `graph` over n back-to-back replays,
+        events recorded on the launch stream; the median of --loops loops."""
+        per = []
+        for _ in range(max(1, args.loops)):
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n)
+        return float(np.median(per)), per
+
+    ms_per_step, step_loops = timed(g_step, args.steps)
 
     # attention launches alone, back to back: average duration per call
-    e0.record(stream)
-    for _ in range(args.steps):
-        g_att.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    att_ms = e0.elapsed_time(e1) / (args.steps * layers)
+    att_graph_ms, _ = timed(g_att, args.steps)
+    att_ms = att_graph_ms / layers
+
+    # the step's scatter-write alone (kv_append_scatter of every new row into
+    # one layer's pools), timed the same way
+    g_sc = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_sc):
+        for l in range(layers):
+            pk.kv_append_scatter(st.k_step, st.v_step, st.step_slots, st.k_pools[l], st.v_pools[l])
+    g_sc.replay()
+    scatter_ms = timed(g_sc, args.steps)[0] / layers
 
     # the same step launched eagerly (host launch cost included), for reference
     e0.record(stream)
@@ -616,6 +649,8 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "loops": max(1, args.loops),
+        "ms_per_step_loops": [round(x, 4) for x in step_loops],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -633,6 +668,9 @@ def main(argv=None):
         "ctx_tokens_per_s": round(visible_keys(w, window, tree_mask_words(w) if tree else None)
                                   / (ms_per_step * 1e-3), 1),
         "attention_call_us": round(att_ms * 1e3, 3),
+        "scatter_call_us": round(scatter_ms * 1e3, 3),
+        "scatter_tokens": n_step_tok,
+        "scatter_gbs": round(scatter_bytes / (scatter_ms * 1e-3) / 1e9, 2) if scatter_ms > 0 else None,
         "eager_ms_per_step": round(eager_ms, 4),
         "layer_us": round(ms_per_step * 1e3 / layers, 3),
         "host_alloc_us_per_batch": round(alloc_us, 1),

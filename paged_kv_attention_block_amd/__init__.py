@@ -206,6 +206,18 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for buffers a call creates: torch's caching
+    allocator ties a block to the stream current at allocation and hands it
+    out again, once freed, to later allocations on that stream only. Buffers
+    the kernels of `stream` use are therefore allocated on `stream`, so that
+    their reuse is ordered after those kernels."""
+    import contextlib
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def _need(t, name, dtype=None, ndim=None):
     torch = _torch()
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -308,12 +320,13 @@ def kv_accept_paths(parents, draft_tokens, choices, root_choices, query_start_lo
     rows, S = parents.shape[0], root_choices.shape[0]
     if draft_tokens.shape[0] != rows or choices.shape[0] != rows or query_start_loc.shape[0] != S + 1:
         raise KVError(KV_EINVAL, "parents, draft_tokens, choices, root_choices and query_start_loc disagree")
-    if path is None:
-        path = torch.empty(rows, dtype=torch.int32, device=parents.device)
-    if path_len is None:
-        path_len = torch.empty(S, dtype=torch.int32, device=parents.device)
-    if bonus is None:
-        bonus = torch.empty(S, dtype=torch.int32, device=parents.device)
+    with _on(stream):
+        if path is None:
+            path = torch.empty(rows, dtype=torch.int32, device=parents.device)
+        if path_len is None:
+            path_len = torch.empty(S, dtype=torch.int32, device=parents.device)
+        if bonus is None:
+            bonus = torch.empty(S, dtype=torch.int32, device=parents.device)
     for t, name, n in ((path, "path", rows), (path_len, "path_len", S), (bonus, "bonus", S)):
         _need(t, name, dtype=torch.int32, ndim=1)
         if t.shape[0] != n:
@@ -347,7 +360,8 @@ def kv_qknorm_rope_scatter(q, k, v, positions, slot_mapping, k_pool, v_pool, q_n
             if w.shape[0] != d:
                 raise KVError(KV_EINVAL, f"{name} needs head_dim values")
     if q_out is None:
-        q_out = torch.empty_like(q)
+        with _on(stream):
+            q_out = torch.empty_like(q)
     _need(q_out, "q_out", dtype=torch.bfloat16, ndim=3)
     if q_out.shape != q.shape:
         raise KVError(KV_EINVAL, "q_out has the wrong shape")
@@ -368,7 +382,7 @@ def paged_attention_workspace_size(num_seqs: int, total_q_rows: int, num_q_heads
 
 
 def _forward_args(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out,
-                  workspace):
+                  workspace, stream):
     torch = _torch()
     _need(q, "q", ndim=3)
     _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
@@ -385,13 +399,16 @@ def _forward_args(q, k_pool, v_pool, block_tables, context_lens, query_start_loc
         if sinks.shape[0] != hq:
             raise KVError(KV_EINVAL, "sinks must hold num_q_heads values")
     if out is None:
-        out = torch.empty((total, hq, d), dtype=torch.float32, device=q.device)
+        with _on(stream):
+            out = torch.empty((total, hq, d), dtype=torch.float32, device=q.device)
     _need(out, "out", dtype=torch.float32, ndim=3)
     if tuple(out.shape) != (total, hq, d):
         raise KVError(KV_EINVAL, "out has the wrong shape")
     need = paged_attention_workspace_size(S, total, hq, d, max_context_len)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        # freed when the call returns: only allocations on `stream` reuse it
+        with _on(stream):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _need(workspace, "workspace")
     ws_bytes = workspace.numel() * workspace.element_size()
     return S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes
@@ -402,7 +419,7 @@ def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query
                             stream=None):
     """out [total_rows, Hq, D] float32 = attention of q over the paged cache (see pagedkv.h)."""
     S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
-        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace, stream)
     _check(_lib.paged_attention_forward(
         q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), code, block_tables.data_ptr(),
         block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len,
@@ -419,7 +436,7 @@ def paged_attention_append_forward(q, k_new, v_new, slot_mapping, k_pool, v_pool
     [total_rows]) and paged_attention_forward in one call (see pagedkv.h); returns out."""
     torch = _torch()
     S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
-        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace, stream)
     _need(k_new, "k_new", dtype=q.dtype, ndim=3)
     _need(v_new, "v_new", dtype=q.dtype, ndim=3)
     _need(slot_mapping, "slot_mapping", dtype=torch.int32, ndim=1)
@@ -442,7 +459,7 @@ def paged_attention_masked_forward(q, k_pool, v_pool, block_tables, context_lens
     sliding window (0 = none); see pagedkv.h."""
     torch = _torch()
     S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
-        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace)
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace, stream)
     if tree_mask is not None:
         _need(tree_mask, "tree_mask", dtype=torch.int32, ndim=1)
         if tree_mask.shape[0] != total:

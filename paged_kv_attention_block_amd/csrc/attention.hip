@@ -2121,7 +2121,11 @@ template <int D, int KF, bool MASKED>
 static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
     const bool fold = P.max_splits > 1;
-    if (rows_per_seq <= 16) {
+    if (P.G > kParRows) {
+        // Every sequence brings at least G > 32 rows to its KV head: all of
+        // them take the sequential shape, and the split and fold launches
+        // would have nothing to do.
+    } else if (rows_per_seq <= 16) {
         launch_parallel<D, 1, KF, MASKED>(P, st);
         if (fold)
             hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 16 * D / 4 / 256), dim3(256), 0, st, P);

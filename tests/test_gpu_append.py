@@ -112,3 +112,12 @@ def test_other_batches_scatter_first(pk, dtype):
     launch first; the result is the same as two calls."""
     w = custom(dtype, 16, 4, 64, [300, 1100, 70, 40], [8, 130, 1, 40], seed=99)
     _check(pk, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_wide_query_groups_append(pk, dtype, D):
+    """64 query heads on one KV head: the appending call scatters first and
+    equals two calls."""
+    w = custom(dtype, 64, 1, D, [3000, 700, 1025, 64, 1], [1] * 5, seed=320 + D, sinks=True)
+    _check(pk, w)

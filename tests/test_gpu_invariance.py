@@ -208,3 +208,58 @@ def test_shared_prefix_batch_rows(pk, dtype, Hq, Hkv, D):
     st2 = stage(w2)
     assert not (st2.tables_np[0, :131] == st2.tables_np[1, :131]).any()
     np.testing.assert_array_equal(full, bits(run_forward(pk, st2, w2)))
+
+
+@pytest.mark.parametrize("name", ["verify_window", "verify_window_fp8", "verify_window_fp4"])
+def test_verify_window_workload_every_row_equals_row_alone(pk, name):
+    """The 8-row speculative verify windows of 16 sequences with contexts of
+    4096-16384 keys (the TensorFold page's row-invariant wide-window rule):
+    each of the 128 rows, computed alone as a decode row over the keys up to
+    its position, gives the bits it has inside its window."""
+    import synth
+    from paged_kv_attention_block_amd.staging import stage
+    w = synth.by_name(name)
+    announce(f"{name}: all {w.total_rows} rows alone, contexts {min(s.ctx for s in w.seqs)}-"
+             f"{max(s.ctx for s in w.seqs)}")
+    st = stage(w)
+    full = bits(run_forward(pk, st, w))
+    for i in range(w.total_rows):
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp4"])
+def test_mixed_step_workload_rows_equal_rows_alone(pk, dtype):
+    """The continuous-batching step: every decode row over the 181 hash-shared
+    prefix blocks, and prefill rows 0, 15, 16, 63, 64 and 1023 of both
+    1024-row chunks, each equal to itself computed alone (the ds4 glossary's
+    rule that batched results equal per-session results)."""
+    import synth
+    from paged_kv_attention_block_amd.staging import stage
+    w = synth.mixed_step(dtype=dtype)
+    qsl = w.qsl
+    n_dec = sum(1 for s in w.seqs if s.q_len == 1)
+    rows = list(range(n_dec))
+    for s in range(n_dec, len(w.seqs)):
+        rows += [int(qsl[s]) + r for r in (0, 15, 16, 63, 64, 1023)]
+    announce(f"mixed_step {dtype}: {len(rows)} rows alone ({n_dec} decode rows over the shared prefix)")
+    st = stage(w)
+    shared = set(st.tables_np[0, :181].tolist())
+    assert all(set(st.tables_np[s, :181].tolist()) == shared for s in range(n_dec))
+    full = bits(run_forward(pk, st, w))
+    for i in rows:
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_wide_query_groups_rows_equal_rows_alone(pk, dtype, D):
+    """64 query heads on one KV head (more rows per KV head than one split
+    workgroup takes): decode rows and an 8-row window, each row equal to
+    itself alone."""
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom(dtype, 64, 1, D, [3000, 700, 1025, 64], [1, 8, 1, 1], seed=310 + D, sinks=True)
+    announce(f"wide groups invariance {dtype} 64/1 D{D}")
+    st = stage(w)
+    full = bits(run_forward(pk, st, w))
+    for i in range(w.total_rows):
+        np.testing.assert_array_equal(bits(alone(pk, st, w, i))[0], full[i], err_msg=f"row {i}")

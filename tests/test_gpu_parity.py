@@ -216,3 +216,13 @@ def test_scatter_patterns_bit_exact(pk, dtype, D):
     oracle.scatter(ko, vo, kn, vn, slots)
     np.testing.assert_array_equal(_bits(kp), ko.view(np.uint16 if dtype == "bf16" else np.uint32))
     np.testing.assert_array_equal(_bits(vp), vo.view(np.uint16 if dtype == "bf16" else np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("q_lens", [[1, 1, 1, 1, 1], [1, 8, 1, 3, 1]])
+def test_wide_query_groups(pk, dtype, D, q_lens):
+    """64 query heads sharing one KV head: even a decode row brings 64 rows to
+    its KV head, more than one split workgroup takes."""
+    w = custom(dtype, 64, 1, D, [3000, 700, 1025, 64, 2049], q_lens, seed=300 + D + sum(q_lens), sinks=True)
+    check_workload(pk, w)
