@@ -371,6 +371,31 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
                             size_t workspace_bytes, void *hip_stream);
 
 /*
+ * paged_attention_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, kernels and results, bit for bit, without
+ * `workspace` and `workspace_bytes`. The split states live in a scratch array
+ * the library holds in device memory, one per device, 64 MiB
+ * (67108864 bytes), kept until the process ends; its device address is
+ * looked up once per device on the first call there. The call allocates
+ * nothing. Every call on one device shares that device's array, and the
+ * array needs no clearing (each call writes every split state it reads), so
+ * calls that may overlap on one device (different streams, or several host
+ * threads) race and must be serialized by the caller.
+ * Errors: those of paged_attention_forward; KV_EINVAL also when the batch
+ * needs more than 64 MiB of split states (paged_attention_workspace_size of
+ * its sizes), with the number in the message; KV_EDEVICE when the scratch
+ * array's address cannot be found.
+ */
+int paged_attention_forward_noalloc(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, const int32_t *query_start_loc,
+                                    int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                    int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                    const float *sinks, float *out, void *hip_stream);
+
+/*
  * One decode step's append and attention in one call ("原生分页注意力", its
  * batched-forward paragraph: the batched forward paired with a paged K/V
  * scatter-write). Row i's own token is the new token of its sequence: it sits

@@ -28,7 +28,7 @@ __all__ = [
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
     "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks", "kv_append_scatter",
     "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter", "paged_attention_workspace_size", "paged_attention_forward",
-    "paged_attention_append_forward", "paged_attention_masked_forward", "empty_pools", "BLOCK_SIZE",
+    "paged_attention_forward_noalloc", "paged_attention_append_forward", "paged_attention_masked_forward", "empty_pools", "BLOCK_SIZE",
 ]
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
@@ -68,6 +68,9 @@ _lib.paged_attention_workspace_size.restype = _sz
 _lib.paged_attention_forward.argtypes = [
     _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
     _f32, _p, _p, _p, _sz, _p]
+_lib.paged_attention_forward_noalloc.argtypes = [
+    _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    _f32, _p, _p, _p]
 _lib.paged_attention_append_forward.argtypes = [
     _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
     _f32, _p, _p, _p, _sz, _p]
@@ -77,7 +80,7 @@ _lib.paged_attention_masked_forward.argtypes = [
 for _name in ("kv_pool_create", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
               "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks",
               "kv_append_scatter", "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter",
-              "paged_attention_forward",
+              "paged_attention_forward", "paged_attention_forward_noalloc",
               "paged_attention_append_forward", "paged_attention_masked_forward"):
     getattr(_lib, _name).restype = ctypes.c_int
 
@@ -426,6 +429,40 @@ def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query
         max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
         _stream_ptr(stream)))
+    return out
+
+
+def paged_attention_forward_noalloc(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
+                                    max_context_len: int, scale: float, sinks=None, out=None, stream=None):
+    """paged_attention_forward with the library's own scratch array for the
+    split states (see pagedkv.h): no workspace argument; `out` must be given
+    by callers that cannot allocate."""
+    torch = _torch()
+    _need(q, "q", ndim=3)
+    _need(block_tables, "block_tables", dtype=torch.int32, ndim=2)
+    _need(context_lens, "context_lens", dtype=torch.int32, ndim=1)
+    _need(query_start_loc, "query_start_loc", dtype=torch.int32, ndim=1)
+    total, hq, d = q.shape
+    code, nb = _pools(k_pool, v_pool, q.dtype, None, d)
+    hkv = k_pool.shape[1]
+    S = context_lens.shape[0]
+    if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise KVError(KV_EINVAL, "context_lens, query_start_loc and block_tables disagree on num_seqs")
+    if sinks is not None:
+        _need(sinks, "sinks", dtype=torch.float32, ndim=1)
+        if sinks.shape[0] != hq:
+            raise KVError(KV_EINVAL, "sinks must hold num_q_heads values")
+    if out is None:
+        with _on(stream):
+            out = torch.empty((total, hq, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", dtype=torch.float32, ndim=3)
+    if tuple(out.shape) != (total, hq, d):
+        raise KVError(KV_EINVAL, "out has the wrong shape")
+    _check(_lib.paged_attention_forward_noalloc(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), code, block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len,
+        max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        None if sinks is None else sinks.data_ptr(), out.data_ptr(), _stream_ptr(stream)))
     return out
 
 

@@ -35,6 +35,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "pagedkv.h"
 #include "status.h"
@@ -2170,6 +2171,48 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows, in
 }  // extern "C"
 
 namespace pkv {
+// Split-state scratch of paged_attention_forward_noalloc, for callers that
+// cannot allocate: 64 MiB, enough for 128 verify rows x 32 heads over 16384
+// keys (40.5 MB). The module holds one copy per device for the process's
+// life; calls on one device share it.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+}  // namespace pkv
+
+static __device__ __align__(256) unsigned char scratch[pkv::kScratchBytes];
+
+namespace pkv {
+
+// Device address of `scratch` on the device `hip_stream` belongs to (the
+// current device for the null stream). In host code the array's name is a
+// host-side stand-in, never a device address: the address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static int scratch_on_stream(void *hip_stream, void **out) {
+    static std::mutex mu;
+    static void *addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hip_stream ? hipStreamGetDevice(reinterpret_cast<hipStream_t>(hip_stream), &dev)
+                              : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        PKV_FAIL(KV_EDEVICE, "paged_attention_forward_noalloc: no device for the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward_noalloc: device %d", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            PKV_FAIL(KV_EDEVICE, "paged_attention_forward_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            PKV_FAIL(KV_EDEVICE, "paged_attention_forward_noalloc: hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p)
+            PKV_FAIL(KV_EDEVICE, "paged_attention_forward_noalloc: hipGetSymbolAddress(scratch) on device %d: %s",
+                     dev, hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return KV_OK;
+}
 
 struct AppendArgs {
     const void *k_new, *v_new;
@@ -2337,6 +2380,31 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
                              query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, workspace,
                              workspace_bytes, hip_stream, nullptr, nullptr);
+}
+
+int paged_attention_forward_noalloc(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t *context_lens, const int32_t *query_start_loc,
+                                    int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                    int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                    const float *sinks, float *out, void *hip_stream) {
+    if (num_q_heads <= 0 || head_dim <= 0 || num_seqs < 0 || total_q_rows < 0 || max_context_len < 0)
+        PKV_FAIL(KV_EINVAL, "paged_attention_forward_noalloc: invalid sizes");
+    const size_t need = paged_attention_workspace_size(num_seqs, total_q_rows, num_q_heads, head_dim,
+                                                       max_context_len);
+    if (need > pkv::kScratchBytes)
+        PKV_FAIL(KV_EINVAL,
+                 "paged_attention_forward_noalloc: this batch needs %zu bytes of split states, above the "
+                 "library's fixed %zu-byte scratch array; call paged_attention_forward with a workspace",
+                 need, pkv::kScratchBytes);
+    void *ws = nullptr;
+    const int rc = pkv::scratch_on_stream(hip_stream, &ws);
+    if (rc != KV_OK) return rc;
+    return pkv::forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens,
+                             query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, ws,
+                             pkv::kScratchBytes, hip_stream, nullptr, nullptr);
 }
 
 int paged_attention_masked_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,

@@ -129,3 +129,17 @@ def test_pool_create_validation(pk):
         pk.kv_pool_alloc(p, 1, range(100), 4)      # needs 7 blocks > max_blocks
     assert e.value.code == pk.KV_EINVAL
     assert pk.kv_pool_stats(p) == (4, 0, 0)
+
+
+def test_noalloc_forward_rejects_batches_beyond_its_scratch_on_the_host(pk):
+    """The size check comes before any device call: 2096 rows x 32 heads x 7
+    splits of 128 channels need about 244 MB of split states, more than the
+    64 MiB array."""
+    lib = _lib(pk)
+    fake = ctypes.c_void_p(256)   # never dereferenced: the size check fails first
+    need = pk.paged_attention_workspace_size(50, 2096, 32, 128, 3925)
+    assert need > 64 << 20
+    rc = lib.paged_attention_forward_noalloc(fake, fake, fake, pk.KV_BF16, fake, 256, fake, fake, 50, 2096, 1024,
+                                             3925, 32, 8, 128, 16, 64, 0.1, None, fake, None)
+    assert rc == pk.KV_EINVAL
+    assert str(need) in pk.kv_last_error() and "67108864" in pk.kv_last_error()
