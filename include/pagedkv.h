@@ -96,12 +96,17 @@ enum kv_dtype { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2, KV_FP4 = 3 };
 
 #define PAGEDKV_ABI_VERSION 1
 
-/* ABI version of the loaded library (PAGEDKV_ABI_VERSION). */
+/* ABI version of the loaded library (PAGEDKV_ABI_VERSION). Library plumbing:
+ * no passage of the pages describes it. */
 int kv_abi_version(void);
 
 /* Message of the last failed call on this thread ("" if none). The pointer is
  * owned by the library and stays valid until the next failing call on the
- * thread. */
+ * thread. The pages describe no such call; it carries the style of failure
+ * they ask for (TensorSharp "高级功能" page, "内存优化": a request the pool
+ * cannot serve fails at once with an explicit message that gives the
+ * numbers, instead of degrading silently), so every KV_E* code comes with
+ * the sizes that caused it. */
 const char *kv_last_error(void);
 
 /* ------------------------------------------------------------------------ */
@@ -170,7 +175,10 @@ int kv_pool_alloc(kv_pool *pool, int64_t seq_id, const int32_t *new_token_ids, i
 int kv_pool_release(kv_pool *pool, int64_t seq_id);
 
 /* Counts: blocks in the free list, of which still hash-addressable (cached),
- * and blocks with a nonzero refcount. Any output pointer may be NULL. */
+ * and blocks with a nonzero refcount ("内存优化": the paged pool's LRU list
+ * of cached blocks beside the blocks in use; the counts are this library's
+ * observability of it, not a call the pages name). Any output pointer may be
+ * NULL. */
 int kv_pool_stats(const kv_pool *pool, int32_t *free_blocks, int32_t *cached_blocks,
                   int32_t *live_blocks);
 
@@ -319,7 +327,9 @@ int kv_qknorm_rope_scatter(const void *q, const void *k, const void *v, const in
 
 /*
  * Bytes of device workspace paged_attention_forward needs for these sizes
- * (0 on invalid sizes). The workspace holds per-split partial results; its
+ * (0 on invalid sizes). Library plumbing, no passage: the split-K partial
+ * states it sizes are this library's way of spreading long contexts over the
+ * GPU, not part of what the pages describe. The workspace holds per-split partial results; its
  * contents need no initialisation and are meaningless after a call. Calls that
  * may run at the same time (different streams) need different workspaces.
  */
@@ -348,6 +358,9 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
  *                   <= max_context_len
  *   query_start_loc device int32 [num_seqs + 1], ascending, [0] = 0,
  *                   [num_seqs] = total_q_rows, q_len <= max_q_len
+ *   num_blocks      blocks each pool holds; a block id outside
+ *                   0 .. num_blocks - 1 reads as an empty block, so no
+ *                   table entry can make a kernel read outside the pools
  *   sinks           device float [num_q_heads] or NULL
  *   out             device float [total_q_rows][num_q_heads][head_dim]
  *   workspace       device, >= paged_attention_workspace_size(...) bytes
