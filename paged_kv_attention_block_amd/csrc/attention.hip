@@ -372,7 +372,7 @@ __device__ inline uint32_t visible8(const RowVis &v, int key0) {
     return m;
 }
 
-template <int D, bool SCALED, bool MASKED, class KOp, class VOp>
+template <int D, bool SCALED, bool MASKED, bool ALWAYS = false, class KOp, class VOp>
 __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const float (&ksc)[8],
                                  const float (&vsc)[8], const u32x4_t (&qop)[D / 32], int kc, const RowVis &rv,
                                  int g, float scale_log2) {
@@ -430,7 +430,10 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     // are kept) or the accumulators are still zero, and its weights are 0
     // against finite V (masked tails are zeroed), so the products add zeros.
     // Only a zero's sign can change (-0 + 0 = +0), which finalize removes.
-    if (__any(alpha != 1.f)) {
+    // ALWAYS (the prefill shape, where some row's max moves in most steps):
+    // the rescale runs unconditionally, the same values (x * 1 == x), so that
+    // the accumulators keep one set of registers through the step.
+    if (ALWAYS || __any(alpha != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
     }
@@ -532,11 +535,11 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
     }
 }
 
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool ALWAYS = false>
 __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
                                    const RowVis &rv, int g, float scale_log2) {
     const float none[8] = {};
-    step_core<D, false, MASKED>(
+    step_core<D, false, MASKED, ALWAYS>(
         st, [&](int tau, int j) { return __builtin_bit_cast(bf16x8_t, r.k[tau][j]); },
         [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, rv, g, scale_log2);
 }
@@ -666,12 +669,12 @@ __device__ inline void step_update8x2(TileState<D / 16> (&st)[2], const StepRegs
         ksc, vsc, qop, kc, rv, g, scale_log2);
 }
 
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool ALWAYS = false>
 __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r, const u32x4_t (&qop)[D / 32],
                                     int kc, const RowVis &rv, int g, float scale_log2) {
     float ksc[8], vsc[8];
     step_scales(r, ksc, vsc);
-    step_core<D, true, MASKED>(
+    step_core<D, true, MASKED, ALWAYS>(
         st,
         [&](int tau, int j) {
             const u32x4_t w = r.k[tau][j >> 1];
@@ -699,10 +702,10 @@ struct Pool<D, kKvBf16> {
                      reinterpret_cast<const uint16_t *>(k1), reinterpret_cast<const uint16_t *>(v1), g, n);
     }
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail<D>(r, kc, ctx, g); }
-    template <bool MASKED>
+    template <bool MASKED, bool ALWAYS = false>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
                                   const RowVis &rv, int g, float sl2) {
-        step_update<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+        step_update<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2);
     }
     template <bool MASKED>
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
@@ -720,10 +723,10 @@ struct Pool<D, kKvFp8> {
         load_step8<D>(r, k0, v0, k1, v1, g, n);
     }
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail8<D>(r, kc, ctx, g); }
-    template <bool MASKED>
+    template <bool MASKED, bool ALWAYS = false>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
                                   const RowVis &rv, int g, float sl2) {
-        step_update8<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+        step_update8<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2);
     }
     template <bool MASKED>
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
@@ -832,12 +835,12 @@ __device__ inline void mask_tail4(StepRegs4<D> &r, int kc, int ctx, int g) {
     }
 }
 
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool ALWAYS = false>
 __device__ inline void step_update4(TileState<D / 16> &st, const StepRegs4<D> &r, const u32x4_t (&qop)[D / 32],
                                     int kc, const RowVis &rv, int g, float scale_log2) {
     float ksc[8], vsc[8];
     step_scales(r, ksc, vsc);
-    step_core<D, true, MASKED>(
+    step_core<D, true, MASKED, ALWAYS>(
         st, [&](int tau, int j) { return fp4x8_to_bf16(r.k[tau][j]); }, [&](int dt) { return fp4x8_to_bf16(r.v[dt]); },
         ksc, vsc, qop, kc, rv, g, scale_log2);
 }
@@ -862,10 +865,10 @@ struct Pool<D, kKvFp4> {
         load_step4<D, false>(r, k0, v0, k1, v1, g, n);
     }
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail4<D>(r, kc, ctx, g); }
-    template <bool MASKED>
+    template <bool MASKED, bool ALWAYS = false>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
                                   const RowVis &rv, int g, float sl2) {
-        step_update4<D, MASKED>(st, r, qop, kc, rv, g, sl2);
+        step_update4<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2);
     }
     template <bool MASKED>
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
@@ -1524,7 +1527,7 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
                                  reinterpret_cast<const uint16_t *>(buf + PS),
                                  reinterpret_cast<const uint16_t *>(buf + 3 * PS), g, n);
             PoolT::mask(r, kc, ctx, g);
-            PoolT::template update<MASKED>(qtr, r, qop, kc, rv, g, P.scale_log2);
+            PoolT::template update<MASKED, true>(qtr, r, qop, kc, rv, g, P.scale_log2);
         }
         // quarter and split boundaries fall on step boundaries; quarters are
         // kSplitA / 4 keys up to the edge and kSplitB / 4 after it, both
