@@ -467,6 +467,8 @@ def main(argv=None):
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="only write the MFMA/VALU counter summary from one rocprofv3 --pmc run")
     ap.add_argument("--commands", nargs="*", default=[], help="commands recorded in the summary")
+    ap.add_argument("--no-prefix", action="store_true",
+                    help="do not pass the batch's shared prompt prefix (from its block tables) to the attention calls")
     ap.add_argument("--producer", action="store_true",
                     help="time kv_qknorm_rope_scatter on the workload's step tokens instead of the attention step")
     args = ap.parse_args(argv)
@@ -488,7 +490,7 @@ def main(argv=None):
 
     import synth
     import paged_kv_attention_block_amd as pk
-    from paged_kv_attention_block_amd.staging import stage
+    from paged_kv_attention_block_amd.staging import prefix_hint, stage
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -527,6 +529,10 @@ def main(argv=None):
         tables = torch.from_numpy(rows_np.astype(np.int32)).to(dev)
     tmask = torch.from_numpy(tree_mask_words(w).view(np.int32)).to(dev) if tree else None
     masked = tree or window > 0
+    # a prompt prefix the batch's sequences hold in the same physical blocks,
+    # as the host tables show it: the attention calls read it once per group
+    pre_seqs, pre_tokens = (0, 0) if (masked or args.no_prefix) else prefix_hint(st.tables_np)
+    use_prefix = pre_seqs >= 2
     rows = w.total_rows
     q_bytes = rows * w.num_q_heads * w.head_dim * elt
     out_bytes = rows * w.num_q_heads * w.head_dim * 4
@@ -540,14 +546,18 @@ def main(argv=None):
                                               st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks,
                                               tree_mask=tmask, sliding_window=window, out=st.out,
                                               workspace=st.workspace)
+        elif use_prefix:
+            pk.paged_attention_prefix_forward(st.q, st.k_pools[l], st.v_pools[l], tables, st.context_lens, st.qsl,
+                                              st.max_q_len, st.max_context_len, w.scale, pre_seqs, pre_tokens,
+                                              sinks=st.sinks, out=st.out, workspace=st.workspace)
         else:
             pk.paged_attention_forward(st.q, st.k_pools[l], st.v_pools[l], tables, st.context_lens, st.qsl,
                                        st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=st.out,
                                        workspace=st.workspace)
 
     def layer_call(l):
-        if masked:
-            # masked calls take no appended rows: scatter, then attend
+        if masked or use_prefix:
+            # masked and prefix calls take no appended rows: scatter, then attend
             pk.kv_append_scatter(st.k_step, st.v_step, st.step_slots, st.k_pools[l], st.v_pools[l])
             attend(l)
         else:
@@ -661,6 +671,7 @@ def main(argv=None):
             "rows_per_layer": rows, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "block_size": 16, "layers_per_step": layers,
             "tree_windows": tree, "sliding_window": window,
+            "shared_prefix": {"seqs": pre_seqs, "tokens": pre_tokens} if use_prefix else None,
             "kv_bytes_per_layer": kv_bytes, "logical_kv_bytes_per_layer": logical_kv_bytes(w),
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

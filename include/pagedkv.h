@@ -384,6 +384,36 @@ int paged_attention_forward(const void *q, const void *k_pool, const void *v_poo
                             size_t workspace_bytes, void *hip_stream);
 
 /*
+ * paged_attention_forward for a batch whose first sequences share a prompt
+ * prefix ("连续批处理与分页 KV 缓存": identical prefix blocks are shared
+ * between concurrent requests through the block hash, so many sequences hold
+ * one system prompt in the same physical blocks). Sequences 0 .. prefix_seqs
+ * - 1 are expected to be decode rows (one query row each) whose first
+ * prefix_tokens positions lie in the same physical blocks; the caller knows
+ * this from the block manager (kv_pool_alloc reports those slots as
+ * resident). The splits that lie wholly inside the prefix are then computed
+ * once for each group of up to four such sequences, as one 16-row tile that
+ * reads the shared blocks once, instead of once per sequence.
+ * The result is paged_attention_forward's, bit for bit, whatever the hint:
+ * every group checks the block ids of each split it takes and the rows of its
+ * sequences; where they differ, or a sequence has more than one row, it
+ * computes its sequences one after another over their own blocks. Other
+ * arguments, ownership and errors are paged_attention_forward's;
+ * prefix_seqs < 2, a prefix shorter than the first split (256 tokens), more
+ * than 8 query heads per KV head, or a batch with 17 to 32 rows per sequence
+ * and KV head and no longer sequence take paged_attention_forward's launch.
+ * Errors also: KV_EINVAL for prefix_seqs or prefix_tokens < 0.
+ */
+int paged_attention_prefix_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                   int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                   const float *sinks, int32_t prefix_seqs, int32_t prefix_tokens, float *out,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
  * paged_attention_forward for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments, kernels and results, bit for bit, without

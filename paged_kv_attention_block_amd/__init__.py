@@ -28,7 +28,7 @@ __all__ = [
     "kv_pool_create", "kv_pool_destroy", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
     "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks", "kv_append_scatter",
     "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter", "paged_attention_workspace_size", "paged_attention_forward",
-    "paged_attention_forward_noalloc", "paged_attention_append_forward", "paged_attention_masked_forward", "empty_pools", "BLOCK_SIZE",
+    "paged_attention_forward_noalloc", "paged_attention_prefix_forward", "paged_attention_append_forward", "paged_attention_masked_forward", "empty_pools", "BLOCK_SIZE",
 ]
 
 KV_OK, KV_EINVAL, KV_ENOMEM, KV_EUNSUPPORTED, KV_EDEVICE, KV_EINTERNAL = 0, -1, -2, -3, -4, -5
@@ -68,6 +68,9 @@ _lib.paged_attention_workspace_size.restype = _sz
 _lib.paged_attention_forward.argtypes = [
     _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
     _f32, _p, _p, _p, _sz, _p]
+_lib.paged_attention_prefix_forward.argtypes = [
+    _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+    _f32, _p, _i32, _i32, _p, _p, _sz, _p]
 _lib.paged_attention_forward_noalloc.argtypes = [
     _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
     _f32, _p, _p, _p]
@@ -80,7 +83,7 @@ _lib.paged_attention_masked_forward.argtypes = [
 for _name in ("kv_pool_create", "kv_pool_alloc", "kv_pool_release", "kv_pool_stats",
               "kv_pool_set_hash_mask", "kv_pool_truncate", "kv_pool_drop_prefix", "kv_tree_masks",
               "kv_append_scatter", "kv_copy_blocks", "kv_accept_paths", "kv_qknorm_rope_scatter",
-              "paged_attention_forward", "paged_attention_forward_noalloc",
+              "paged_attention_forward", "paged_attention_forward_noalloc", "paged_attention_prefix_forward",
               "paged_attention_append_forward", "paged_attention_masked_forward"):
     getattr(_lib, _name).restype = ctypes.c_int
 
@@ -429,6 +432,25 @@ def paged_attention_forward(q, k_pool, v_pool, block_tables, context_lens, query
         max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
         None if sinks is None else sinks.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
         _stream_ptr(stream)))
+    return out
+
+
+def paged_attention_prefix_forward(q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_q_len: int,
+                                   max_context_len: int, scale: float, prefix_seqs: int, prefix_tokens: int,
+                                   sinks=None, out=None, workspace=None, stream=None):
+    """paged_attention_forward for a batch whose first prefix_seqs sequences
+    (decode rows) hold their first prefix_tokens positions in the same
+    physical blocks (see pagedkv.h); the same bits, shared splits read once
+    per group of sequences."""
+    S, total, hq, hkv, d, nb, code, out, workspace, ws_bytes = _forward_args(
+        q, k_pool, v_pool, block_tables, context_lens, query_start_loc, max_context_len, sinks, out, workspace,
+        stream)
+    _check(_lib.paged_attention_prefix_forward(
+        q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), code, block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), query_start_loc.data_ptr(), S, total, max_q_len,
+        max_context_len, hq, hkv, d, BLOCK_SIZE, nb, float(scale),
+        None if sinks is None else sinks.data_ptr(), int(prefix_seqs), int(prefix_tokens), out.data_ptr(),
+        workspace.data_ptr(), ws_bytes, _stream_ptr(stream)))
     return out
 
 

@@ -103,6 +103,12 @@ struct AttnParams {
     const uint16_t *k_new, *v_new;
     const int32_t *slots;
     uint16_t *kp_w, *vp_w;
+    // Shared prompt prefix (paged_attention_prefix_forward), else all 0:
+    // sequences 0 .. pre_seqs - 1 are taken in groups of pre_m consecutive
+    // sequences, and splits 0 .. pre_splits - 1 (wholly inside the prefix)
+    // of a group are one item (see prefix_slot). pre_a: slots of the prefix
+    // sequences' own splits (pre_seqs * (max_splits - pre_splits)).
+    int32_t pre_seqs, pre_m, pre_groups, pre_splits, pre_a;
     // Restricted visibility (paged_attention_masked_forward), else null / 0:
     // one ancestor mask word per query row of a tree window, and a sliding
     // window of `window` keys ending at each row's position.
@@ -1038,11 +1044,199 @@ struct ParLds {
     float2 ml[3][NT][64];
 };
 
+// Slot order of a grid with a shared prefix, per KV head (rest = blockIdx /
+// Hkv), longest items first:
+//   group items of the prefix's 1024-key splits  (g fastest),
+//   the prefix sequences' own splits from pre_splits on (s fastest),
+//   every split of the other sequences             (s fastest, split_of_slot),
+//   group items of the prefix's 256-key splits    (g fastest).
+// Returns 1 for a group item (s = its group), 0 for a sequence's split, -1
+// past the grid.
+__device__ inline int prefix_slot(const AttnParams &P, int rest, int &s, int &j) {
+    const int js = min(P.pre_splits, kSplitsA), jl = P.pre_splits - js;
+    int r = rest;
+    if (r < P.pre_groups * jl) {
+        s = r % P.pre_groups;
+        j = kSplitsA + r / P.pre_groups;
+        return 1;
+    }
+    r -= P.pre_groups * jl;
+    if (r < P.pre_a) {
+        s = r % P.pre_seqs;
+        j = P.pre_splits + r / P.pre_seqs;
+        return 0;
+    }
+    r -= P.pre_a;
+    const int others = P.num_seqs - P.pre_seqs;
+    if (r < others * P.max_splits) {
+        s = P.pre_seqs + r % others;
+        j = split_of_slot(r / others, P.max_splits);
+        return 0;
+    }
+    r -= others * P.max_splits;
+    if (r < P.pre_groups * js) {
+        s = r % P.pre_groups;
+        j = r / P.pre_groups;
+        return 1;
+    }
+    return -1;
+}
+
+// One group item: split j of the prefix sequences g * pre_m .. + pre_m - 1,
+// all of them decode rows whose keys of the split lie in the same physical
+// blocks. Wave w streams quarter w once, for a tile holding every member's
+// rows (member m's head hl at tile row m * G + hl): the bits of each row are
+// those of the row alone, since an MFMA's per-element results do not depend
+// on the other rows of its tile and every row is masked by its own position.
+// The block ids are checked: if any quarter of the split is not the same
+// physical blocks for every member, or a member has more than one row, the
+// workgroup computes the members one after another over their own blocks
+// (the rows of a member with more than 32 rows are the prefill shape's).
+template <int D, int KF>
+__device__ void prefix_group_item(const AttnParams &P, int kvh, int grp, int j, int wave, int lane,
+                                  ParLds<D, 1> &lds) {
+    using PoolT = Pool<D, KF>;
+    using Regs = typename PoolT::Regs;
+    constexpr int DT = D / 16, KJ = D / 32;
+    const int g = lane >> 4, n = lane & 15;
+    const int s0 = grp * P.pre_m;
+    const int nm = min(P.pre_m, P.pre_seqs - s0);
+    // member metadata (lane m) and block ids (lane 16 m + i: block i of the
+    // wave's quarter of member m), one round trip
+    const int ks = split_begin(j);
+    const int ql = (split_begin(j + 1) - ks) >> 2;
+    const int kq0 = ks + wave * ql;
+    const int nqb = ql / kBlock;  // blocks per quarter (4 or 16)
+    int mc = 0, ma = 0, mb = 0;
+    if (lane < nm) {
+        mc = P.ctx_lens[s0 + lane];
+        ma = P.qsl[s0 + lane];
+        mb = P.qsl[s0 + lane + 1];
+    }
+    int bidm = -1;
+    {
+        const int m = lane >> 4, i = lane & 15;
+        if (m < nm && i < nqb) {
+            const int jb = kq0 / kBlock + i;
+            const int b = P.bt[(size_t)(s0 + m) * P.max_blocks_per_seq + min(jb, P.max_blocks_per_seq - 1)];
+            bidm = (jb < P.max_blocks_per_seq && b >= 0 && b < P.num_blocks) ? b : -1;
+        }
+    }
+    // shared: every member one decode row whose context holds the whole
+    // quarter, and the same valid block ids as member 0
+    bool ok = true;
+    for (int m = 0; m < nm; ++m) {
+        const int c = __builtin_amdgcn_readlane(mc, m);
+        const int a = __builtin_amdgcn_readlane(ma, m), b = __builtin_amdgcn_readlane(mb, m);
+        ok = ok && b - a == 1 && a >= 0 && b <= P.total_rows && c >= kq0 + ql;
+    }
+    const int lead = __shfl(bidm, lane & 15, 64);
+    const bool mine = (lane >> 4) < nm && (lane & 15) < nqb;
+    ok = ok && !__any(mine && (bidm < 0 || bidm != lead));
+    __shared__ int s_ok[4];
+    if (lane == 0) s_ok[wave] = ok;
+    __syncthreads();
+    const bool shared = s_ok[0] && s_ok[1] && s_ok[2] && s_ok[3];
+
+    const size_t tile = PoolT::tile_bytes;
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * tile;
+    const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * tile;
+    const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_zero_tile);
+    const size_t bstride = (size_t)P.Hkv * tile;
+
+    // One pass: the rows of the tile (per lane: q row, head, position, or
+    // prow -1 for no row), the member whose block ids the keys come from
+    // (lanes 16 src ..) and its context length; writes each row's split state.
+    auto pass = [&](int qrow, int hl, int prow, int src, int ctx) {
+        RowInfo ri;
+        ri.r = 0;
+        ri.hl = hl;
+        ri.prow = prow;
+        RowVis rv;
+        rv.prow = prow;
+        rv.lo = kFarBelow;
+        rv.wbase = kFarAbove;
+        rv.tm = 0xFFFFFFFFu;
+        u32x4_t qop[KJ];
+        load_q<D>(qop, P, qrow, ri, kvh, g);  // row qrow + r, r = 0
+        TileState<DT> st;
+        state_clear(st);
+        const int kq1 = min(kq0 + ql, ctx);
+        for (int kc = kq0; kc < kq1; kc += kStep) {
+            const int li = src * 16 + (kc - kq0) / kBlock;
+            const int b0 = __builtin_amdgcn_readlane(bidm, li);
+            const int b1 = __builtin_amdgcn_readlane(bidm, li + 1);
+            Regs r;
+            PoolT::load(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : zero, b0 >= 0 ? vbase + (size_t)b0 * bstride : zero,
+                        b1 >= 0 ? kbase + (size_t)b1 * bstride : zero, b1 >= 0 ? vbase + (size_t)b1 * bstride : zero,
+                        g, n);
+            PoolT::mask(r, kc, ctx, g);
+            PoolT::template update<false>(st, r, qop, kc, rv, g, P.scale_log2);
+        }
+        if (wave > 0) {
+            lds.ml[wave - 1][0][lane] = make_float2(st.m, st.l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) lds.acc[wave - 1][0][dt][lane] = st.acc[dt];
+        }
+        __syncthreads();
+        if (wave == 0 && prow >= 0) {
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                TileState<DT> o;
+                const float2 ml = lds.ml[w][0][lane];
+                o.m = ml.x;
+                o.l = ml.y;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds.acc[w][0][dt][lane];
+                fold_state(st, o);
+            }
+            const size_t base = ((size_t)qrow * P.Hq + kvh * P.G + hl) * P.max_splits + j;
+            if (g == 0) P.ws_ml[base] = make_float2(st.m, st.l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st.acc[dt];
+        }
+        __syncthreads();  // wave 0 has read the LDS states before the next pass writes them
+    };
+
+    if (shared) {
+        const int m = n / P.G, hl = n - m * P.G;
+        const bool row = m < nm && n < nm * P.G;
+        const int mm = row ? m : 0;
+        // one readlane per member (nm <= 4), so that no lane indexes a register
+        int a = 0, c = 0;
+        for (int k = 0; k < nm; ++k)
+            if (mm == k) {
+                a = __builtin_amdgcn_readlane(ma, k);
+                c = __builtin_amdgcn_readlane(mc, k);
+            }
+        int cmax = 0;
+        for (int k = 0; k < nm; ++k) cmax = max(cmax, __builtin_amdgcn_readlane(mc, k));
+        pass(a, row ? hl : 0, row ? c - 1 : -1, 0, cmax);
+    } else {
+        for (int m = 0; m < nm; ++m) {
+            const int c = __builtin_amdgcn_readlane(mc, m);
+            const int a = __builtin_amdgcn_readlane(ma, m), b = __builtin_amdgcn_readlane(mb, m);
+            const int q_len = b - a, rows = q_len * P.G;
+            if (!(a >= 0 && q_len > 0 && b <= P.total_rows && rows <= kParRows && c - q_len >= 0)) continue;
+            for (int p0 = 0; p0 < rows; p0 += 16) {
+                const int rho = p0 + n;
+                const bool row = rho < rows;
+                const int r = row ? rho / P.G : 0, hl = row ? rho - (rho / P.G) * P.G : 0;
+                pass(a + r, hl, row ? c - q_len + r : -1, m, c);
+            }
+        }
+    }
+}
+
 // TWO: one-tile instances that also take sequences of 17 to 32 rows, in two
 // passes of 16 rows over the same keys (quantized batches with prefill
 // chunks, so that one launch covers decode and verify rows).
-template <int D, int NT, bool PF, bool APPEND, int KF, bool MASKED, bool TWO = false>
-__global__ __launch_bounds__(256, par_waves(D, NT, PF) - (TWO && D == 64 ? 1 : 0)) void attn_parallel(AttnParams P) {
+// PREFIX: the instances of paged_attention_prefix_forward (one tile,
+// unmasked, no append), whose grid is prefix_slot's.
+template <int D, int NT, bool PF, bool APPEND, int KF, bool MASKED, bool TWO = false, bool PREFIX = false>
+__global__ __launch_bounds__(256, par_waves(D, NT, PF) - ((TWO || PREFIX) && D == 64 ? 1 : 0)) void attn_parallel(
+    AttnParams P) {
     constexpr int NPASS = TWO ? 2 : 1;
     using PoolT = Pool<D, KF>;
     using Regs = typename PoolT::Regs;
@@ -1052,8 +1246,20 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - (TWO && D == 64 ? 1 : 0
     const int g = lane >> 4, n = lane & 15;
     const int kvh = blockIdx.x % P.Hkv;
     const int rest = blockIdx.x / P.Hkv;
+    __shared__ ParLds<D, NT> lds;  // quarter states of waves 1-3
     int s, j, ctx, qa, qb;
-    if (!MASKED && P.seq_stride == 0) {
+    static_assert(!PREFIX || (NT == 1 && !APPEND && !MASKED), "prefix instances: one tile, unmasked, no append");
+    if constexpr (PREFIX) {
+        const int kind = prefix_slot(P, rest, s, j);
+        if (kind < 0) return;
+        if (kind == 1) {
+            prefix_group_item<D, KF>(P, kvh, s, j, wave, lane, lds);
+            return;
+        }
+        ctx = P.ctx_lens[s];
+        qa = P.qsl[s];
+        qb = P.qsl[s + 1];
+    } else if (!MASKED && P.seq_stride == 0) {
         if (!balanced_item(P, rest, 16 * NT * NPASS, lane, s, j, ctx, qa, qb)) return;
     } else {
         s = rest % P.seq_stride;
@@ -1222,7 +1428,6 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - (TWO && D == 64 ? 1 : 0
                 }
             }
         }
-        __shared__ ParLds<D, NT> lds;
         if (wave > 0) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -2090,6 +2295,9 @@ static int device_cus() {
 
 // workgroups of the parallel grid
 static int64_t par_grid(const AttnParams &P) {
+    if (P.pre_groups > 0)  // the slots of prefix_slot
+        return (int64_t)P.Hkv * ((int64_t)P.pre_groups * P.pre_splits + P.pre_a +
+                                 (int64_t)(P.num_seqs - P.pre_seqs) * P.max_splits);
     return (int64_t)P.Hkv * (P.seq_stride ? P.seq_stride : P.num_seqs) * P.grid_splits;
 }
 
@@ -2130,7 +2338,13 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
         // them take the sequential shape, and the split and fold launches
         // would have nothing to do.
     } else if (rows_per_seq <= 16) {
-        launch_parallel<D, 1, KF, MASKED>(P, st);
+        if (P.pre_groups > 0) {
+            if constexpr (!MASKED)
+                hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, false, false, true>),
+                                   dim3((unsigned)par_grid(P)), dim3(256), 0, st, P);
+        } else {
+            launch_parallel<D, 1, KF, MASKED>(P, st);
+        }
         if (fold)
             hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 16 * D / 4 / 256), dim3(256), 0, st, P);
     } else {
@@ -2140,10 +2354,20 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
             // quantized tiles, 5 % for bf16; its two-stage variant was slower),
             // takes its decode rows, and sequences of 17 to 32 rows in two
             // passes, in one launch.
-            hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, MASKED, true>), dim3((unsigned)par_grid(P)),
-                               dim3(256), 0, st, P);
+            if (P.pre_groups > 0) {
+                if constexpr (!MASKED)
+                    hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, false, true, true>),
+                                       dim3((unsigned)par_grid(P)), dim3(256), 0, st, P);
+            } else {
+                hipLaunchKernelGGL((attn_parallel<D, 1, false, false, KF, MASKED, true>),
+                                   dim3((unsigned)par_grid(P)), dim3(256), 0, st, P);
+            }
         } else {
-            launch_parallel<D, 2, KF, MASKED>(P, st);
+            // two-tile windows take no prefix groups (a group tile holds
+            // decode rows): their own grid
+            AttnParams P2 = P;
+            P2.pre_seqs = P2.pre_m = P2.pre_groups = P2.pre_splits = P2.pre_a = 0;
+            launch_parallel<D, 2, KF, MASKED>(P2, st);
         }
         if (fold)
             hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 32 * D / 4 / 256), dim3(256), 0, st, P);
@@ -2227,13 +2451,18 @@ struct MaskArgs {
     int32_t window;
 };
 
+struct PrefixArgs {
+    int32_t seqs, tokens;
+};
+
 static int forward_impl(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
                         const int32_t *block_tables, int32_t max_blocks_per_seq,
                         const int32_t *context_lens, const int32_t *query_start_loc, int32_t num_seqs,
                         int32_t total_q_rows, int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                         float scale, const float *sinks, float *out, void *workspace, size_t workspace_bytes,
-                        void *hip_stream, const AppendArgs *app, const MaskArgs *mk) {
+                        void *hip_stream, const AppendArgs *app, const MaskArgs *mk,
+                        const PrefixArgs *pre = nullptr) {
     if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8 && dtype != KV_FP4)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: dtype %d not supported", dtype);
     if (head_dim != 64 && head_dim != 128)
@@ -2253,6 +2482,9 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
     if (mk && mk->tree_mask && max_q_len > 32)
         PKV_FAIL(KV_EINVAL, "paged_attention_masked_forward: tree masks cover 32 window rows, max_q_len is %d",
                  max_q_len);
+    if (pre && (pre->seqs < 0 || pre->tokens < 0))
+        PKV_FAIL(KV_EINVAL, "paged_attention_prefix_forward: prefix_seqs %d and prefix_tokens %d must be >= 0",
+                 pre->seqs, pre->tokens);
     if (mk && mk->tree_mask && !aligned4(mk->tree_mask))
         PKV_FAIL(KV_EINVAL, "paged_attention_masked_forward: tree_mask must be 4-byte aligned");
     if (num_seqs == 0 || total_q_rows == 0) return KV_OK;
@@ -2318,6 +2550,23 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
         const bool restricted = mk && (mk->tree_mask || mk->window > 0);
         if (P.decode_only && !restricted && num_seqs <= 64 && max_splits < 1024) P.seq_stride = 0;
         else P.seq_stride += (5 - num_seqs % 4) % 4;
+    }
+    // Shared prompt prefix: groups of up to four decode sequences (at most
+    // 16 rows per group tile) over the splits wholly inside the prefix. The
+    // fixed (not the balanced) slot order is then prefix_slot's.
+    P.pre_seqs = P.pre_m = P.pre_groups = P.pre_splits = P.pre_a = 0;
+    if (pre && pre->seqs > 1 && P.G <= 8) {
+        const int seqs = std::min(pre->seqs, num_seqs);
+        int js = 0;
+        while (js < max_splits && split_begin(js + 1) <= pre->tokens) ++js;
+        if (js > 0) {
+            P.pre_m = std::min(4, 16 / P.G);
+            P.pre_seqs = seqs;
+            P.pre_groups = (seqs + P.pre_m - 1) / P.pre_m;
+            P.pre_splits = js;
+            P.pre_a = seqs * (max_splits - js);
+            P.seq_stride = num_seqs;
+        }
     }
     P.scale_log2 = scale * kLog2e;
     P.k_new = P.v_new = nullptr;
@@ -2408,6 +2657,21 @@ int paged_attention_forward_noalloc(const void *q, const void *k_pool, const voi
                              query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, ws,
                              pkv::kScratchBytes, hip_stream, nullptr, nullptr);
+}
+
+int paged_attention_prefix_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *context_lens, const int32_t *query_start_loc,
+                                   int32_t num_seqs, int32_t total_q_rows, int32_t max_q_len,
+                                   int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                   const float *sinks, int32_t prefix_seqs, int32_t prefix_tokens, float *out,
+                                   void *workspace, size_t workspace_bytes, void *hip_stream) {
+    const pkv::PrefixArgs pre{prefix_seqs, prefix_tokens};
+    return pkv::forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens,
+                             query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
+                             num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, workspace,
+                             workspace_bytes, hip_stream, nullptr, nullptr, &pre);
 }
 
 int paged_attention_masked_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,

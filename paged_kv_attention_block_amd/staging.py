@@ -39,6 +39,29 @@ class Staged:
     unique_blocks: int           # physical blocks holding the batch's keys
 
 
+def prefix_hint(tables, min_tokens: int = 256):
+    """(prefix_seqs, prefix_tokens) for paged_attention_prefix_forward from
+    the host block tables of a batch (int32 [S, max_blocks]): the run of
+    sequences from 0 whose leading table entries name the same physical
+    blocks as sequence 0's for at least min_tokens positions, and the
+    positions all of them hold in those blocks. (0, 0) when there is none.
+    This is what the block manager knows when it hands out shared blocks."""
+    tables = np.asarray(tables)
+    if tables.shape[0] < 2:
+        return 0, 0
+    first = tables[0]
+    common = []
+    for row in tables[1:]:
+        same = (row == first) & (first >= 0)
+        k = int(np.argmin(same)) if not same.all() else same.size
+        if k * BLOCK_SIZE < min_tokens:
+            break
+        common.append(k)
+    if not common:
+        return 0, 0
+    return len(common) + 1, min(common) * BLOCK_SIZE
+
+
 def _torch_dtype(name):
     """Element type of the pools for a workload dtype ("fp8", "fp4": 8- and
     4-bit pools)."""

@@ -225,3 +225,26 @@ def test_enomem_is_atomic(pk):
     assert pk.kv_pool_stats(p) == before
     with pytest.raises(pk.KVError):
         pk.kv_pool_release(p, 2)                 # the failed sequence was not created
+
+
+def test_prefix_hint_from_host_tables():
+    """staging.prefix_hint reads the run of sequences sharing sequence 0's
+    leading physical blocks off the host tables, and the positions they all
+    hold in those blocks (by hand: 3 sequences share 20, 18 and 25 blocks)."""
+    from paged_kv_attention_block_amd.staging import prefix_hint
+    base = np.arange(100, 140, dtype=np.int32)
+    t = np.full((5, 40), -1, dtype=np.int32)
+    t[0] = base
+    t[1, :20] = base[:20]
+    t[1, 20:30] = np.arange(500, 510)
+    t[2, :18] = base[:18]
+    t[2, 18:25] = np.arange(600, 607)
+    t[3, :25] = base[:25]
+    t[4, :10] = np.arange(700, 710)          # shares nothing: ends the run
+    assert prefix_hint(t) == (4, 18 * 16)
+    assert prefix_hint(t[[0, 4]]) == (0, 0)
+    assert prefix_hint(t[:1]) == (0, 0)
+    t2 = t.copy()
+    t2[1, :15] = base[:15]
+    t2[1, 15:] = 900                          # 15 blocks = 240 tokens < 256: no run
+    assert prefix_hint(t2[:2]) == (0, 0)
