@@ -163,6 +163,34 @@ __device__ inline void fold_state(TileState<DT> &a, const TileState<DT> &b) {
     a.m = M;
 }
 
+// fold_state without branches, for states whose empty members (m = -inf)
+// may hold any finite l and accumulators rather than zeros: an empty b weighs
+// 0 (be = 2^-inf) against a's weight 1, an empty a weighs 0 against b's 1,
+// and otherwise the arithmetic is fold_state's, so every value equals
+// fold_state's over cleared states (the sign of a zero aside, which finalize
+// removes). Both empty: a stays empty. Lets a shape that folds often skip
+// clearing the accumulators it has just folded.
+// (fmaf(x, y, z) with the result in x's register: the compiler's own
+// choice, z's register plus a copy back, costs 16 64-bit moves per fold.)
+__device__ inline float fma_in_place(float x, float y, float z) {
+    asm("v_fma_f32 %0, %0, %1, %2" : "+v"(x) : "v"(y), "v"(z));
+    return x;
+}
+
+template <int DT>
+__device__ inline void fold_state_flat(TileState<DT> &a, const TileState<DT> &b) {
+    const float M = fmaxf(a.m, b.m);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float al = b.m == -INFINITY ? 1.f : fast_exp2(a.m - Mu);
+    const float be = fast_exp2(b.m - Mu);
+    a.l = fmaf(a.l, al, b.l * be);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.acc[dt][i] = fma_in_place(a.acc[dt][i], al, b.acc[dt][i] * be);
+    a.m = M;
+}
+
 // out = acc / (l + sink term); the sink logit (log2 units, -inf if none)
 // takes part in the max. A zero output is written as +0 (x + 0 turns -0 into
 // +0 and keeps every other value): a row's accumulators carry its values
@@ -381,7 +409,7 @@ __device__ inline uint32_t visible8(const RowVis &v, int key0) {
 template <int D, bool SCALED, bool MASKED, bool ALWAYS = false, class KOp, class VOp>
 __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const float (&ksc)[8],
                                  const float (&vsc)[8], const u32x4_t (&qop)[D / 32], int kc, const RowVis &rv,
-                                 int g, float scale_log2) {
+                                 int g, float scale_log2, bool fresh = false) {
     const int prow = rv.prow;
     constexpr int KJ = D / 32, DT = D / 16;
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -439,15 +467,28 @@ __device__ inline void step_core(TileState<D / 16> &st, KOp kop, VOp vop, const 
     // ALWAYS (the prefill shape, where some row's max moves in most steps):
     // the rescale runs unconditionally, the same values (x * 1 == x), so that
     // the accumulators keep one set of registers through the step.
-    if (ALWAYS || __any(alpha != 1.f)) {
+    // fresh (ALWAYS only, uniform): the first step of a quarter whose state
+    // was emptied by its max alone; every row's alpha is 0, so the
+    // accumulators restart from zero in the MFMA instead of being scaled by 0
+    // (the same values; only a zero's sign could differ).
+    if (ALWAYS && fresh) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
-    }
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8_t va = vop(dt);
+            st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, st.acc[dt], 0, 0, 0);
+        }
+    } else {
+        if (ALWAYS || __any(alpha != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8_t va = vop(dt);
-        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, st.acc[dt], 0, 0, 0);
-        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, st.acc[dt], 0, 0, 0);
+            for (int dt = 0; dt < DT; ++dt) st.acc[dt] *= alpha;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16x8_t va = vop(dt);
+            st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, st.acc[dt], 0, 0, 0);
+            st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, st.acc[dt], 0, 0, 0);
+        }
     }
     const float l_new = fmaf(alpha, st.l, rs);
     st.l = has ? l_new : st.l;
@@ -543,11 +584,11 @@ __device__ inline void step_core2(TileState<D / 16> (&st)[2], KOp kop, VOp vop, 
 
 template <int D, bool MASKED, bool ALWAYS = false>
 __device__ inline void step_update(TileState<D / 16> &st, const StepRegs<D> &r, const u32x4_t (&qop)[D / 32], int kc,
-                                   const RowVis &rv, int g, float scale_log2) {
+                                   const RowVis &rv, int g, float scale_log2, bool fresh = false) {
     const float none[8] = {};
     step_core<D, false, MASKED, ALWAYS>(
         st, [&](int tau, int j) { return __builtin_bit_cast(bf16x8_t, r.k[tau][j]); },
-        [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, rv, g, scale_log2);
+        [&](int dt) { return __builtin_bit_cast(bf16x8_t, r.v[dt]); }, none, none, qop, kc, rv, g, scale_log2, fresh);
 }
 
 template <int D, bool MASKED>
@@ -677,7 +718,7 @@ __device__ inline void step_update8x2(TileState<D / 16> (&st)[2], const StepRegs
 
 template <int D, bool MASKED, bool ALWAYS = false>
 __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r, const u32x4_t (&qop)[D / 32],
-                                    int kc, const RowVis &rv, int g, float scale_log2) {
+                                    int kc, const RowVis &rv, int g, float scale_log2, bool fresh = false) {
     float ksc[8], vsc[8];
     step_scales(r, ksc, vsc);
     step_core<D, true, MASKED, ALWAYS>(
@@ -690,7 +731,7 @@ __device__ inline void step_update8(TileState<D / 16> &st, const StepRegs8<D> &r
             const u32x4_t w = r.v[dt >> 1];
             return (dt & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
         },
-        ksc, vsc, qop, kc, rv, g, scale_log2);
+        ksc, vsc, qop, kc, rv, g, scale_log2, fresh);
 }
 
 // Pool access of the parallel and sequential shapes for each tile format
@@ -710,8 +751,8 @@ struct Pool<D, kKvBf16> {
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail<D>(r, kc, ctx, g); }
     template <bool MASKED, bool ALWAYS = false>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
-                                  const RowVis &rv, int g, float sl2) {
-        step_update<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2);
+                                  const RowVis &rv, int g, float sl2, bool fresh = false) {
+        step_update<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2, fresh);
     }
     template <bool MASKED>
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
@@ -731,8 +772,8 @@ struct Pool<D, kKvFp8> {
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail8<D>(r, kc, ctx, g); }
     template <bool MASKED, bool ALWAYS = false>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
-                                  const RowVis &rv, int g, float sl2) {
-        step_update8<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2);
+                                  const RowVis &rv, int g, float sl2, bool fresh = false) {
+        step_update8<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2, fresh);
     }
     template <bool MASKED>
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
@@ -843,12 +884,12 @@ __device__ inline void mask_tail4(StepRegs4<D> &r, int kc, int ctx, int g) {
 
 template <int D, bool MASKED, bool ALWAYS = false>
 __device__ inline void step_update4(TileState<D / 16> &st, const StepRegs4<D> &r, const u32x4_t (&qop)[D / 32],
-                                    int kc, const RowVis &rv, int g, float scale_log2) {
+                                    int kc, const RowVis &rv, int g, float scale_log2, bool fresh = false) {
     float ksc[8], vsc[8];
     step_scales(r, ksc, vsc);
     step_core<D, true, MASKED, ALWAYS>(
         st, [&](int tau, int j) { return fp4x8_to_bf16(r.k[tau][j]); }, [&](int dt) { return fp4x8_to_bf16(r.v[dt]); },
-        ksc, vsc, qop, kc, rv, g, scale_log2);
+        ksc, vsc, qop, kc, rv, g, scale_log2, fresh);
 }
 
 template <int D, bool MASKED>
@@ -873,8 +914,8 @@ struct Pool<D, kKvFp4> {
     __device__ static void mask(Regs &r, int kc, int ctx, int g) { mask_tail4<D>(r, kc, ctx, g); }
     template <bool MASKED, bool ALWAYS = false>
     __device__ static void update(TileState<D / 16> &st, const Regs &r, const u32x4_t (&qop)[D / 32], int kc,
-                                  const RowVis &rv, int g, float sl2) {
-        step_update4<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2);
+                                  const RowVis &rv, int g, float sl2, bool fresh = false) {
+        step_update4<D, MASKED, ALWAYS>(st, r, qop, kc, rv, g, sl2, fresh);
     }
     template <bool MASKED>
     __device__ static void update2(TileState<D / 16> (&st)[2], const Regs &r, const u32x4_t (&qop)[2][D / 32], int kc,
@@ -1708,6 +1749,8 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     state_clear(spl);
     state_clear(qtr);
     fin_ml[wave][lane] = make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) fin_acc[wave][dt][lane] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite, weighed by 0
     const int nsteps = (p_max + kStep) / kStep;
     // One step: stage the piece fetched for step c, fetch step c + 2 into
     // the same registers, then compute step c.
@@ -1732,7 +1775,9 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
                                  reinterpret_cast<const uint16_t *>(buf + PS),
                                  reinterpret_cast<const uint16_t *>(buf + 3 * PS), g, n);
             PoolT::mask(r, kc, ctx, g);
-            PoolT::template update<MASKED, true>(qtr, r, qop, kc, rv, g, P.scale_log2);
+            // the first step of a quarter (quarter lengths divide every split start)
+            const bool fresh = (kc & ((kc < kEdge ? kSplitA / 4 : kSplitB / 4) - 1)) == 0;
+            PoolT::template update<MASKED, true>(qtr, r, qop, kc, rv, g, P.scale_log2, fresh);
         }
         // quarter and split boundaries fall on step boundaries; quarters are
         // kSplitA / 4 keys up to the edge and kSplitB / 4 after it, both
@@ -1741,9 +1786,14 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
         const int se = split_begin(split_index(kc) + 1);
         const int qmask = (next <= kEdge ? kSplitA / 4 : kSplitB / 4) - 1;
         const bool last = c + 1 == nsteps;
+        // Folded states are emptied by their max alone: the accumulators of
+        // an empty quarter are scaled by alpha = 0 in its first step with a
+        // key (the rescale is unconditional here), and fold_state_flat weighs
+        // an empty state's values by 0.
         if ((next & qmask) == 0 || last) {
-            fold_state(spl, qtr);
-            state_clear(qtr);
+            fold_state_flat(spl, qtr);
+            qtr.m = -INFINITY;
+            qtr.l = 0.f;
         }
         if (next == se || last) {
             TileState<DT> fin;
@@ -1752,11 +1802,12 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
             fin.l = ml.y;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) fin.acc[dt] = fin_acc[wave][dt][lane];
-            fold_state(fin, spl);
+            fold_state_flat(fin, spl);
             fin_ml[wave][lane] = make_float2(fin.m, fin.l);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) fin_acc[wave][dt][lane] = fin.acc[dt];
-            state_clear(spl);
+            spl.m = -INFINITY;
+            spl.l = 0.f;
         }
     };
     // two register stages, unrolled so that each stays in fixed registers

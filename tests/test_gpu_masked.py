@@ -372,3 +372,34 @@ def test_rollback_round(pk, dtype):
     err = max_err(out.cpu().numpy(), want)
     print(f"[case] rollback round {dtype}: max abs err {err:.3e}", flush=True)
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("fp4", 128)])
+def test_window_prefill_rows_invariant(pk, dtype, D):
+    """Prefill chunks under a sliding window take the sequential shape, whose
+    walk starts at the step of the lowest key any row of the workgroup sees;
+    with window 600 that start falls inside a 256-key quarter past key 1024.
+    Each sampled row equals itself computed alone (a decode row at its
+    position)."""
+    import torch
+    from paged_kv_attention_block_amd.staging import stage
+    w = custom(dtype, 16, 4, D, [3000, 1800, 900], [200, 40, 64], seed=911 + D, sinks=True)
+    st = stage(w)
+    W = 600
+    print(f"\n[case] window prefill invariance {dtype} D={D} window={W}", flush=True)
+    full = bits(masked(pk, st, w, window=W))
+    qsl = [int(x) for x in w.qsl]
+    rows = []
+    for s in range(len(w.seqs)):
+        rows += [qsl[s], qsl[s] + 15, qsl[s] + 16, qsl[s + 1] - 17, qsl[s + 1] - 1]
+    for i in rows:
+        s = max(k for k in range(len(w.seqs)) if qsl[k] <= i)
+        seq = w.seqs[s]
+        p = seq.ctx - seq.q_len + (i - qsl[s])
+        out = pk.paged_attention_masked_forward(
+            st.q[i:i + 1].contiguous(), st.k_pools[0], st.v_pools[0], st.tables[s:s + 1].contiguous(),
+            torch.tensor([p + 1], dtype=torch.int32, device="cuda"), torch.tensor([0, 1], dtype=torch.int32,
+                                                                                  device="cuda"),
+            1, p + 1, w.scale, sinks=st.sinks, sliding_window=W)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(out)[0], full[i], err_msg=f"row {i}")
