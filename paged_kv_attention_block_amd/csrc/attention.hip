@@ -826,6 +826,23 @@ __device__ inline void load_dw4(uint32_t *d, const uint8_t *src) {
     d[3] = w.w;
 }
 
+// Asynchronous copy of 16 bytes per lane from global memory (sbase + voff,
+// sbase wave-uniform) to LDS (lds + 16 * lane, lds wave-uniform): the
+// gfx950 global-to-LDS load, counted by vmcnt. It has no register result;
+// the compiler does not see the LDS write, so the caller waits for vmcnt and
+// synchronises the workgroup before any wave reads the bytes, and waits
+// again before the workgroup ends. M0 (the LDS address) is not otherwise
+// used by the kernels that call it.
+__device__ inline void lds_copy16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ inline uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+// A wave-uniform load through the scalar cache (read-only data).
+__device__ inline int32_t load_scalar(const int32_t *p) { return *(const __attribute__((address_space(4))) int32_t *)p; }
+
 // Staged copies in LDS (attn_sequential) permute 16-byte pieces so that the
 // 8 or 16 lanes of one LDS cycle read distinct banks: at D = 128 a K piece is
 // one token's run, kept in lds_k_pos order; a V piece c of channel row m's
@@ -1680,27 +1697,29 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     // step's two blocks then start 128 bytes apart modulo 256, so that the 16
     // lanes of one 256-byte LDS cycle that read both blocks hit distinct banks.
     constexpr int PS = (TB + 255) / 256 * 256 + 128;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][4 * PS];
-    // the row state of each wave's tile, touched only at split ends
-    __shared__ f32x4_t fin_acc[4][DT][64];
-    __shared__ float2 fin_ml[4][64];
+    // NB step buffers, filled by asynchronous global-to-LDS copies that hold
+    // no registers: the copies of NB - 1 steps are in flight while a step
+    // computes.
+    constexpr int NB = 4;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[NB][4 * PS];
     const size_t bstride = (size_t)P.Hkv * TB;
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * TB;
     const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * TB;
     const uint8_t *zero = reinterpret_cast<const uint8_t *>(g_zero_tile);
     const int nblk_seq = (ctx + kBlock - 1) / kBlock;
     // Wave w stages part w of every step: parts 0, 1 are the K tiles of the
-    // step's blocks 0, 1; parts 2, 3 their V. Lane l stages pieces l + 64 v.
+    // step's blocks 0, 1; parts 2, 3 their V.
     const int blk = wave & 1;
     const bool is_v = wave >= 2;
     // LDS layout of the staged tiles (see load_step_lds, load_step8 and
     // load_step4): K keeps the token order 0-3, 8-11, 4-7, 12-15 within each
     // 16-piece chunk, V pieces of a channel row are permuted by the row's
-    // bits, scales stay in place. Staged index i = lane + 64 v: a V part
-    // loads piece i and writes it to its position; a K part writes position
-    // i and loads the piece that belongs there (the token order swaps bits 2
-    // and 3 of the token, so it is its own inverse). Either way each group of
-    // 8 lanes writes 128 contiguous bytes, free of bank conflicts.
+    // bits, scales stay in place. A copy writes lane l's 16 bytes to position
+    // l of its 64-piece run, so lane l of copy v loads the piece that belongs
+    // at position i = l + 64 v: both permutations are their own inverses
+    // (the token order swaps bits 2 and 3 of the token; the V permutations
+    // flip low bits of the piece index by its higher bits). Each group of 8
+    // lanes writes 128 contiguous bytes, free of bank conflicts.
     auto k_piece_at = [&](int i) {
         if constexpr (KF == kKvFp4) {
             if (D != 128 || i >= D / 2) return i;  // 8-byte runs in order; scales
@@ -1709,60 +1728,60 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
         }
         return (i >> 4) * kBlock + lds_k_pos(i & 15);
     };
-    auto v_pos_of = [&](int i) {
+    auto v_piece_at = [&](int i) {
         if constexpr (KF == kKvFp4) return i >= D / 2 ? i : lds_v4_piece<D>(i);
         else if constexpr (KF == kKvFp8) return i >= D ? i : (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
         else return (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
     };
-    auto src_piece = [&](int i) { return is_v ? i : k_piece_at(i); };
-    auto lds_pos = [&](int i) { return is_v ? v_pos_of(i) : i; };
 
-    // Block ids in register windows of 64 blocks (32 steps): lane i of bcur
-    // holds table entry 64 bw + i, bnxt the next window, loaded a window
-    // ahead. Entries are checked where they are used, so that no load waits.
+    // The block id of this wave's part of step c, through the scalar cache
+    // (the step loop issues no vector loads of its own, so that its waits
+    // count the copies alone); -1 past the sequence's blocks, whose parts
+    // read the zero tile.
     const int32_t *bt_row = P.bt + (size_t)s * P.max_blocks_per_seq;
-    const int jb_max = min(nblk_seq, P.max_blocks_per_seq);  // blocks past it read the zero tile
-    auto load_bids = [&](int first) { return bt_row[min(first + lane, P.max_blocks_per_seq - 1)]; };
-    // Steps wholly below every row's lowest visible key change no state: the
-    // walk starts at an even step at or below blk_lo (an even start keeps
-    // the two prefetch stages in order).
-    const int c_start = blk_lo > 0 ? blk_lo / (2 * kStep) * 2 : 0;
-    int bw = c_start >> 5;  // window of the steps being computed
-    int bcur = load_bids(64 * bw), bnxt = load_bids(64 * (bw + 1));
-    // Step c's piece into dst; fetches run two steps ahead of the compute
-    // (so into the next window at a window's end) and past the last step
-    // they read the zero tile.
-    auto fetch = [&](u32x4_t (&dst)[NV], int c) {
+    const int jb_max = min(nblk_seq, P.max_blocks_per_seq);
+    auto bid_of = [&](int c) {
         const int jb = 2 * c + blk;
-        const int bc = __builtin_amdgcn_readlane(bcur, jb & 63);
-        const int bn = __builtin_amdgcn_readlane(bnxt, jb & 63);
-        int b = (c >> 5) == bw ? bc : bn;
-        b = (jb < jb_max && b >= 0 && b < P.num_blocks) ? b : -1;
+        const int b = load_scalar(bt_row + min(jb, P.max_blocks_per_seq - 1));
+        return (jb < jb_max && b >= 0 && b < P.num_blocks) ? b : -1;
+    };
+    // This wave's part of step c into buffer c % NB.
+    auto stage = [&](int c, int b) {
         const uint8_t *src = b >= 0 ? (is_v ? vbase : kbase) + (size_t)b * bstride : zero;
+        const uint32_t dst = lds_addr(&lds[c % NB][wave * PS]);
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             if (NP % 64 == 0 || lane + 64 * v < NP)
-                dst[v] = *reinterpret_cast<const u32x4_t *>(src + (size_t)src_piece(lane + 64 * v) * 16);
+                lds_copy16(src, (uint32_t)(is_v ? v_piece_at(lane + 64 * v) : k_piece_at(lane + 64 * v)) * 16,
+                           dst + 1024 * v);
     };
 
-    TileState<DT> spl, qtr;
+    TileState<DT> spl, qtr, fin;  // quarter, split and row states of the wave's tile
     state_clear(spl);
     state_clear(qtr);
-    fin_ml[wave][lane] = make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) fin_acc[wave][dt][lane] = f32x4_t{0.f, 0.f, 0.f, 0.f};  // finite, weighed by 0
+    state_clear(fin);
     const int nsteps = (p_max + kStep) / kStep;
-    // One step: stage the piece fetched for step c, fetch step c + 2 into
-    // the same registers, then compute step c.
-    auto step = [&](int c, u32x4_t (&pre)[NV]) {
-        const int kc = c * kStep;
-        uint8_t *buf = lds[c & 1];
+    // Steps wholly below every row's lowest visible key change no state: the
+    // walk starts at the step holding blk_lo.
+    const int c_start = blk_lo > 0 ? blk_lo / kStep : 0;
+    // The query rows (and visibility words) are in registers before the first
+    // copy: a wait the compiler places for them inside the loop would count
+    // the copies too, and drain them at every step.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-            if (NP % 64 == 0 || lane + 64 * v < NP)
-                *reinterpret_cast<u32x4_t *>(buf + wave * PS + lds_pos(lane + 64 * v) * 16) = pre[v];
-        fetch(pre, c + 2);
+    for (int c = c_start; c < c_start + NB - 1; ++c) stage(c, bid_of(c));
+    int bid_next = bid_of(c_start + NB - 1);
+    for (int c = c_start; c < nsteps; ++c) {
+        const int kc = c * kStep;
+        // This wave's copies of step c are done once at most those of the
+        // NB - 2 steps after it are in flight; the barrier then shows every
+        // wave's part, and that all waves are past step c - 1, whose buffer
+        // the copy of step c + NB - 1 refills.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NB - 2) * NV) : "memory");
         __syncthreads();
+        stage(c + NB - 1, bid_next);
+        bid_next = bid_of(c + NB);
+        const uint8_t *buf = lds[c % NB];
         if (kc <= wave_pmax && (!MASKED || kc + kStep > wave_lo)) {
             Regs r;
             if constexpr (KF == kKvFp8)
@@ -1781,58 +1800,28 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
         }
         // quarter and split boundaries fall on step boundaries; quarters are
         // kSplitA / 4 keys up to the edge and kSplitB / 4 after it, both
-        // powers of two that divide every split start
+        // powers of two that divide every split start. Folded states are
+        // emptied by their max alone: the accumulators of an empty quarter
+        // are scaled by alpha = 0 in its first step with a key (the rescale is
+        // unconditional here), and fold_state_flat weighs an empty state's
+        // values by 0.
         const int next = kc + kStep;
         const int se = split_begin(split_index(kc) + 1);
         const int qmask = (next <= kEdge ? kSplitA / 4 : kSplitB / 4) - 1;
         const bool last = c + 1 == nsteps;
-        // Folded states are emptied by their max alone: the accumulators of
-        // an empty quarter are scaled by alpha = 0 in its first step with a
-        // key (the rescale is unconditional here), and fold_state_flat weighs
-        // an empty state's values by 0.
         if ((next & qmask) == 0 || last) {
             fold_state_flat(spl, qtr);
             qtr.m = -INFINITY;
             qtr.l = 0.f;
         }
         if (next == se || last) {
-            TileState<DT> fin;
-            const float2 ml = fin_ml[wave][lane];
-            fin.m = ml.x;
-            fin.l = ml.y;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) fin.acc[dt] = fin_acc[wave][dt][lane];
             fold_state_flat(fin, spl);
-            fin_ml[wave][lane] = make_float2(fin.m, fin.l);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) fin_acc[wave][dt][lane] = fin.acc[dt];
             spl.m = -INFINITY;
             spl.l = 0.f;
         }
-    };
-    // two register stages, unrolled so that each stays in fixed registers
-    u32x4_t pre0[NV], pre1[NV];
-    fetch(pre0, c_start);
-    fetch(pre1, c_start + 1);
-    // An even number of steps keeps the two stages in one order at the loop
-    // head; a step past the last computes nothing and folds empty states,
-    // which is exact.
-    const int nsteps2 = (nsteps + 1) & ~1;
-    for (int w0 = c_start; w0 < nsteps2; w0 = (w0 & ~31) + 32, ++bw) {
-        const int wend = min((w0 & ~31) + 32, nsteps2);
-        for (int c = w0; c < wend; c += 2) {
-            step(c, pre0);
-            step(c + 1, pre1);
-        }
-        bcur = bnxt;
-        bnxt = load_bids(64 * (bw + 2));
     }
-    TileState<DT> fin;
-    const float2 ml = fin_ml[wave][lane];
-    fin.m = ml.x;
-    fin.l = ml.y;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) fin.acc[dt] = fin_acc[wave][dt][lane];
+    // the copies past the last step land before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     f32x4_t o[DT];
     finalize(fin, sink_log2(P, kvh, ri.hl), o);
     store_out<DT>(P, q0, ri, kvh, g, o);
