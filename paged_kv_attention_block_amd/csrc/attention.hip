@@ -857,6 +857,31 @@ __device__ inline int lds_v4_piece(int pc) {
     else return (pc & ~1) | ((pc & 1) ^ (((pc >> 3) ^ (pc >> 4)) & 1));
 }
 
+// LDS copies of a tile (16-byte pieces, staged by global-to-LDS copies that
+// write lane l's piece at position l): the piece that belongs at position i,
+// for the layouts load_step_lds, load_step8 and load_step4 read. K keeps the
+// token order 0-3, 8-11, 4-7, 12-15 within each 16-piece chunk; V pieces of
+// a channel row are permuted by the row's bits; scales stay in place. Both
+// permutations are their own inverses (the token order swaps bits 2 and 3
+// of the token; the V permutations flip low bits of the piece index by its
+// higher bits), so position and source piece may be read either way.
+template <int D, int KF>
+__device__ inline int lds_k_piece(int i) {
+    if constexpr (KF == kKvFp4) {
+        if (D != 128 || i >= D / 2) return i;  // 8-byte runs in order; scales
+    } else if constexpr (KF == kKvFp8) {
+        if (i >= D) return i;  // scales
+    }
+    return (i >> 4) * kBlock + lds_k_pos(i & 15);
+}
+template <int D, int KF>
+__device__ inline int lds_v_piece(int i) {
+    if constexpr (KF == kKvFp4) return i >= D / 2 ? i : lds_v4_piece<D>(i);
+    else if constexpr (KF == kKvFp8) return i >= D ? i : (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
+    else return (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
+}
+
+
 // Operands of one chunk from 4-bit tiles kt0/vt0 and kt1/vt1 (blocks 0, 1),
 // in the pools (LDS = false) or staged in LDS.
 template <int D, bool LDS>
@@ -1101,6 +1126,7 @@ struct ParLds {
     f32x4_t acc[3][NT][D / 16][64];
     float2 ml[3][NT][64];
 };
+
 
 // Slot order of a grid with a shared prefix, per KV head (rest = blockIdx /
 // Hkv), longest items first:
@@ -1711,28 +1737,9 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
     // step's blocks 0, 1; parts 2, 3 their V.
     const int blk = wave & 1;
     const bool is_v = wave >= 2;
-    // LDS layout of the staged tiles (see load_step_lds, load_step8 and
-    // load_step4): K keeps the token order 0-3, 8-11, 4-7, 12-15 within each
-    // 16-piece chunk, V pieces of a channel row are permuted by the row's
-    // bits, scales stay in place. A copy writes lane l's 16 bytes to position
-    // l of its 64-piece run, so lane l of copy v loads the piece that belongs
-    // at position i = l + 64 v: both permutations are their own inverses
-    // (the token order swaps bits 2 and 3 of the token; the V permutations
-    // flip low bits of the piece index by its higher bits). Each group of 8
-    // lanes writes 128 contiguous bytes, free of bank conflicts.
-    auto k_piece_at = [&](int i) {
-        if constexpr (KF == kKvFp4) {
-            if (D != 128 || i >= D / 2) return i;  // 8-byte runs in order; scales
-        } else if constexpr (KF == kKvFp8) {
-            if (i >= D) return i;  // scales
-        }
-        return (i >> 4) * kBlock + lds_k_pos(i & 15);
-    };
-    auto v_piece_at = [&](int i) {
-        if constexpr (KF == kKvFp4) return i >= D / 2 ? i : lds_v4_piece<D>(i);
-        else if constexpr (KF == kKvFp8) return i >= D ? i : (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
-        else return (i >> 1) * 2 + lds_v_half(i >> 1, i & 1);
-    };
+    // LDS layout of the staged tiles: lds_k_piece, lds_v_piece (lane l of
+    // copy v loads the piece that belongs at position l + 64 v). Each group
+    // of 8 lanes writes 128 contiguous bytes, free of bank conflicts.
 
     // The block id of this wave's part of step c, through the scalar cache
     // (the step loop issues no vector loads of its own, so that its waits
@@ -1752,7 +1759,8 @@ __global__ __launch_bounds__(256, 2) void attn_sequential(AttnParams P) {
 #pragma unroll
         for (int v = 0; v < NV; ++v)
             if (NP % 64 == 0 || lane + 64 * v < NP)
-                lds_copy16(src, (uint32_t)(is_v ? v_piece_at(lane + 64 * v) : k_piece_at(lane + 64 * v)) * 16,
+                lds_copy16(src,
+                           (uint32_t)(is_v ? lds_v_piece<D, KF>(lane + 64 * v) : lds_k_piece<D, KF>(lane + 64 * v)) * 16,
                            dst + 1024 * v);
     };
 
