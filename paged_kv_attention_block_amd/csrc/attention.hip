@@ -826,19 +826,34 @@ __device__ inline void load_dw4(uint32_t *d, const uint8_t *src) {
     d[3] = w.w;
 }
 
-// Asynchronous copy of 16 bytes per lane from global memory (sbase + voff,
-// sbase wave-uniform) to LDS (lds + 16 * lane, lds wave-uniform): the
-// gfx950 global-to-LDS load, counted by vmcnt. It has no register result;
-// the compiler does not see the LDS write, so the caller waits for vmcnt and
-// synchronises the workgroup before any wave reads the bytes, and waits
-// again before the workgroup ends. M0 (the LDS address) is not otherwise
-// used by the kernels that call it.
+// Asynchronous copy of 16 bytes per lane from global memory (sbase + voff)
+// to LDS (lds + 16 * lane): the gfx950 global-to-LDS load, counted by vmcnt.
+// sbase and lds must be wave-uniform; both are read from the first lane into
+// scalar registers. It has no register result; the compiler does not see
+// the LDS write, so the caller waits for vmcnt and synchronises the
+// workgroup before any wave reads the bytes, and waits again before the
+// workgroup ends. M0 carries the LDS address and is restored afterwards.
 __device__ inline void lds_copy16(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
+    // (readfirstlane returns int: each half goes through uint32_t before it
+    // widens, or a low half with bit 31 set would fill the high half with ones)
+    const uint64_t a = (uint64_t)(uintptr_t)sbase;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"((const void *)(uintptr_t)u), "s"(l)
+        : "memory");
 }
 __device__ inline uint32_t lds_addr(const void *p) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
 }
 // A wave-uniform load through the scalar cache (read-only data).
 __device__ inline int32_t load_scalar(const int32_t *p) { return *(const __attribute__((address_space(4))) int32_t *)p; }
