@@ -137,3 +137,19 @@ def test_rejects_negative_hint(pk):
         _prefix(pk, st, w, -1, 100)
     with pytest.raises(KVError):
         _prefix(pk, st, w, 2, -5)
+
+
+@pytest.mark.parametrize("dtype,shared", [("bf16", 1100), ("bf16", 1280), ("bf16", 1700), ("bf16", 2048),
+                                          ("bf16", 600), ("bf16", 700), ("fp4", 1700), ("fp8", 1300)])
+def test_prefix_ending_inside_a_split(pk, dtype, shared):
+    """Prompts ending inside a quarter and on a quarter edge, in 1024-key
+    splits and in 256-key ones (600, 700): the splits wholly inside the
+    prompt are group items, the one holding its end and all later ones are
+    each sequence's own; groups of four sequences (G = 4) with tails of
+    different lengths. The output is the plain forward's, bit for bit."""
+    rng = np.random.default_rng(shared + (dtype == "fp4"))
+    n = 9
+    ctxs = [shared + int(x) for x in rng.integers(1, 900, size=n)] + [1500]
+    w = custom(dtype, 16, 4, 128, ctxs, [1] * len(ctxs), seed=int(rng.integers(1 << 30)), sinks=True,
+               shared_prefix=shared, n_shared=n)
+    _check(pk, w, n, (shared // 16) * 16, oracle_sample=[0, 4, 8, 9])
