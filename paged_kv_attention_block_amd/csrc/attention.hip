@@ -1434,7 +1434,10 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - ((TWO || PREFIX) && D =
             const bool fused = APPEND && KF == kKvBf16 && kq0 <= pn && pn < kq1;
             // The new token's K and V rows wait in LDS (this wave's slot) for the
             // step that holds pn, rather than in registers through the loop.
+            // Staged after the wave's first K/V loads are issued, so that the
+            // two round trips overlap.
             __shared__ __attribute__((aligned(16))) uint16_t s_new[APPEND ? 4 : 1][2][D];
+            auto stage_new = [&]() {
             if (APPEND && KF == kKvBf16 && fused) {
                 const size_t rowoff = ((size_t)s * P.Hkv + kvh) * D;
                 const int slot = P.slots[s];
@@ -1457,6 +1460,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - ((TWO || PREFIX) && D =
                         P.vp_w[tb * kBlock + (size_t)c * kBlock + slot % kBlock] = P.v_new[rowoff + c];
                 }
             }
+            };
             const size_t tile = PoolT::tile_bytes;
             const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * tile;
             const uint8_t *vbase = reinterpret_cast<const uint8_t *>(P.vp) + (size_t)kvh * tile;
@@ -1511,6 +1515,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - ((TWO || PREFIX) && D =
                 Regs r0, r1;
                 if (!MASKED || kstart < kq1) fetch(r0, kstart);
                 if (kstart + kStep < kq1) fetch(r1, kstart + kStep);
+                stage_new();
                 for (int kc = kstart; kc < kq1; kc += 2 * kStep) {
                     compute(r0, kc);
                     if (kc + 2 * kStep < kq1) fetch(r0, kc + 2 * kStep);
@@ -1523,6 +1528,7 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - ((TWO || PREFIX) && D =
                 for (int kc = kstart; kc < kq1; kc += kStep) {
                     Regs r;
                     fetch(r, kc);
+                    if (kc == kstart) stage_new();  // (a fused quarter holds pn, so it has a step)
                     compute(r, kc);
                 }
             }
