@@ -1587,7 +1587,9 @@ __global__ __launch_bounds__(256, par_waves(D, NT, PF) - ((TWO || PREFIX) && D =
 // d and every lane of a cell repeats the same m, l fold. The split states are
 // folded left to right, sixteen per round trip, then finalized.
 // ---------------------------------------------------------------------------
-template <int D, int NT>
+// WIDE: the instance for rows of 17 to 32 split slots (launched when the
+// batch has that many), whose registers the others do not pay for.
+template <int D, int NT, bool WIDE = false>
 __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
     constexpr int LPC = D / 4;         // lanes per cell
     constexpr int CPG = 256 / LPC;     // cells per workgroup
@@ -1617,8 +1619,40 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
         j0 = split_index(max(P.ctx_lens[s] - q_len - P.window + 1, 0));
         j1 = min(j0 + P.grid_splits, P.max_splits);
     }
-    // sixteen split states per round trip
     constexpr int U = 16;
+    if (WIDE && j1 - j0 > U && j1 - j0 <= 2 * U) {
+        // Two round trips either way: the (m, l) of every slot first, then
+        // the accumulators of the slots that hold a state (an empty slot's
+        // were never written).
+        float2 xml[2 * U];
+        f32x4_t xacc[2 * U];
+#pragma unroll
+        for (int u = 0; u < 2 * U; ++u) xml[u] = j0 + u < j1 ? P.ws_ml[base0 + j0 + u] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int u = 0; u < 2 * U; ++u) {
+            xacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (xml[u].x != -INFINITY) xacc[u] = *reinterpret_cast<const f32x4_t *>(P.ws_acc + (base0 + j0 + u) * D + e);
+        }
+#pragma unroll
+        for (int u = 0; u < 2 * U; ++u) {
+            if (xml[u].x == -INFINITY) continue;
+            if (m == -INFINITY) {
+                m = xml[u].x;
+                l = xml[u].y;
+                acc = xacc[u];
+                continue;
+            }
+            const float M = fmaxf(m, xml[u].x);
+            const float al = fast_exp2(m - M);
+            const float be = fast_exp2(xml[u].x - M);
+            l = fmaf(l, al, xml[u].y * be);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(acc[i], al, xacc[u][i] * be);
+            m = M;
+        }
+        j0 = j1;  // done
+    }
+    // sixteen split states per round trip
     for (int j = j0; j < j1; j += U) {
         float2 xml[U];
         f32x4_t xacc[U];
@@ -2398,6 +2432,15 @@ static void launch_parallel(const AttnParams &P, hipStream_t st) {
     else launch_parallel_as<D, NT, false, kKvBf16, false>(P, st);
 }
 
+template <int D, int NT>
+static void launch_fold(const AttnParams &P, hipStream_t st) {
+    const dim3 grid(P.num_seqs, P.Hkv, 16 * NT * D / 4 / 256);
+    if (P.grid_splits > 16 && P.grid_splits <= 32)
+        hipLaunchKernelGGL((attn_fold<D, NT, true>), grid, dim3(256), 0, st, P);
+    else
+        hipLaunchKernelGGL((attn_fold<D, NT, false>), grid, dim3(256), 0, st, P);
+}
+
 template <int D, int KF, bool MASKED>
 static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
     const int rows_per_seq = max_q_len * P.G;
@@ -2415,7 +2458,7 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
             launch_parallel<D, 1, KF, MASKED>(P, st);
         }
         if (fold)
-            hipLaunchKernelGGL((attn_fold<D, 1>), dim3(P.num_seqs, P.Hkv, 16 * D / 4 / 256), dim3(256), 0, st, P);
+            launch_fold<D, 1>(P, st);
     } else {
         if (rows_per_seq > kParRows) {
             // A batch with prefill chunks: the one-tile instance, which holds
@@ -2439,7 +2482,7 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
             launch_parallel<D, 2, KF, MASKED>(P2, st);
         }
         if (fold)
-            hipLaunchKernelGGL((attn_fold<D, 2>), dim3(P.num_seqs, P.Hkv, 32 * D / 4 / 256), dim3(256), 0, st, P);
+            launch_fold<D, 2>(P, st);
     }
     if (rows_per_seq > kParRows) {
         const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
