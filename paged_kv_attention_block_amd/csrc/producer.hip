@@ -9,18 +9,25 @@
 // pos * theta^(-2i / rotary_dim), and the result is rounded once to bf16; Q
 // goes to q_out, K and V (unchanged) into the bf16 pools at their slots.
 //
-// Workgroup: 16 consecutive tokens x up to kHeadsPerWG rows of the Q, K and
-// V heads (in that order). Lane group t (16 lanes) owns token t; lane p of it
-// owns the D/16 consecutive dimensions p*D/16 .. p*D/16 + D/16 - 1, so that a
-// row loads and stores in 16-byte pieces and the K tile layout
-// [D/8][16][8] takes whole pieces. The NeoX partner of a dimension sits
-// rotary_dim/2 / (D/16) lanes away, in the same register. The angles are
-// computed once per workgroup: the angle in float64, reduced to [-pi, pi],
-// then sine and cosine in float32.
+// Workgroup: 16 consecutive tokens x up to kHeadsPerWG heads of one kind (Q,
+// K or V). Lane group t (16 lanes) owns token t; lane p of it owns the D/16
+// consecutive dimensions p*D/16 .. p*D/16 + D/16 - 1, held as packed bf16
+// pairs, so that a row loads and stores in 16-byte pieces and the K tile
+// layout [D/8][16][8] takes whole pieces. The NeoX partner of a dimension
+// sits rotary_dim/2 / (D/16) lanes away, in the same register (8 lanes when
+// the whole head turns: one DPP row rotation). A Q or K workgroup computes
+// its 16 x rotary_dim/2 angles once, spread over all its lanes and shared
+// through LDS: the angle in float64, reduced by multiples of pi/2, then
+// short polynomials in float32. The norm weights fold into the rotation
+// factors (w cos, and the partner's weight times the signed sine), and each
+// row is rounded to bf16 once by the hardware's packed conversion (nearest,
+// ties to even). A V workgroup only moves rows: whole blocks turn into the
+// [D][16] tile through LDS.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "pagedkv.h"
 #include "status.h"
@@ -33,6 +40,8 @@ constexpr int kHeadsPerWG = 4;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 struct ProdArgs {
     const uint16_t *q, *k, *v;  // [n][H][D] bf16
@@ -43,201 +52,270 @@ struct ProdArgs {
     uint16_t *kp, *vp;          // pools
     int n, Hq, Hkv, num_blocks, rotary_dim;
     float eps, weight_offset;
-    double log2_theta;
+    double freq_step;  // 2 log2(theta) / rotary_dim: pair i turns at 2^(-i freq_step) per position
 };
 
-__device__ inline float bf16_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+// A row piece is held as packed bf16 pairs: word i has dimension 2i in its
+// low half and 2i + 1 in its high half.
+__device__ inline float lo_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float hi_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+__device__ inline float half_f32(uint32_t w, int e) { return e & 1 ? hi_f32(w) : lo_f32(w); }
 
-// Nearest bf16, ties to even (finite inputs).
-__device__ inline uint16_t f32_to_bf16(float f) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, f);
-    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+// Two floats to a bf16 pair, each rounded to the nearest, ties to even
+// (one packed conversion instruction on gfx950).
+__device__ inline uint32_t pack_bf16(float a, float b) {
+    const f32x2_t f = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-template <int CPT>
-__device__ inline void load_row(const uint16_t *src, uint16_t (&x)[CPT]) {
-    if constexpr (CPT == 4) {
+template <int W>
+__device__ inline void load_words(const uint16_t *src, uint32_t (&x)[W]) {
+    if constexpr (W == 2) {
         const u32x2_t w = *reinterpret_cast<const u32x2_t *>(src);
-        __builtin_memcpy(x, &w, 8);
+        x[0] = w.x;
+        x[1] = w.y;
     } else {
 #pragma unroll
-        for (int c = 0; c < CPT; c += 8) {
-            const u32x4_t w = *reinterpret_cast<const u32x4_t *>(src + c);
-            __builtin_memcpy(x + c, &w, 16);
+        for (int c = 0; c < W; c += 4) {
+            const u32x4_t w = *reinterpret_cast<const u32x4_t *>(src + 2 * c);
+            x[c] = w.x;
+            x[c + 1] = w.y;
+            x[c + 2] = w.z;
+            x[c + 3] = w.w;
         }
     }
 }
 
-template <int CPT>
-__device__ inline void store_row(uint16_t *dst, const uint16_t (&x)[CPT]) {
-    if constexpr (CPT == 4) {
-        u32x2_t w;
-        __builtin_memcpy(&w, x, 8);
-        *reinterpret_cast<u32x2_t *>(dst) = w;
+template <int W>
+__device__ inline void store_words(uint16_t *dst, const uint32_t (&x)[W]) {
+    if constexpr (W == 2) {
+        *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{x[0], x[1]};
     } else {
 #pragma unroll
-        for (int c = 0; c < CPT; c += 8) {
-            u32x4_t w;
-            __builtin_memcpy(&w, x + c, 16);
-            *reinterpret_cast<u32x4_t *>(dst + c) = w;
-        }
+        for (int c = 0; c < W; c += 4)
+            *reinterpret_cast<u32x4_t *>(dst + 2 * c) = u32x4_t{x[c], x[c + 1], x[c + 2], x[c + 3]};
     }
+}
+
+// Lane (i + n) mod 16 of the lane's 16-lane row (DPP row rotation).
+template <int N>
+__device__ inline float row_ror(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sine and cosine of an angle held in float64. The angle is reduced by the
+// nearest multiple q of pi/2 in float64 (one fused multiply-add with the
+// double-precision pi/2), leaving |r| <= pi/4, which goes to float32; the
+// Taylor series of sin r to r^9 and of cos r to r^10 are below 2e-9 from
+// the exact values there, and q mod 4 picks and signs the pair:
+// sin(q pi/2 + r) is sin r, cos r, -sin r, -cos r and the cosine is
+// cos r, -sin r, -cos r, sin r for q = 0, 1, 2, 3 (signs set on the sign
+// bit).
+__device__ inline void sincos_turned(double ang, float &s, float &c) {
+    const double q = rint(ang * (2.0 / M_PI));
+    const float r = (float)fma(-q, M_PI_2, ang);
+    const int k = (int)q;  // the quadrant is k mod 4 (two's complement keeps it for k < 0)
+    const float r2 = r * r;
+    float ps = fmaf(r2, 1.f / 362880.f, -1.f / 5040.f);
+    ps = fmaf(ps, r2, 1.f / 120.f);
+    ps = fmaf(ps, r2, -1.f / 6.f);
+    const float sr = fmaf(ps * r2, r, r);
+    float pc = fmaf(r2, -1.f / 3628800.f, 1.f / 40320.f);
+    pc = fmaf(pc, r2, -1.f / 720.f);
+    pc = fmaf(pc, r2, 1.f / 24.f);
+    pc = fmaf(pc, r2, -0.5f);
+    const float cr = fmaf(pc, r2, 1.f);
+    const float a = (k & 1) ? cr : sr, b = (k & 1) ? sr : cr;
+    s = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a) ^ ((uint32_t)(k & 2) << 30));
+    c = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) ^ ((uint32_t)((k + 1) & 2) << 30));
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
-    constexpr int CPT = D / 16;
+    constexpr int CPT = D / 16, W = CPT / 2;
     const int tid = threadIdx.x;
     const int t = tid >> 4, part = tid & 15, lane = tid & 63;
     const int i0 = blockIdx.x * kBlk;
     const int tok = i0 + t;
     const bool have = tok < A.n;
-    const int half = A.rotary_dim / 2;
-    const int shift = half / CPT;  // lanes between NeoX partners
+
+    // Head groups: the Q heads kHeadsPerWG at a time, then the K heads, then
+    // the V heads (the last group of each kind may hold fewer), so that a
+    // workgroup's rows are all of one kind.
+    const int gq = (A.Hq + kHeadsPerWG - 1) / kHeadsPerWG, gk = (A.Hkv + kHeadsPerWG - 1) / kHeadsPerWG;
+    const int gy = blockIdx.y;
+    const int kind = gy < gq ? 0 : gy < gq + gk ? 1 : 2;  // Q, K, V
+    const int head0 = (kind == 0 ? gy : kind == 1 ? gy - gq : gy - gq - gk) * kHeadsPerWG;
+    const int H = kind == 0 ? A.Hq : A.Hkv;
+    const int nh = min(H - head0, kHeadsPerWG);
 
     __shared__ int s_slot[kBlk];
-    __shared__ int s_full;
-    __shared__ __attribute__((aligned(16))) uint16_t sv[kBlk][D];
+    __shared__ int s_pos[kBlk];
     __shared__ double s_inv_freq[D / 2];  // theta^(-2i / rotary_dim), i < rotary_dim / 2
-    if (tid < half) s_inv_freq[tid] = exp2(-(2.0 * tid / A.rotary_dim) * A.log2_theta);
-    if (tid < kBlk) {
-        const int i = i0 + tid;
-        const int sl = i < A.n ? A.slots[i] : -1;
-        s_slot[tid] = (sl >= 0 && sl < A.num_blocks * kBlk) ? sl : -1;
-    }
+    // Q and K workgroups: (cos, sin) of token t's pair index i, [kBlk][D/2];
+    // V workgroups: their rows, [kHeadsPerWG][kBlk][D] bf16
+    constexpr int kCsBytes = kBlk * (D / 2) * 8, kVBytes = kHeadsPerWG * kBlk * D * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char s_u[kCsBytes > kVBytes ? kCsBytes : kVBytes];
+    float2(&s_cs)[kBlk][D / 2] = *reinterpret_cast<float2(*)[kBlk][D / 2]>(s_u);
+    uint16_t(&sv)[kHeadsPerWG][kBlk][D] = *reinterpret_cast<uint16_t(*)[kHeadsPerWG][kBlk][D]>(s_u);
 
-    // The rows of the workgroup's heads are loaded first, so that their
-    // latency overlaps the angle arithmetic.
-    const int Htot = A.Hq + 2 * A.Hkv;
-    const int h0 = blockIdx.y * kHeadsPerWG;
-    const int nh = min(Htot - h0, kHeadsPerWG);
-    auto kind_of = [&](int hh) { return hh < A.Hq ? 0 : hh < A.Hq + A.Hkv ? 1 : 2; };  // Q, K, V
-    auto head_of = [&](int hh) { return hh < A.Hq ? hh : hh < A.Hq + A.Hkv ? hh - A.Hq : hh - A.Hq - A.Hkv; };
-    uint16_t xs[kHeadsPerWG][CPT];
+    // Every global read is issued up front, the per-token ones first, so
+    // that one memory latency covers them all and the angle arithmetic
+    // overlaps the row reads (indices clamped to the last token, n >= 1, so
+    // that no load sits in a branch of its own; the clamped values are
+    // masked below).
+    const int slot_g = A.slots[min(i0 + (tid & (kBlk - 1)), A.n - 1)];
+    const int pos_g = A.pos[min(i0 + (tid & (kBlk - 1)), A.n - 1)];
+    const uint16_t *wsrc = kind == 0 ? A.qw : kind == 1 ? A.kw : nullptr;
+    uint32_t wv[W];  // the lane's dimensions of the kind's norm weights
+    if (wsrc) load_words<W>(wsrc + part * CPT, wv);
+    const uint16_t *rows_in = kind == 0 ? A.q : kind == 1 ? A.k : A.v;
+    uint32_t xs[kHeadsPerWG][W];
 #pragma unroll
-    for (int j = 0; j < kHeadsPerWG; ++j) {
-        const int hh = h0 + min(j, nh - 1);
-        const int kind = kind_of(hh), head = head_of(hh);
-        const int H = kind == 0 ? A.Hq : A.Hkv;
-        const uint16_t *src = (kind == 0 ? A.q : kind == 1 ? A.k : A.v) +
-                              ((size_t)(have ? tok : 0) * H + head) * D + part * CPT;
-        load_row<CPT>(src, xs[j]);
-    }
+    for (int j = 0; j < kHeadsPerWG; ++j)
+        load_words<W>(rows_in + ((size_t)(have ? tok : 0) * H + head0 + min(j, nh - 1)) * D + part * CPT, xs[j]);
+    if (tid < kBlk) s_slot[tid] = (i0 + tid < A.n && slot_g >= 0 && slot_g < A.num_blocks * kBlk) ? slot_g : -1;
 
-    __syncthreads();
-    // cosine and sine of the lane's dimensions (identity past rotary_dim):
-    // lanes of the lower half of each pair compute them, their partners
-    // `shift` lanes up take them by shuffle
-    float cs[CPT], sn[CPT];
-    {
-        const double p = have ? (double)A.pos[tok] : 0.0;
-        const bool lower = part * CPT < half;
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) {
-            const int c = part * CPT + e;
-            float cv = 1.f, sv_ = 0.f;
-            if (lower) {
-                const double ang = p * s_inv_freq[c];
-                const double turns = rint(ang * (1.0 / (2.0 * M_PI)));
-                sincosf((float)fma(-turns, 2.0 * M_PI, ang), &sv_, &cv);
-            }
-            const int src = lower || !shift ? lane : lane - shift;
-            const float co = __shfl(cv, src, 64), so = __shfl(sv_, src, 64);
-            const bool rot = c < A.rotary_dim;
-            cs[e] = rot ? co : 1.f;
-            sn[e] = rot ? so : 0.f;
-        }
-    }
-    if (tid < 64) {
+    if (kind == 2) {
+        // V rows go into the pools unchanged. Tile [D][16]: when the 16
+        // tokens fill one block in order, the rows turn through LDS and
+        // leave in 16-byte pieces of 8 tokens; otherwise value by value.
+        __syncthreads();
+        const int slot = s_slot[t];
         const int sl0 = s_slot[0];
-        const bool ok = tid >= kBlk || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlk == 0);
-        const bool full = __all(ok);
-        if (tid == 0) s_full = full;
+        const int li = lane & (kBlk - 1);
+        const bool full = __all(lane >= kBlk || (s_slot[li] >= 0 && s_slot[li] == sl0 + li && sl0 % kBlk == 0));
+        if (full) {
+#pragma unroll
+            for (int j = 0; j < kHeadsPerWG; ++j)
+                if (j < nh) store_words<W>(&sv[j][t][part * CPT], xs[j]);
+            __syncthreads();
+            for (int pc = tid; pc < nh * 2 * D; pc += 256) {  // row j, piece q: channel q/2, tokens 8 (q&1) .. +7
+                const int j = pc / (2 * D), q = pc - j * 2 * D;
+                const int c = q >> 1, t0 = (q & 1) * 8;
+                uint32_t b[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    b[e] = (uint32_t)sv[j][t0 + 2 * e][c] | ((uint32_t)sv[j][t0 + 2 * e + 1][c] << 16);
+                uint16_t *tile = A.vp + ((size_t)(sl0 / kBlk) * A.Hkv + head0 + j) * kBlk * D;
+                *reinterpret_cast<u32x4_t *>(tile + (size_t)q * 8) = u32x4_t{b[0], b[1], b[2], b[3]};
+            }
+        } else if (have && slot >= 0) {
+#pragma unroll
+            for (int j = 0; j < kHeadsPerWG; ++j) {
+                if (j >= nh) break;
+                uint16_t *tile = A.vp + ((size_t)(slot / kBlk) * A.Hkv + head0 + j) * kBlk * D;
+#pragma unroll
+                for (int e = 0; e < CPT; ++e)
+                    tile[(size_t)(part * CPT + e) * kBlk + slot % kBlk] =
+                        (uint16_t)(e & 1 ? xs[j][e / 2] >> 16 : xs[j][e / 2] & 0xFFFFu);
+            }
+        }
+        return;
+    }
+
+    const int half = A.rotary_dim / 2;
+    const int shift = half / CPT;  // lanes between NeoX partners; 8 when the whole head turns
+    if (tid < half) s_inv_freq[tid] = exp2(-(double)tid * A.freq_step);
+    if (tid < kBlk) s_pos[tid] = i0 + tid < A.n ? pos_g : 0;
+    __syncthreads();
+    // the workgroup's 16 x rotary_dim/2 angles, once each, over all lanes;
+    // when rotary_dim/2 is a power of two a lane keeps one pair index and
+    // steps over the tokens
+    if (half > 0 && (half & (half - 1)) == 0) {
+        const int lg = __builtin_ctz(half);
+        const int i = tid & (half - 1);
+        const double f = s_inv_freq[i];
+        for (int tt = tid >> lg; tt < kBlk; tt += 256 >> lg) {
+            float sv_, cv;
+            sincos_turned((double)s_pos[tt] * f, sv_, cv);
+            s_cs[tt][i] = make_float2(cv, sv_);
+        }
+    } else {
+        for (int idx = tid; idx < kBlk * half; idx += 256) {
+            const int tt = idx / half, i = idx - tt * half;
+            float sv_, cv;
+            sincos_turned((double)s_pos[tt] * s_inv_freq[i], sv_, cv);
+            s_cs[tt][i] = make_float2(cv, sv_);
+        }
     }
     __syncthreads();
     const int slot = s_slot[t];
+    const bool lower = part * CPT < half;
+    const int src_lane = lower ? lane + shift : lane - shift;
 
+    // A row value and its partner's, normalized (xh = x inv) and weighted,
+    // turn into xh w cos + xh' w' sin, w' the partner dimension's weight and
+    // the sine signed for the pair member (the lower member takes minus its
+    // partner's share, the upper plus). Both factors are formed once:
+    // fa = w cos, fb = w' sin. Dimension c < rotary_dim turns by the angle
+    // of pair index c mod rotary_dim/2; past rotary_dim, cos 1 and sin 0.
+    float fa[CPT], fb[CPT];
+    {
+        const int base = lower ? part * CPT : part * CPT - half;
 #pragma unroll
-    for (int j = 0; j < kHeadsPerWG; ++j) {
-        if (j >= nh) break;  // uniform over the workgroup
-        const int hh = h0 + j;
-        const int kind = kind_of(hh), head = head_of(hh);
-        uint16_t(&x)[CPT] = xs[j];
-        if (kind != 2) {
-            float y[CPT];
+        for (int e = 0; e < CPT; ++e) {
+            const float w = wsrc ? A.weight_offset + half_f32(wv[e / 2], e) : 1.f;
+            const bool rot = part * CPT + e < A.rotary_dim;
+            const float2 v = rot ? s_cs[t][base + e] : make_float2(1.f, 0.f);
+            const float wp = shift == 8 ? row_ror<8>(w) : __shfl(w, shift ? src_lane : lane, 64);
+            fa[e] = w * v.x;
+            fb[e] = wp * (lower ? -v.y : v.y);
+        }
+    }
+
+    // norm and rotation of each row, stored as soon as it is done
+    auto rows = [&](auto dpp) {
+        constexpr bool DPP = decltype(dpp)::value;  // the whole head turns: partners 8 lanes apart
+#pragma unroll
+        for (int j = 0; j < kHeadsPerWG; ++j) {
+            if (j >= nh) break;  // uniform over the workgroup
+            const int head = head0 + j;
+            uint32_t(&x)[W] = xs[j];
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
-                y[e] = bf16_to_f32(x[e]);
-                ss = fmaf(y[e], y[e], ss);
+                const float y = half_f32(x[e / 2], e);
+                ss = fmaf(y, y, ss);
             }
+            // sum over the token's 16 lanes: after the step by n, lanes n
+            // apart hold equal sums, so a rotation by n adds the same pair as
+            // an exchange with lane i ^ n
+            ss += row_ror<8>(ss);
+            ss += row_ror<4>(ss);
+            ss += row_ror<2>(ss);
+            ss += row_ror<1>(ss);
+            const float inv = __frsqrt_rn(ss * (1.f / D) + A.eps);  // D a power of two: the mean is exact
+            float xh[CPT], r[CPT];
 #pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-            const float inv = 1.f / __fsqrt_rn(__fdiv_rn(ss, (float)D) + A.eps);
-            const uint16_t *wt = kind == 0 ? A.qw : A.kw;
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) {
-                const float w = wt ? A.weight_offset + bf16_to_f32(wt[part * CPT + e]) : 1.f;
-                y[e] = (y[e] * inv) * w;
-            }
-            // NeoX pairs: the lower half takes its partner from `shift` lanes up,
-            // the upper half from `shift` lanes down (same register)
-            const bool lower = part * CPT < half;
-            const int src_lane = lower ? lane + shift : lane - shift;
+            for (int e = 0; e < CPT; ++e) xh[e] = half_f32(x[e / 2], e) * inv;
 #pragma unroll
             for (int e = 0; e < CPT; ++e) {
-                const float other = __shfl(y[e], shift ? src_lane : lane, 64);
-                const float rot = lower ? y[e] * cs[e] - other * sn[e] : y[e] * cs[e] + other * sn[e];
-                x[e] = f32_to_bf16(part * CPT + e < A.rotary_dim ? rot : y[e]);
+                const float other = DPP ? row_ror<8>(xh[e]) : __shfl(xh[e], shift ? src_lane : lane, 64);
+                const float own = xh[e] * fa[e];  // xh w where the dimension does not turn
+                r[e] = DPP || part * CPT + e < A.rotary_dim ? fmaf(other, fb[e], own) : own;
             }
-        }
-        if (kind == 0) {
-            if (have) store_row<CPT>(A.q_out + ((size_t)tok * A.Hq + head) * D + part * CPT, x);
-            continue;
-        }
-        if (kind == 1) {
-            // K tile [D/8][16][8]: the lane's dimensions are whole 8-element pieces
-            if (have && slot >= 0) {
+#pragma unroll
+            for (int i = 0; i < W; ++i) x[i] = pack_bf16(r[2 * i], r[2 * i + 1]);
+            if (kind == 0) {
+                if (have) store_words<W>(A.q_out + ((size_t)tok * A.Hq + head) * D + part * CPT, x);
+            } else if (have && slot >= 0) {
+                // K tile [D/8][16][8]: the lane's dimensions are whole 8-element pieces
                 uint16_t *tile = A.kp + ((size_t)(slot / kBlk) * A.Hkv + head) * kBlk * D;
                 const int o = slot % kBlk;
 #pragma unroll
-                for (int c = 0; c < CPT; c += 8 < CPT ? 8 : CPT) {
-                    const int c0 = part * CPT + c;
+                for (int i = 0; i < W; i += 4 < W ? 4 : W) {
+                    const int c0 = part * CPT + 2 * i;
                     uint16_t *dst = tile + ((c0 / 8) * kBlk + o) * 8 + c0 % 8;
-                    if constexpr (CPT == 4) {
-                        u32x2_t w;
-                        __builtin_memcpy(&w, x + c, 8);
-                        *reinterpret_cast<u32x2_t *>(dst) = w;
-                    } else {
-                        u32x4_t w;
-                        __builtin_memcpy(&w, x + c, 16);
-                        *reinterpret_cast<u32x4_t *>(dst) = w;
-                    }
+                    if constexpr (W == 2) *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{x[i], x[i + 1]};
+                    else *reinterpret_cast<u32x4_t *>(dst) = u32x4_t{x[i], x[i + 1], x[i + 2], x[i + 3]};
                 }
             }
-            continue;
         }
-        // V tile [D][16]
-        if (s_full) {
-            store_row<CPT>(&sv[t][part * CPT], x);
-            __syncthreads();
-            uint16_t *tile = A.vp + ((size_t)(s_slot[0] / kBlk) * A.Hkv + head) * kBlk * D;
-            for (int pc = tid; pc < 2 * D; pc += 256) {  // piece pc: channel pc/2, tokens 8 (pc&1) .. +7
-                const int c = pc >> 1, t0 = (pc & 1) * 8;
-                uint16_t b[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) b[e] = sv[t0 + e][c];
-                u32x4_t w;
-                __builtin_memcpy(&w, b, 16);
-                *reinterpret_cast<u32x4_t *>(tile + (size_t)pc * 8) = w;
-            }
-            __syncthreads();
-        } else if (have && slot >= 0) {
-            uint16_t *tile = A.vp + ((size_t)(slot / kBlk) * A.Hkv + head) * kBlk * D;
-#pragma unroll
-            for (int e = 0; e < CPT; ++e) tile[(size_t)(part * CPT + e) * kBlk + slot % kBlk] = x[e];
-        }
-    }
+    };
+    if (shift == 8) rows(std::true_type{});
+    else rows(std::false_type{});
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -277,7 +355,8 @@ int kv_qknorm_rope_scatter(const void *q, const void *k, const void *v, const in
         PKV_FAIL(KV_EINVAL, "kv_qknorm_rope_scatter: rows, q_out and pools must be 16-byte aligned");
     if ((int64_t)num_blocks * kBlk > INT32_MAX) PKV_FAIL(KV_EINVAL, "kv_qknorm_rope_scatter: pool too large");
     const int64_t groups = ((int64_t)n + kBlk - 1) / kBlk;
-    const int64_t hgroups = ((int64_t)num_q_heads + 2 * num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG;
+    const int64_t hgroups = ((int64_t)num_q_heads + kHeadsPerWG - 1) / kHeadsPerWG +
+                            2 * (((int64_t)num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG);
     if (groups > INT32_MAX || hgroups > 65535) PKV_FAIL(KV_EINVAL, "kv_qknorm_rope_scatter: too many tokens or heads");
     ProdArgs A;
     A.q = static_cast<const uint16_t *>(q);
@@ -297,7 +376,7 @@ int kv_qknorm_rope_scatter(const void *q, const void *k, const void *v, const in
     A.rotary_dim = rotary_dim;
     A.eps = eps;
     A.weight_offset = weight_offset;
-    A.log2_theta = std::log2((double)rope_theta);
+    A.freq_step = rotary_dim ? 2.0 * std::log2((double)rope_theta) / rotary_dim : 0.0;
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     const dim3 grid((unsigned)groups, (unsigned)hgroups);
