@@ -9,8 +9,9 @@
 // pos * theta^(-2i / rotary_dim), and the result is rounded once to bf16; Q
 // goes to q_out, K and V (unchanged) into the bf16 pools at their slots.
 //
-// Workgroup: 16 consecutive tokens x up to kHeadsPerWG heads of one kind (Q,
-// K or V). Lane group t (16 lanes) owns token t; lane p of it owns the D/16
+// Workgroup: 16 consecutive tokens x up to HPW heads of one kind (Q, K or
+// V): 4, or 2 when a batch is so small that 4 would leave most compute
+// units idle. Lane group t (16 lanes) owns token t; lane p of it owns the D/16
 // consecutive dimensions p*D/16 .. p*D/16 + D/16 - 1, held as packed bf16
 // pairs, so that a row loads and stores in 16-byte pieces and the K tile
 // layout [D/8][16][8] takes whole pieces. The NeoX partner of a dimension
@@ -36,7 +37,6 @@ namespace pkv {
 namespace {
 
 constexpr int kBlk = 16;
-constexpr int kHeadsPerWG = 4;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -131,7 +131,7 @@ __device__ inline void sincos_turned(double ang, float &s, float &c) {
     c = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b) ^ ((uint32_t)((k + 1) & 2) << 30));
 }
 
-template <int D>
+template <int D, int HPW>
 __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
     constexpr int CPT = D / 16, W = CPT / 2;
     const int tid = threadIdx.x;
@@ -140,25 +140,25 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
     const int tok = i0 + t;
     const bool have = tok < A.n;
 
-    // Head groups: the Q heads kHeadsPerWG at a time, then the K heads, then
+    // Head groups: the Q heads HPW at a time, then the K heads, then
     // the V heads (the last group of each kind may hold fewer), so that a
     // workgroup's rows are all of one kind.
-    const int gq = (A.Hq + kHeadsPerWG - 1) / kHeadsPerWG, gk = (A.Hkv + kHeadsPerWG - 1) / kHeadsPerWG;
+    const int gq = (A.Hq + HPW - 1) / HPW, gk = (A.Hkv + HPW - 1) / HPW;
     const int gy = blockIdx.y;
     const int kind = gy < gq ? 0 : gy < gq + gk ? 1 : 2;  // Q, K, V
-    const int head0 = (kind == 0 ? gy : kind == 1 ? gy - gq : gy - gq - gk) * kHeadsPerWG;
+    const int head0 = (kind == 0 ? gy : kind == 1 ? gy - gq : gy - gq - gk) * HPW;
     const int H = kind == 0 ? A.Hq : A.Hkv;
-    const int nh = min(H - head0, kHeadsPerWG);
+    const int nh = min(H - head0, HPW);
 
     __shared__ int s_slot[kBlk];
     __shared__ int s_pos[kBlk];
     __shared__ double s_inv_freq[D / 2];  // theta^(-2i / rotary_dim), i < rotary_dim / 2
     // Q and K workgroups: (cos, sin) of token t's pair index i, [kBlk][D/2];
-    // V workgroups: their rows, [kHeadsPerWG][kBlk][D] bf16
-    constexpr int kCsBytes = kBlk * (D / 2) * 8, kVBytes = kHeadsPerWG * kBlk * D * 2;
+    // V workgroups: their rows, [HPW][kBlk][D] bf16
+    constexpr int kCsBytes = kBlk * (D / 2) * 8, kVBytes = HPW * kBlk * D * 2;
     __shared__ __attribute__((aligned(16))) unsigned char s_u[kCsBytes > kVBytes ? kCsBytes : kVBytes];
     float2(&s_cs)[kBlk][D / 2] = *reinterpret_cast<float2(*)[kBlk][D / 2]>(s_u);
-    uint16_t(&sv)[kHeadsPerWG][kBlk][D] = *reinterpret_cast<uint16_t(*)[kHeadsPerWG][kBlk][D]>(s_u);
+    uint16_t(&sv)[HPW][kBlk][D] = *reinterpret_cast<uint16_t(*)[HPW][kBlk][D]>(s_u);
 
     // Every global read is issued up front, the per-token ones first, so
     // that one memory latency covers them all and the angle arithmetic
@@ -171,9 +171,9 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
     uint32_t wv[W];  // the lane's dimensions of the kind's norm weights
     if (wsrc) load_words<W>(wsrc + part * CPT, wv);
     const uint16_t *rows_in = kind == 0 ? A.q : kind == 1 ? A.k : A.v;
-    uint32_t xs[kHeadsPerWG][W];
+    uint32_t xs[HPW][W];
 #pragma unroll
-    for (int j = 0; j < kHeadsPerWG; ++j)
+    for (int j = 0; j < HPW; ++j)
         load_words<W>(rows_in + ((size_t)(have ? tok : 0) * H + head0 + min(j, nh - 1)) * D + part * CPT, xs[j]);
     if (tid < kBlk) s_slot[tid] = (i0 + tid < A.n && slot_g >= 0 && slot_g < A.num_blocks * kBlk) ? slot_g : -1;
 
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
         const bool full = __all(lane >= kBlk || (s_slot[li] >= 0 && s_slot[li] == sl0 + li && sl0 % kBlk == 0));
         if (full) {
 #pragma unroll
-            for (int j = 0; j < kHeadsPerWG; ++j)
+            for (int j = 0; j < HPW; ++j)
                 if (j < nh) store_words<W>(&sv[j][t][part * CPT], xs[j]);
             __syncthreads();
             for (int pc = tid; pc < nh * 2 * D; pc += 256) {  // row j, piece q: channel q/2, tokens 8 (q&1) .. +7
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
             }
         } else if (have && slot >= 0) {
 #pragma unroll
-            for (int j = 0; j < kHeadsPerWG; ++j) {
+            for (int j = 0; j < HPW; ++j) {
                 if (j >= nh) break;
                 uint16_t *tile = A.vp + ((size_t)(slot / kBlk) * A.Hkv + head0 + j) * kBlk * D;
 #pragma unroll
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_scatter_kernel(ProdArgs A) {
     auto rows = [&](auto dpp) {
         constexpr bool DPP = decltype(dpp)::value;  // the whole head turns: partners 8 lanes apart
 #pragma unroll
-        for (int j = 0; j < kHeadsPerWG; ++j) {
+        for (int j = 0; j < HPW; ++j) {
             if (j >= nh) break;  // uniform over the workgroup
             const int head = head0 + j;
             uint32_t(&x)[W] = xs[j];
@@ -355,8 +355,13 @@ int kv_qknorm_rope_scatter(const void *q, const void *k, const void *v, const in
         PKV_FAIL(KV_EINVAL, "kv_qknorm_rope_scatter: rows, q_out and pools must be 16-byte aligned");
     if ((int64_t)num_blocks * kBlk > INT32_MAX) PKV_FAIL(KV_EINVAL, "kv_qknorm_rope_scatter: pool too large");
     const int64_t groups = ((int64_t)n + kBlk - 1) / kBlk;
-    const int64_t hgroups = ((int64_t)num_q_heads + kHeadsPerWG - 1) / kHeadsPerWG +
-                            2 * (((int64_t)num_kv_heads + kHeadsPerWG - 1) / kHeadsPerWG);
+    // head groups of `hpw` heads per kind; 2 when 4 would give fewer than
+    // 128 workgroups (decode-sized batches, where latency rules)
+    auto head_groups = [&](int64_t hpw) {
+        return (num_q_heads + hpw - 1) / hpw + 2 * ((num_kv_heads + hpw - 1) / hpw);
+    };
+    const int hpw = groups * head_groups(4) < 128 ? 2 : 4;
+    const int64_t hgroups = head_groups(hpw);
     if (groups > INT32_MAX || hgroups > 65535) PKV_FAIL(KV_EINVAL, "kv_qknorm_rope_scatter: too many tokens or heads");
     ProdArgs A;
     A.q = static_cast<const uint16_t *>(q);
@@ -380,9 +385,11 @@ int kv_qknorm_rope_scatter(const void *q, const void *k, const void *v, const in
     hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
     (void)hipGetLastError();
     const dim3 grid((unsigned)groups, (unsigned)hgroups);
-    if (head_dim == 64) hipLaunchKernelGGL(qknorm_rope_scatter_kernel<64>, grid, dim3(256), 0, st, A);
-    else if (head_dim == 128) hipLaunchKernelGGL(qknorm_rope_scatter_kernel<128>, grid, dim3(256), 0, st, A);
-    else hipLaunchKernelGGL(qknorm_rope_scatter_kernel<256>, grid, dim3(256), 0, st, A);
+    auto launch = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, A); };
+    if (head_dim == 64) hpw == 2 ? launch(qknorm_rope_scatter_kernel<64, 2>) : launch(qknorm_rope_scatter_kernel<64, 4>);
+    else if (head_dim == 128)
+        hpw == 2 ? launch(qknorm_rope_scatter_kernel<128, 2>) : launch(qknorm_rope_scatter_kernel<128, 4>);
+    else hpw == 2 ? launch(qknorm_rope_scatter_kernel<256, 2>) : launch(qknorm_rope_scatter_kernel<256, 4>);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) PKV_FAIL(KV_EDEVICE, "kv_qknorm_rope_scatter: launch failed: %s", hipGetErrorString(e));
     return KV_OK;

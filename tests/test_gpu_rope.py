@@ -79,7 +79,8 @@ CONFIGS = [
 
 
 @pytest.mark.parametrize("cfg", CONFIGS, ids=lambda c: f"{c[0]}-{c[1]}-D{c[2]}-rd{c[3]}")
-@pytest.mark.parametrize("n", [1, 37, 130])
+# n = 700 runs the workgroups of 4 heads, the smaller batches those of 2
+@pytest.mark.parametrize("n", [1, 37, 130, 700])
 def test_qknorm_rope_scatter_parity(pk, cfg, n):
     import torch
     Hq, Hkv, D, rd, theta, off, weights = cfg
