@@ -3,11 +3,12 @@ scatter (TensorSharp "高级功能" page: the fused QK-Norm + NeoX RoPE kernel o
 Qwen 3.5/3.6 and the batched forward's paged K/V scatter-write).
 
 The oracle computes the exact value and rounds once to bf16; the kernel
-computes in float32 (the angle in float64, reduced to [-pi, pi] before the
-float32 sine and cosine) and rounds once. Its float32 error before the
-rounding stays below 2^-20 of the row's largest magnitude (a few float32
-rounding steps in the norm, the angle and the rotation; where a cos - b sin
-cancels, that error is large next to the result). The bar per value: at most
+computes in float32 (the angle in float64, reduced by multiples of pi/2 to
+at most pi/4, then polynomials for the float32 sine and cosine) and rounds
+once. Its float32 error before the rounding stays below 2^-20 of the row's
+largest magnitude (a few float32 rounding steps in the norm, the angle and
+the rotation; where a cos - b sin cancels, that error is large next to the
+result). The bar per value: at most
 one bf16 step of the oracle's value plus 2^-20 of the row's largest
 magnitude, and at most 1 in 500 values differing at all. V is copied, so it
 is bit-exact, and every pool slot that is not written keeps its NaN fill.
