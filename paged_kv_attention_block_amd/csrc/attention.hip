@@ -36,6 +36,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "pagedkv.h"
 #include "status.h"
@@ -2015,52 +2016,60 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
 
 // ---------------------------------------------------------------------------
 // Scatter-write: one workgroup per 16 consecutive new tokens and one KV head.
-// Where the 16 tokens fill one block in order (a prefill chunk, a verify
-// window), the K tile and the transposed V tile are written as whole 16-byte
-// pieces, the V rows gathered through LDS; otherwise each token's K chunks are
-// 16-byte stores and its V values single-element stores.
+// Every read is issued first (the tokens' slots and the group's K and V rows,
+// 16-byte pieces row-major over the tokens), and the V rows go to LDS before
+// the one barrier. Where the 16 tokens fill one block in order (a prefill
+// chunk, a verify window), the K tile and the transposed V tile are written
+// as whole 16-byte pieces, the V columns gathered from LDS; otherwise each
+// token's K chunks are 16-byte stores and its V values single-element stores.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int kMaxP>  // kMaxP: pieces per lane, 16 tokens x D / X pieces over 256 lanes
 __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, const T *__restrict__ vn,
                                                      const int32_t *__restrict__ slots, int n, T *kp, T *vp,
                                                      int num_blocks, int Hkv, int D) {
     constexpr int X = 16 / sizeof(T);  // elements per 16-byte piece
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
-    const int cpt = D / X;              // 16-byte pieces per token row
+    const int cpt = D / X;  // 16-byte pieces per token row
+    const int np = kBlock * cpt;
     __shared__ int s_slot[kBlock];
-    __shared__ int s_full;
     __shared__ __attribute__((aligned(16))) T sv[kBlock * 256];
-    if (tid < kBlock) {
-        const int i = i0 + tid;
-        int sl = i < n ? slots[i] : -1;
-        s_slot[tid] = (sl >= 0 && sl < num_blocks * kBlock) ? sl : -1;
+    // indices clamped to the last token (n >= 1) and the last piece, so that
+    // no read sits in a branch; the clamped tokens have no slot and the
+    // clamped pieces are never stored
+    const int slot_g = slots[min(i0 + (tid & (kBlock - 1)), n - 1)];
+    u32x4_t kr[kMaxP], vr[kMaxP];
+#pragma unroll
+    for (int r = 0; r < kMaxP; ++r) {
+        const int p = min(tid + 256 * r, np - 1);
+        const int t = p / cpt, c = p - t * cpt;
+        const size_t src = ((size_t)min(i0 + t, n - 1) * Hkv + h) * D + (size_t)c * X;
+        kr[r] = *reinterpret_cast<const u32x4_t *>(kn + src);
+        vr[r] = *reinterpret_cast<const u32x4_t *>(vn + src);
     }
-    __syncthreads();
-    if (tid < 64) {
-        const int sl0 = s_slot[0];
-        const bool ok = tid >= kBlock || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlock == 0);
-        const bool full = __all(ok);
-        if (tid == 0) s_full = full;
+#pragma unroll
+    for (int r = 0; r < kMaxP; ++r) {
+        const int p = tid + 256 * r;
+        const int t = p / cpt, c = p - t * cpt;
+        if (p < np) *reinterpret_cast<u32x4_t *>(sv + (size_t)t * D + (size_t)c * X) = vr[r];
     }
+    if (tid < kBlock)
+        s_slot[tid] = (i0 + tid < n && slot_g >= 0 && slot_g < num_blocks * kBlock) ? slot_g : -1;
     __syncthreads();
-    const bool full = s_full;
-    const int ntok = min(kBlock, n - i0);
+    // every wave tests the group itself: whole block, in order
+    const int sl0 = s_slot[0];
+    const int li = lane & (kBlock - 1);
+    const bool full = __all(lane >= kBlock || (s_slot[li] >= 0 && s_slot[li] == sl0 + li && sl0 % kBlock == 0));
     if (full) {
-        const size_t tile = ((size_t)(s_slot[0] / kBlock) * Hkv + h) * D * kBlock;  // element offset
-        // K: piece (c, token t) of the tile is token t's chunk c
-        for (int p = tid; p < cpt * kBlock; p += 256) {
-            const int c = p / kBlock, t = p % kBlock;
-            *reinterpret_cast<u32x4_t *>(kp + tile + (size_t)p * X) =
-                *reinterpret_cast<const u32x4_t *>(kn + ((size_t)(i0 + t) * Hkv + h) * D + (size_t)c * X);
+        const size_t tile = ((size_t)(sl0 / kBlock) * Hkv + h) * D * kBlock;  // element offset
+        // K: piece (c, token t) of the tile [D/X][16][X] is token t's chunk c
+#pragma unroll
+        for (int r = 0; r < kMaxP; ++r) {
+            const int p = tid + 256 * r;
+            const int t = p / cpt, c = p - t * cpt;
+            if (p < np) *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)c * kBlock + t) * X) = kr[r];
         }
-        // V: rows through LDS, then each 16-byte piece of a channel row holds X tokens
-        for (int p = tid; p < cpt * kBlock; p += 256) {
-            const int t = p / cpt, c = p % cpt;
-            *reinterpret_cast<u32x4_t *>(sv + (size_t)t * D + (size_t)c * X) =
-                *reinterpret_cast<const u32x4_t *>(vn + ((size_t)(i0 + t) * Hkv + h) * D + (size_t)c * X);
-        }
-        __syncthreads();
+        // V [D][16]: each 16-byte piece of a channel row holds X tokens
         constexpr int PPR = kBlock / X;  // pieces per channel row
         for (int p = tid; p < D * PPR; p += 256) {
             const int ch = p / PPR, q = p % PPR;
@@ -2073,18 +2082,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
         }
         return;
     }
-    for (int p = tid; p < ntok * cpt; p += 256) {
-        const int t = p / cpt, c = p % cpt;
-        const int sl = s_slot[t];
+#pragma unroll
+    for (int r = 0; r < kMaxP; ++r) {
+        const int p = tid + 256 * r;
+        const int t = p / cpt, c = p - t * cpt;
+        const int sl = p < np ? s_slot[t] : -1;
         if (sl < 0) continue;
         const int b = sl / kBlock, o = sl % kBlock;
         const size_t tile = ((size_t)b * Hkv + h) * D * kBlock;
-        const size_t src = ((size_t)(i0 + t) * Hkv + h) * D + (size_t)c * X;
-        *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)c * kBlock + o) * X) =
-            *reinterpret_cast<const u32x4_t *>(kn + src);
-        const u32x4_t vv = *reinterpret_cast<const u32x4_t *>(vn + src);
+        *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)c * kBlock + o) * X) = kr[r];
         T e[X];
-        __builtin_memcpy(e, &vv, 16);
+        __builtin_memcpy(e, &vr[r], 16);
 #pragma unroll
         for (int x = 0; x < X; ++x) vp[tile + ((size_t)c * X + x) * kBlock + o] = e[x];
     }
@@ -2108,27 +2116,38 @@ __global__ __launch_bounds__(256) void scatter8_kernel(const uint16_t *__restric
     const int tid = threadIdx.x;
     const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
     __shared__ int s_slot[kBlock];
-    __shared__ int s_full;
     __shared__ __attribute__((aligned(16))) uint8_t kc[kBlock][D], vc[kBlock][D];
     __shared__ float ksc[kBlock], vsc[kBlock];
-    if (tid < kBlock) {
-        const int i = i0 + tid;
-        const int sl = i < n ? slots[i] : -1;
-        s_slot[tid] = (sl >= 0 && sl < num_blocks * kBlock) ? sl : -1;
-    }
+    // every read first, as vectors (indices clamped to the last token, n >= 1,
+    // so that no read sits in a branch; clamped tokens are masked below)
+    const int slot_g = slots[min(i0 + (tid & (kBlock - 1)), n - 1)];
     const int t = tid >> 4, part = tid & 15;  // token of the group, channel group
     const int i = i0 + t;
     const bool have = i < n;
     float xk[CPT], xv[CPT];
     {
-        const uint16_t *rk = kn + ((size_t)i * Hkv + h) * D + part * CPT;
-        const uint16_t *rv = vn + ((size_t)i * Hkv + h) * D + part * CPT;
+        const size_t row = ((size_t)min(i, n - 1) * Hkv + h) * D + part * CPT;
+        uint32_t wk[CPT / 2], wv[CPT / 2];
+        if constexpr (CPT == 4) {
+            const u32x2_t a = *reinterpret_cast<const u32x2_t *>(kn + row);
+            const u32x2_t b = *reinterpret_cast<const u32x2_t *>(vn + row);
+            wk[0] = a.x, wk[1] = a.y, wv[0] = b.x, wv[1] = b.y;
+        } else {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(kn + row);
+            const u32x4_t b = *reinterpret_cast<const u32x4_t *>(vn + row);
+            wk[0] = a.x, wk[1] = a.y, wk[2] = a.z, wk[3] = a.w;
+            wv[0] = b.x, wv[1] = b.y, wv[2] = b.z, wv[3] = b.w;
+        }
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            xk[c] = have ? __builtin_bit_cast(float, (uint32_t)rk[c] << 16) : 0.f;
-            xv[c] = have ? __builtin_bit_cast(float, (uint32_t)rv[c] << 16) : 0.f;
+            const uint32_t bk = c & 1 ? wk[c / 2] & 0xFFFF0000u : wk[c / 2] << 16;
+            const uint32_t bv = c & 1 ? wv[c / 2] & 0xFFFF0000u : wv[c / 2] << 16;
+            xk[c] = have ? __builtin_bit_cast(float, bk) : 0.f;
+            xv[c] = have ? __builtin_bit_cast(float, bv) : 0.f;
         }
     }
+    if (tid < kBlock)
+        s_slot[tid] = (i0 + tid < n && slot_g >= 0 && slot_g < num_blocks * kBlock) ? slot_g : -1;
     auto quantize = [&](float (&x)[CPT], uint8_t *codes_row, float *scale_slot) {
         float amax = 0.f;
 #pragma unroll
@@ -2150,13 +2169,10 @@ __global__ __launch_bounds__(256) void scatter8_kernel(const uint16_t *__restric
     quantize(xk, kc[t], &ksc[t]);
     quantize(xv, vc[t], &vsc[t]);
     __syncthreads();
-    if (tid < 64) {
-        const int sl0 = s_slot[0];
-        const bool ok = tid >= kBlock || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlock == 0);
-        const bool full = __all(ok);
-        if (tid == 0) s_full = full;
-    }
-    __syncthreads();
+    // every wave tests the group itself: whole block, in order
+    const int li = tid & (kBlock - 1);
+    const bool s_full = __all((tid & 63) >= kBlock ||
+                              (s_slot[li] >= 0 && s_slot[li] == s_slot[0] + li && s_slot[0] % kBlock == 0));
     // bytes of piece pc of a tile, from the group's codes (token tok of the
     // group sits at offset tok of the block in the whole-block case)
     auto k_piece = [&](int pc, int tok) {  // K piece ((p*4 + g)*16 + o): jj = 0 bytes then jj = 1 bytes
@@ -2243,27 +2259,38 @@ __global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restric
     const int tid = threadIdx.x;
     const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
     __shared__ int s_slot[kBlock];
-    __shared__ int s_full;
     __shared__ __attribute__((aligned(16))) uint8_t kc[kBlock][D], vc[kBlock][D];  // one code a byte
     __shared__ float ksc[kBlock], vsc[kBlock];
-    if (tid < kBlock) {
-        const int i = i0 + tid;
-        const int sl = i < n ? slots[i] : -1;
-        s_slot[tid] = (sl >= 0 && sl < num_blocks * kBlock) ? sl : -1;
-    }
+    // every read first, as vectors (indices clamped to the last token, n >= 1,
+    // so that no read sits in a branch; clamped tokens are masked below)
+    const int slot_g = slots[min(i0 + (tid & (kBlock - 1)), n - 1)];
     const int t = tid >> 4, part = tid & 15;  // token of the group, channel group
     const int i = i0 + t;
     const bool have = i < n;
     float xk[CPT], xv[CPT];
     {
-        const uint16_t *rk = kn + ((size_t)i * Hkv + h) * D + part * CPT;
-        const uint16_t *rv = vn + ((size_t)i * Hkv + h) * D + part * CPT;
+        const size_t row = ((size_t)min(i, n - 1) * Hkv + h) * D + part * CPT;
+        uint32_t wk[CPT / 2], wv[CPT / 2];
+        if constexpr (CPT == 4) {
+            const u32x2_t a = *reinterpret_cast<const u32x2_t *>(kn + row);
+            const u32x2_t b = *reinterpret_cast<const u32x2_t *>(vn + row);
+            wk[0] = a.x, wk[1] = a.y, wv[0] = b.x, wv[1] = b.y;
+        } else {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t *>(kn + row);
+            const u32x4_t b = *reinterpret_cast<const u32x4_t *>(vn + row);
+            wk[0] = a.x, wk[1] = a.y, wk[2] = a.z, wk[3] = a.w;
+            wv[0] = b.x, wv[1] = b.y, wv[2] = b.z, wv[3] = b.w;
+        }
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            xk[c] = have ? __builtin_bit_cast(float, (uint32_t)rk[c] << 16) : 0.f;
-            xv[c] = have ? __builtin_bit_cast(float, (uint32_t)rv[c] << 16) : 0.f;
+            const uint32_t bk = c & 1 ? wk[c / 2] & 0xFFFF0000u : wk[c / 2] << 16;
+            const uint32_t bv = c & 1 ? wv[c / 2] & 0xFFFF0000u : wv[c / 2] << 16;
+            xk[c] = have ? __builtin_bit_cast(float, bk) : 0.f;
+            xv[c] = have ? __builtin_bit_cast(float, bv) : 0.f;
         }
     }
+    if (tid < kBlock)
+        s_slot[tid] = (i0 + tid < n && slot_g >= 0 && slot_g < num_blocks * kBlock) ? slot_g : -1;
     auto quantize = [&](float (&x)[CPT], uint8_t *codes_row, float *scale_slot) {
         float amax = 0.f;
 #pragma unroll
@@ -2285,13 +2312,10 @@ __global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restric
     quantize(xk, kc[t], &ksc[t]);
     quantize(xv, vc[t], &vsc[t]);
     __syncthreads();
-    if (tid < 64) {
-        const int sl0 = s_slot[0];
-        const bool ok = tid >= kBlock || (s_slot[tid] >= 0 && s_slot[tid] == sl0 + tid && sl0 % kBlock == 0);
-        const bool full = __all(ok);
-        if (tid == 0) s_full = full;
-    }
-    __syncthreads();
+    // every wave tests the group itself: whole block, in order
+    const int li = tid & (kBlock - 1);
+    const bool s_full = __all((tid & 63) >= kBlock ||
+                              (s_slot[li] >= 0 && s_slot[li] == s_slot[0] + li && s_slot[0] % kBlock == 0));
     // eight codes into a dword, the first in the low nibble
     auto pack8 = [](const uint8_t (&c)[8]) {
         uint32_t w = 0;
@@ -2873,14 +2897,26 @@ int kv_append_scatter(const void *k_new, const void *v_new, const int32_t *slot_
         else
             hipLaunchKernelGGL(scatter8_kernel<128>, grid, dim3(256), 0, st, kn, vn, slot_mapping, n, kpp, vpp,
                                num_blocks, num_kv_heads);
-    } else if (dtype == KV_BF16)
-        hipLaunchKernelGGL(scatter_kernel<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(k_new),
-                           static_cast<const uint16_t *>(v_new), slot_mapping, n, static_cast<uint16_t *>(k_pool),
-                           static_cast<uint16_t *>(v_pool), num_blocks, num_kv_heads, head_dim);
-    else
-        hipLaunchKernelGGL(scatter_kernel<float>, grid, dim3(256), 0, st, static_cast<const float *>(k_new),
-                           static_cast<const float *>(v_new), slot_mapping, n, static_cast<float *>(k_pool),
-                           static_cast<float *>(v_pool), num_blocks, num_kv_heads, head_dim);
+    } else {
+        // 16-byte pieces of a 16-token group over 256 lanes: 1, 2 or 4 per lane
+        const int np = kBlock * head_dim * (dtype == KV_BF16 ? 2 : 4) / 16;
+        auto launch = [&](auto kernel, auto *tag) {
+            using T = std::remove_pointer_t<decltype(tag)>;
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, static_cast<const T *>(k_new),
+                               static_cast<const T *>(v_new), slot_mapping, n, static_cast<T *>(k_pool),
+                               static_cast<T *>(v_pool), num_blocks, num_kv_heads, head_dim);
+        };
+        if (dtype == KV_BF16) {
+            uint16_t *tag = nullptr;
+            if (np <= 256) launch(scatter_kernel<uint16_t, 1>, tag);
+            else launch(scatter_kernel<uint16_t, 2>, tag);
+        } else {
+            float *tag = nullptr;
+            if (np <= 256) launch(scatter_kernel<float, 1>, tag);
+            else if (np <= 512) launch(scatter_kernel<float, 2>, tag);
+            else launch(scatter_kernel<float, 4>, tag);
+        }
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) PKV_FAIL(KV_EDEVICE, "kv_append_scatter: launch failed: %s", hipGetErrorString(e));
     return KV_OK;
