@@ -2016,9 +2016,10 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
 
 // ---------------------------------------------------------------------------
 // Scatter-write: one workgroup per 16 consecutive new tokens and one KV head.
-// Every read is issued first (the tokens' slots and the group's K and V rows,
-// 16-byte pieces row-major over the tokens), and the V rows go to LDS before
-// the one barrier. Where the 16 tokens fill one block in order (a prefill
+// Every read is issued first: the tokens' slots, the group's K pieces in the
+// tile's order (piece p is chunk p / 16 of token p % 16, so that a whole
+// block goes out in contiguous 16-byte pieces) and its V rows row-major,
+// which go to LDS before the one barrier. Where the 16 tokens fill one block in order (a prefill
 // chunk, a verify window), the K tile and the transposed V tile are written
 // as whole 16-byte pieces, the V columns gathered from LDS; otherwise each
 // token's K chunks are 16-byte stores and its V values single-element stores.
@@ -2042,10 +2043,10 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
 #pragma unroll
     for (int r = 0; r < kMaxP; ++r) {
         const int p = min(tid + 256 * r, np - 1);
-        const int t = p / cpt, c = p - t * cpt;
-        const size_t src = ((size_t)min(i0 + t, n - 1) * Hkv + h) * D + (size_t)c * X;
-        kr[r] = *reinterpret_cast<const u32x4_t *>(kn + src);
-        vr[r] = *reinterpret_cast<const u32x4_t *>(vn + src);
+        const int tk = p % kBlock, ck = p / kBlock;
+        kr[r] = *reinterpret_cast<const u32x4_t *>(kn + ((size_t)min(i0 + tk, n - 1) * Hkv + h) * D + (size_t)ck * X);
+        const int tv = p / cpt, cv = p - tv * cpt;
+        vr[r] = *reinterpret_cast<const u32x4_t *>(vn + ((size_t)min(i0 + tv, n - 1) * Hkv + h) * D + (size_t)cv * X);
     }
 #pragma unroll
     for (int r = 0; r < kMaxP; ++r) {
@@ -2062,12 +2063,11 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
     const bool full = __all(lane >= kBlock || (s_slot[li] >= 0 && s_slot[li] == sl0 + li && sl0 % kBlock == 0));
     if (full) {
         const size_t tile = ((size_t)(sl0 / kBlock) * Hkv + h) * D * kBlock;  // element offset
-        // K: piece (c, token t) of the tile [D/X][16][X] is token t's chunk c
+        // K: the tile [D/X][16][X] in order
 #pragma unroll
         for (int r = 0; r < kMaxP; ++r) {
             const int p = tid + 256 * r;
-            const int t = p / cpt, c = p - t * cpt;
-            if (p < np) *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)c * kBlock + t) * X) = kr[r];
+            if (p < np) *reinterpret_cast<u32x4_t *>(kp + tile + (size_t)p * X) = kr[r];
         }
         // V [D][16]: each 16-byte piece of a channel row holds X tokens
         constexpr int PPR = kBlock / X;  // pieces per channel row
@@ -2085,16 +2085,22 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, 
 #pragma unroll
     for (int r = 0; r < kMaxP; ++r) {
         const int p = tid + 256 * r;
-        const int t = p / cpt, c = p - t * cpt;
-        const int sl = p < np ? s_slot[t] : -1;
-        if (sl < 0) continue;
-        const int b = sl / kBlock, o = sl % kBlock;
-        const size_t tile = ((size_t)b * Hkv + h) * D * kBlock;
-        *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)c * kBlock + o) * X) = kr[r];
-        T e[X];
-        __builtin_memcpy(e, &vr[r], 16);
+        if (p >= np) continue;
+        const int tk = p % kBlock, ck = p / kBlock;
+        const int slk = s_slot[tk];
+        if (slk >= 0) {
+            const size_t tile = ((size_t)(slk / kBlock) * Hkv + h) * D * kBlock;
+            *reinterpret_cast<u32x4_t *>(kp + tile + ((size_t)ck * kBlock + slk % kBlock) * X) = kr[r];
+        }
+        const int tv = p / cpt, cv = p - tv * cpt;
+        const int slv = s_slot[tv];
+        if (slv >= 0) {
+            const size_t tile = ((size_t)(slv / kBlock) * Hkv + h) * D * kBlock;
+            T e[X];
+            __builtin_memcpy(e, &vr[r], 16);
 #pragma unroll
-        for (int x = 0; x < X; ++x) vp[tile + ((size_t)c * X + x) * kBlock + o] = e[x];
+            for (int x = 0; x < X; ++x) vp[tile + ((size_t)cv * X + x) * kBlock + slv % kBlock] = e[x];
+        }
     }
 }
 
