@@ -2251,9 +2251,10 @@ __global__ __launch_bounds__(256) void scatter8_kernel(const uint16_t *__restric
 // instruction (both divisions IEEE float32); a zero row stores s = 0 and zero
 // codes. A whole block written in order goes out as 16-byte pieces built in
 // LDS. A token written alone owns its K run and its scales, but shares each
-// V byte with the neighbouring key, which another workgroup may be writing
-// at the same time: its V codes go in by atomic nibble updates (clear, then
-// set), which commute with the neighbour's.
+// V dword with the other tokens of its half block, which another workgroup
+// may be writing at the same time: the group's tokens of one half block go
+// in together, by a plain store where they fill the dword and otherwise by
+// atomic nibble updates (clear, then set), which commute with the others'.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restrict__ kn, const uint16_t *__restrict__ vn,
@@ -2264,7 +2265,7 @@ __global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restric
     constexpr int KJ = D / 32, DT = D / 16;
     const int tid = threadIdx.x;
     const int i0 = blockIdx.x * kBlock, h = blockIdx.y;
-    __shared__ int s_slot[kBlock];
+    __shared__ __attribute__((aligned(16))) int s_slot[kBlock];
     __shared__ __attribute__((aligned(16))) uint8_t kc[kBlock][D], vc[kBlock][D];  // one code a byte
     __shared__ float ksc[kBlock], vsc[kBlock];
     // every read first, as vectors (indices clamped to the last token, n >= 1,
@@ -2362,6 +2363,25 @@ __global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restric
     }
     const int sl = s_slot[t];
     if (!have || sl < 0) return;
+    // the group's tokens in this token's half block (slot / 8) and their
+    // nibbles, from the 16 slots read at once
+    uint32_t same = 0, nmask = 0;
+    uint64_t nib = 0;  // 4 bits per token u: its nibble within the dword
+    {
+        int su[kBlock];
+#pragma unroll
+        for (int q = 0; q < kBlock / 4; ++q) {
+            const int4 v = reinterpret_cast<const int4 *>(s_slot)[q];
+            su[4 * q] = v.x, su[4 * q + 1] = v.y, su[4 * q + 2] = v.z, su[4 * q + 3] = v.w;
+        }
+#pragma unroll
+        for (int u = 0; u < kBlock; ++u) {
+            const bool m = (su[u] >> 3) == (sl >> 3);  // an empty slot (-1) never matches: sl >= 0
+            same |= (uint32_t)m << u;
+            nmask |= m ? 0xFu << (4 * (su[u] & 7)) : 0u;
+            nib |= (uint64_t)(su[u] & 7) << (4 * u);
+        }
+    }
     const int blk = sl / kBlock, o = sl % kBlock;
     uint32_t *kt = reinterpret_cast<uint32_t *>(kp + ((size_t)blk * Hkv + h) * TB);
     uint32_t *vt = reinterpret_cast<uint32_t *>(vp + ((size_t)blk * Hkv + h) * TB);
@@ -2373,14 +2393,38 @@ __global__ __launch_bounds__(256) void scatter4_kernel(const uint16_t *__restric
         for (int e = 0; e < 8; ++e) ck[e] = kc[t][32 * j + 8 * g + e];
         kt[(g * kBlock + o) * KJ + j] = pack8(ck);
     }
-    // V: nibble o & 7 of one dword per channel
-    const int hh = o >> 3, sh = 4 * (o & 7);
+    // V: a dword holds one channel of a half block (8 tokens, nibble o & 7).
+    // The group's tokens in one half block go in together, written by the
+    // first of them: one plain store where they fill the dword, else one
+    // atomic clear and one atomic set of their nibbles (which commute with
+    // another group's updates of the other nibbles).
+    const int hh = o >> 3;
+    if (same == 1u << t) {  // alone in its half block here
+        const int sh = 4 * (o & 7);
 #pragma unroll
-    for (int c = part * CPT; c < part * CPT + CPT; ++c) {
-        const int dt = c >> 4, nn = c & 15;
-        uint32_t *w = vt + (nn * 2 + hh) * DT + dt;
-        atomicAnd(w, ~(0xFu << sh));
-        atomicOr(w, (uint32_t)vc[t][c] << sh);
+        for (int c = part * CPT; c < part * CPT + CPT; ++c) {
+            const int dt = c >> 4, nn = c & 15;
+            uint32_t *w = vt + (nn * 2 + hh) * DT + dt;
+            atomicAnd(w, ~(0xFu << sh));
+            atomicOr(w, (uint32_t)vc[t][c] << sh);
+        }
+    } else if (__builtin_ctz(same) == t) {
+#pragma unroll
+        for (int c = part * CPT; c < part * CPT + CPT; ++c) {
+            const int dt = c >> 4, nn = c & 15;
+            uint32_t val = (uint32_t)vc[t][c] << (4 * (o & 7));
+            for (uint32_t m = same & (same - 1); m; m &= m - 1) {  // the others
+                const int u = __builtin_ctz(m);
+                val |= (uint32_t)vc[u][c] << (4 * (int)((nib >> (4 * u)) & 7));
+            }
+            uint32_t *w = vt + (nn * 2 + hh) * DT + dt;
+            if (nmask == 0xFFFFFFFFu) {
+                *w = val;
+            } else {
+                atomicAnd(w, ~nmask);
+                atomicOr(w, val);
+            }
+        }
     }
     if (part == 0) {
         reinterpret_cast<float *>(kt + 2 * D)[o] = ksc[t];
