@@ -150,3 +150,38 @@ def test_scatter_tiny_rows(pk, D):
     kn = _bf16(x)
     vn = _bf16(x[::-1].copy())
     _assert_pools(*_run(pk, kn, vn, slots, nb))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_scatter_verify_windows(pk, D):
+    """Verify-window writes: runs of 8 consecutive slots at random offsets
+    (some crossing into the next block), two runs per group of 16 tokens, in
+    blocks whose earlier slots an earlier call wrote. A run's tokens share V
+    dwords (one channel of a half block) with each other and with the earlier
+    tokens; where a run fills a half block the group writes the dword whole.
+    Every pool byte equals the oracle's."""
+    import torch
+    import oracle
+    rng = np.random.default_rng(1200 + D)
+    nb, hkv, nwin = 40, 2, 12
+    # run w starts in block 2w + 1 (and may end in block 2w + 2); one more
+    # run fills the second half of block 25, whose first half came earlier
+    starts = [(2 * w + 1) * 16 + int(rng.integers(0, 16)) for w in range(nwin)] + [25 * 16 + 8]
+    before = np.concatenate([np.arange(st - st % 16, st) for st in starts]).astype(np.int32)
+    wins = np.concatenate([np.arange(st, st + 8) for st in starts]).astype(np.int32)
+    slots = np.concatenate([before, wins])
+    n = slots.size
+    announce(f"fp4 scatter verify windows D={D} n={n}")
+    kn = _bf16(rng.standard_normal((n, hkv, D), dtype=np.float32) * 2)
+    vn = _bf16(rng.standard_normal((n, hkv, D), dtype=np.float32))
+    kp, vp = pk.empty_pools(nb, hkv, D, "fp4", "cuda")
+    kp.fill_(0xFF)
+    vp.fill_(0xFF)
+    for a, b in ((0, before.size), (before.size, n)):
+        if b > a:
+            pk.kv_append_scatter(_device_rows(kn[a:b]), _device_rows(vn[a:b]), torch.from_numpy(slots[a:b]).cuda(),
+                                 kp, vp)
+    torch.cuda.synchronize()
+    ko, vo = oracle.fp4_empty_pools(nb, hkv, D, fill=np.uint8(0xFF))
+    oracle.fp4_scatter(ko, vo, kn, vn, slots)
+    _assert_pools(kp.cpu().numpy(), vp.cpu().numpy(), ko, vo)
