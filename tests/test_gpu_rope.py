@@ -136,3 +136,42 @@ def test_rejects_bad_rotary_dim_and_dtype(pk):
     kf, vf = pk.empty_pools(4, 2, 128, torch.float32, "cuda")
     with pytest.raises(pk.KVError):
         pk.kv_qknorm_rope_scatter(*args[:5], kf, vf)
+
+
+def test_qknorm_rope_scatter_mixed_step_size(pk):
+    """The launch the producer bench times: mixed_step's 2096 step tokens
+    (48 decode tokens after a 2900-token prefix, two 1024-token chunks from
+    position 0), 32 q / 8 KV heads, D 128, whole rotary, theta 1e6, norm
+    weights, whole blocks (slots 16 ..): 131 x 12 workgroups of 4 heads.
+    Every output against the oracle, to the same bar."""
+    import torch
+    w = synth.by_name("mixed_step")
+    n, Hq, Hkv, D = w.total_rows, w.num_q_heads, w.num_kv_heads, w.head_dim
+    rng = np.random.default_rng(2096)
+    bf = lambda *s: synth.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+    q, k, v = bf(n, Hq, D), bf(n, Hkv, D), bf(n, Hkv, D)
+    qw, kw = bf(D), bf(D)
+    pos = np.concatenate([np.arange(s.ctx - s.q_len, s.ctx) for s in w.seqs]).astype(np.int32)
+    slots = (np.arange(n) + 16).astype(np.int32)
+    nb = -(-n // 16) + 2
+    print(f"\n[case] qknorm_rope mixed_step size n={n} Hq={Hq} Hkv={Hkv} D={D}", flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    kp, vp = pk.empty_pools(nb, Hkv, D, torch.bfloat16, "cuda")
+    kp.fill_(float("nan"))
+    vp.fill_(float("nan"))
+    q_out = pk.kv_qknorm_rope_scatter(dev(q), dev(k), dev(v), torch.from_numpy(pos).cuda(),
+                                      torch.from_numpy(slots).cuda(), kp, vp, q_norm_weight=dev(qw),
+                                      k_norm_weight=dev(kw), eps=1e-6, rope_theta=1e6, rotary_dim=D)
+    torch.cuda.synchronize()
+    ko, vo = oracle.empty_pools(nb, Hkv, D, 16, "bf16", fill=np.uint16(0x7FC0))
+    q_want = oracle.qknorm_rope_scatter(ko, vo, q, k, v, pos, slots, qw, kw, 1e-6, 1e6, D)
+    within_bound(q_out.view(torch.int16).cpu().numpy().view(np.uint16), q_want, row_max(q_want), "q_out")
+    kg = kp.view(torch.int16).cpu().numpy().view(np.uint16)
+    vg = vp.view(torch.int16).cpu().numpy().view(np.uint16)
+    written = np.zeros(ko.shape, dtype=bool)
+    written[1:1 + n // 16] = True
+    np.testing.assert_array_equal(kg[~written], ko[~written])
+    kmax = np.abs(oracle.to_f32(np.where(written, ko, 0), "bf16").astype(np.float64))
+    kmax = np.nan_to_num(kmax).max(axis=(2, 4), keepdims=True)
+    within_bound(kg[written], ko[written], np.broadcast_to(kmax, ko.shape)[written], "K pool")
+    np.testing.assert_array_equal(vg, vo)
