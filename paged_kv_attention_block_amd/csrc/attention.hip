@@ -1213,23 +1213,28 @@ __device__ void prefix_group_item(const AttnParams &P, int kvh, int grp, int j, 
         ma = P.qsl[s0 + lane];
         mb = P.qsl[s0 + lane + 1];
     }
-    int bidm = -1;
+    int bidm = -1, bid3 = -1;  // bid3: the same for the split's last quarter
     {
         const int m = lane >> 4, i = lane & 15;
         if (m < nm && i < nqb) {
             const int jb = kq0 / kBlock + i;
             const int b = P.bt[(size_t)(s0 + m) * P.max_blocks_per_seq + min(jb, P.max_blocks_per_seq - 1)];
             bidm = (jb < P.max_blocks_per_seq && b >= 0 && b < P.num_blocks) ? b : -1;
+            const int jb3 = (ks + 3 * ql) / kBlock + i;
+            const int b3 = P.bt[(size_t)(s0 + m) * P.max_blocks_per_seq + min(jb3, P.max_blocks_per_seq - 1)];
+            bid3 = (jb3 < P.max_blocks_per_seq && b3 >= 0 && b3 < P.num_blocks) ? b3 : -1;
         }
     }
     // shared: every member one decode row whose context holds the whole
     // quarter, and the same valid block ids as member 0
-    bool ok = true;
+    bool ok = true, singles = true;
     for (int m = 0; m < nm; ++m) {
         const int c = __builtin_amdgcn_readlane(mc, m);
         const int a = __builtin_amdgcn_readlane(ma, m), b = __builtin_amdgcn_readlane(mb, m);
-        ok = ok && b - a == 1 && a >= 0 && b <= P.total_rows && c >= kq0 + ql;
+        singles = singles && b - a == 1 && a >= 0 && b <= P.total_rows;
+        ok = ok && c >= kq0 + ql;
     }
+    ok = ok && singles;
     const int lead = __shfl(bidm, lane & 15, 64);
     const bool mine = (lane >> 4) < nm && (lane & 15) < nqb;
     ok = ok && !__any(mine && (bidm < 0 || bidm != lead));
@@ -1237,6 +1242,9 @@ __device__ void prefix_group_item(const AttnParams &P, int kvh, int grp, int j, 
     if (lane == 0) s_ok[wave] = ok;
     __syncthreads();
     const bool shared = s_ok[0] && s_ok[1] && s_ok[2] && s_ok[3];
+    // the split that holds the prefix's end: its first three quarters shared,
+    // the last not (every member one decode row)
+    const bool last_only = !shared && s_ok[0] && s_ok[1] && s_ok[2] && singles;
 
     const size_t tile = PoolT::tile_bytes;
     const uint8_t *kbase = reinterpret_cast<const uint8_t *>(P.kp) + (size_t)kvh * tile;
@@ -1298,6 +1306,97 @@ __device__ void prefix_group_item(const AttnParams &P, int kvh, int grp, int j, 
         }
         __syncthreads();  // wave 0 has read the LDS states before the next pass writes them
     };
+
+    // One quarter [qa, qa + ql) of a tile (rows as in pass), keys from member
+    // src's block ids held in bids (lane 16 src + i), into st.
+    auto quarter = [&](int qrow, int hl, int prow, int src, int ctx, int qa, int bids, TileState<DT> &st) {
+        RowInfo ri;
+        ri.r = 0;
+        ri.hl = hl;
+        ri.prow = prow;
+        RowVis rv;
+        rv.prow = prow;
+        rv.lo = kFarBelow;
+        rv.wbase = kFarAbove;
+        rv.tm = 0xFFFFFFFFu;
+        u32x4_t qop[KJ];
+        load_q<D>(qop, P, qrow, ri, kvh, g);
+        state_clear(st);
+        const int kq1 = min(qa + ql, ctx);
+        for (int kc = qa; kc < kq1; kc += kStep) {
+            const int li = src * 16 + (kc - qa) / kBlock;
+            const int b0 = __builtin_amdgcn_readlane(bids, li);
+            const int b1 = __builtin_amdgcn_readlane(bids, li + 1);
+            Regs r;
+            PoolT::load(r, b0 >= 0 ? kbase + (size_t)b0 * bstride : zero, b0 >= 0 ? vbase + (size_t)b0 * bstride : zero,
+                        b1 >= 0 ? kbase + (size_t)b1 * bstride : zero, b1 >= 0 ? vbase + (size_t)b1 * bstride : zero,
+                        g, n);
+            PoolT::mask(r, kc, ctx, g);
+            PoolT::template update<false>(st, r, qop, kc, rv, g, P.scale_log2);
+        }
+    };
+
+    if (last_only) {
+        // Waves 0-2 stream their quarter once for the group tile (member m's
+        // head hl at tile row m * G + hl); the members' last quarters, over
+        // their own blocks with only that member's rows seeing keys, go to
+        // waves 3, 3, 1, 2 (members 0-3), so that no wave streams more than
+        // two quarters. Member rows keep the tile's layout, and every row's
+        // quarter states meet in quarter order, as in the row alone.
+        const int m_row = n / P.G, hl = n - m_row * P.G;
+        const bool row = m_row < nm && n < nm * P.G;
+        const int mm = row ? m_row : 0;
+        int a = 0, c = 0;
+        for (int k = 0; k < nm; ++k)
+            if (mm == k) {
+                a = __builtin_amdgcn_readlane(ma, k);
+                c = __builtin_amdgcn_readlane(mc, k);
+            }
+        int cmax = 0;
+        for (int k = 0; k < nm; ++k) cmax = max(cmax, __builtin_amdgcn_readlane(mc, k));
+        TileState<DT> st;
+        state_clear(st);
+        if (wave < 3) {
+            quarter(a, row ? hl : 0, row ? c - 1 : -1, 0, cmax, kq0, bidm, st);
+            if (wave > 0) {
+                lds.ml[wave - 1][0][lane] = make_float2(st.m, st.l);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lds.acc[wave - 1][0][dt][lane] = st.acc[dt];
+            }
+        }
+        // (wave 0 takes no member: its quarter state stays in st for the fold,
+        // and the other waves reuse st, whose state is in LDS by now)
+        for (int m = 0; m < nm; ++m) {
+            if ((m < 2 ? 3 : m - 1) != wave) continue;  // uniform over the wave
+            const int cm = __builtin_amdgcn_readlane(mc, m), am = __builtin_amdgcn_readlane(ma, m);
+            const bool mine_row = row && m_row == m;
+            quarter(am, mine_row ? hl : 0, mine_row ? cm - 1 : -1, m, cm, ks + 3 * ql, bid3, st);
+            if (mine_row) {
+                lds.ml[2][0][lane] = make_float2(st.m, st.l);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) lds.acc[2][0][dt][lane] = st.acc[dt];
+            }
+        }
+        __syncthreads();
+        if (wave == 0 && row) {
+#pragma unroll
+            for (int w = 0; w < 3; ++w) {
+                TileState<DT> o;
+                const float2 ml = lds.ml[w][0][lane];
+                o.m = ml.x;
+                o.l = ml.y;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) o.acc[dt] = lds.acc[w][0][dt][lane];
+                fold_state(st, o);
+            }
+            const size_t base = ((size_t)a * P.Hq + kvh * P.G + hl) * P.max_splits + j;
+            if (g == 0) P.ws_ml[base] = make_float2(st.m, st.l);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                *reinterpret_cast<f32x4_t *>(P.ws_acc + base * D + 16 * dt + 4 * g) = st.acc[dt];
+        }
+        return;
+    }
 
     if (shared) {
         const int m = n / P.G, hl = n - m * P.G;
@@ -2745,6 +2844,11 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
         const int seqs = std::min(pre->seqs, num_seqs);
         int js = 0;
         while (js < max_splits && split_begin(js + 1) <= pre->tokens) ++js;
+        // the split holding the prefix's end joins the group items when the
+        // prefix covers its first three quarters
+        if (js > 0 && js < max_splits &&
+            pre->tokens - split_begin(js) >= 3 * ((split_begin(js + 1) - split_begin(js)) / 4))
+            ++js;
         if (js > 0) {
             P.pre_m = std::min(4, 16 / P.G);
             P.pre_seqs = seqs;

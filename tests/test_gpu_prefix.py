@@ -140,13 +140,19 @@ def test_rejects_negative_hint(pk):
 
 
 @pytest.mark.parametrize("dtype,shared", [("bf16", 1100), ("bf16", 1280), ("bf16", 1700), ("bf16", 2048),
-                                          ("bf16", 600), ("bf16", 700), ("fp4", 1700), ("fp8", 1300)])
+                                          ("bf16", 600), ("bf16", 700), ("fp4", 1700), ("fp8", 1300),
+                                          ("bf16", 1792), ("bf16", 1850), ("bf16", 2040), ("bf16", 740),
+                                          ("fp4", 1850), ("fp8", 1900)])
 def test_prefix_ending_inside_a_split(pk, dtype, shared):
     """Prompts ending inside a quarter and on a quarter edge, in 1024-key
-    splits and in 256-key ones (600, 700): the splits wholly inside the
-    prompt are group items, the one holding its end and all later ones are
-    each sequence's own; groups of four sequences (G = 4) with tails of
-    different lengths. The output is the plain forward's, bit for bit."""
+    splits and in 256-key ones (600, 700, 740): the splits wholly inside the
+    prompt are group items; the one holding its end is a group item too when
+    the prompt covers its first three quarters (1792, 1850, 2040, 740, 1900:
+    the members' last quarters are computed member by member, some contexts
+    ending inside that quarter), otherwise each sequence's own, as are all
+    later splits; groups of four sequences (G = 4, the last of one) with
+    tails of different lengths. The output is the plain forward's, bit for
+    bit."""
     rng = np.random.default_rng(shared + (dtype == "fp4"))
     n = 9
     ctxs = [shared + int(x) for x in rng.integers(1, 900, size=n)] + [1500]
