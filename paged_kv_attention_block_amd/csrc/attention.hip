@@ -2007,12 +2007,20 @@ __device__ inline int seq_of_row(const int32_t *qsl, int num_seqs, int row) {
 template <int D>
 __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
     constexpr int DU = D / 64;
+    constexpr bool kPreV = D <= 64;  // a chunk's V rows of all four blocks held at once
     const int lane = threadIdx.x;
     const int i = blockIdx.x, h = blockIdx.y;
-    const int s = seq_of_row(P.qsl, P.num_seqs, i);
-    const int q_len = P.qsl[s + 1] - P.qsl[s];
+    // a decode batch's row i is sequence i
+    const int s = P.decode_only ? i : seq_of_row(P.qsl, P.num_seqs, i);
+    // block id of a key's block, read before the key is known to be in the
+    // context (the index clamped to the table row; check() decides)
+    auto bt_at = [&](int key) {
+        return P.bt[(size_t)s * P.max_blocks_per_seq + min(key / kBlock, P.max_blocks_per_seq - 1)];
+    };
+    int raw = P.window == 0 ? bt_at(lane) : 0;  // the first chunk's, beside the context length
+    const int q_len = P.decode_only ? 1 : P.qsl[s + 1] - P.qsl[s];
     const int ctx = P.ctx_lens[s];
-    const int r = i - P.qsl[s];
+    const int r = i - (P.decode_only ? i : P.qsl[s]);
     const int p = ctx - q_len + r;
     if (p < 0) return;
     const int kvh = h / P.G;
@@ -2036,70 +2044,101 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
 #pragma unroll
     for (int u = 0; u < DU; ++u) acc[u] = 0.f;
 
-    for (int kc = lo > 0 ? lo / 64 * 64 : 0; kc <= p; kc += 64) {
+    // the key's block, for every key up to p (lane 16 bb names block bb of
+    // the chunk in the value pass, visible or not), else -1
+    auto check = [&](int key, int b) {
+        return (key <= p && key / kBlock < P.max_blocks_per_seq && b >= 0 && b < P.num_blocks) ? b : -1;
+    };
+    const int kc0 = lo > 0 ? lo / 64 * 64 : 0;
+    if (P.window != 0) raw = bt_at(kc0 + lane);
+    int phys = check(kc0 + lane, raw);
+    for (int kc = kc0; kc <= p; kc += 64) {
         const int key = kc + lane;
         const bool vis = key <= p && key >= lo && (!tree || key < wbase || ((tm >> (key - wbase)) & 1u));
-        // the key's block, for every key up to p: lane 16 bb names block bb of
-        // the chunk in the value pass, visible or not
-        int phys = -1;
-        if (key <= p) {
-            const int jb = key / kBlock;
-            if (jb < P.max_blocks_per_seq) {
-                const int b = P.bt[(size_t)s * P.max_blocks_per_seq + jb];
-                phys = (b >= 0 && b < P.num_blocks) ? b : -1;
+        // every read of the chunk first, with no branch between them: the
+        // lane's key row, the V rows of the chunk's blocks (lane d: channel d)
+        // and the next chunk's block ids. Keys and blocks outside the row read
+        // block 0 (max(b, 0)), whose values the loop below never uses.
+        const float *kb = kp + ((size_t)max(phys, 0) * P.Hkv + kvh) * tile;
+        const int o = key % kBlock;
+        f32x4_t kx[D / 4];
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) kx[c] = *reinterpret_cast<const f32x4_t *>(kb + (c * kBlock + o) * 4);
+        float vv[kPreV ? 4 : 1][DU][kBlock];
+        if constexpr (kPreV) {
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int pb = max(__builtin_amdgcn_readlane(phys, kBlock * bb), 0);
+#pragma unroll
+                for (int u = 0; u < DU; ++u) {
+                    const float *vrow = vp + ((size_t)pb * P.Hkv + kvh) * tile + (size_t)(lane + 64 * u) * kBlock;
+#pragma unroll
+                    for (int q4 = 0; q4 < kBlock / 4; ++q4) {
+                        const f32x4_t x = *reinterpret_cast<const f32x4_t *>(vrow + 4 * q4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) vv[bb][u][4 * q4 + e] = x[e];
+                    }
+                }
             }
         }
+        const int raw_next = kc + 64 <= p ? bt_at(kc + 64 + lane) : 0;
         float dot = 0.f;
         if (vis && phys >= 0) {
-            const float *kb = kp + ((size_t)phys * P.Hkv + kvh) * tile;
-            const int o = key % kBlock;
 #pragma unroll
             for (int c = 0; c < D / 4; ++c) {
-                const f32x4_t kv = *reinterpret_cast<const f32x4_t *>(kb + (c * kBlock + o) * 4);
-                dot = fmaf(qs[4 * c + 0], kv[0], dot);
-                dot = fmaf(qs[4 * c + 1], kv[1], dot);
-                dot = fmaf(qs[4 * c + 2], kv[2], dot);
-                dot = fmaf(qs[4 * c + 3], kv[3], dot);
+                dot = fmaf(qs[4 * c + 0], kx[c][0], dot);
+                dot = fmaf(qs[4 * c + 1], kx[c][1], dot);
+                dot = fmaf(qs[4 * c + 2], kx[c][2], dot);
+                dot = fmaf(qs[4 * c + 3], kx[c][3], dot);
             }
         }
         const float sc = vis ? dot * P.scale_log2 : -INFINITY;
         float mx = sc;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        if (mx == -INFINITY) continue;  // no visible key in the chunk (wave-uniform)
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - m_new);
-        const float pv = fast_exp2(sc - m_new);
-        float rs = pv;
+        for (int o2 = 32; o2 >= 1; o2 >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o2, 64));
+        if (mx != -INFINITY) {  // some key of the chunk visible (wave-uniform)
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - m_new);
+            const float pv = fast_exp2(sc - m_new);
+            float rs = pv;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) rs += __shfl_xor(rs, o, 64);
-        l = fmaf(alpha, l, rs);
-        m = m_new;
+            for (int o2 = 32; o2 >= 1; o2 >>= 1) rs += __shfl_xor(rs, o2, 64);
+            l = fmaf(alpha, l, rs);
+            m = m_new;
 #pragma unroll
-        for (int u = 0; u < DU; ++u) acc[u] *= alpha;
-        for (int bb = 0; bb < 4; ++bb) {
-            const int kb0 = kc + kBlock * bb;
-            if (kb0 > p) break;
-            const int pb = __builtin_amdgcn_readlane(phys, kBlock * bb);
-            if (pb < 0) continue;
+            for (int u = 0; u < DU; ++u) acc[u] *= alpha;
 #pragma unroll
-            for (int u = 0; u < DU; ++u) {
-                const float *vrow = vp + ((size_t)pb * P.Hkv + kvh) * tile + (size_t)(lane + 64 * u) * kBlock;
-                float vv[kBlock];
+            for (int bb = 0; bb < 4; ++bb) {
+                const int kb0 = kc + kBlock * bb;
+                if (kb0 > p) break;
+                const int pb = __builtin_amdgcn_readlane(phys, kBlock * bb);
+                if (pb < 0) continue;
 #pragma unroll
-                for (int q4 = 0; q4 < kBlock / 4; ++q4) {
-                    const f32x4_t x = *reinterpret_cast<const f32x4_t *>(vrow + 4 * q4);
+                for (int u = 0; u < DU; ++u) {
+                    float w8[kBlock];
+                    if constexpr (kPreV) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) vv[4 * q4 + e] = x[e];
-                }
+                        for (int tt = 0; tt < kBlock; ++tt) w8[tt] = vv[bb][u][tt];
+                    } else {
+                        const float *vrow =
+                            vp + ((size_t)pb * P.Hkv + kvh) * tile + (size_t)(lane + 64 * u) * kBlock;
 #pragma unroll
-                for (int tt = 0; tt < kBlock; ++tt) {
-                    const float w = bcast(pv, kBlock * bb + tt);
-                    const float v = kb0 + tt <= p ? vv[tt] : 0.f;
-                    acc[u] = fmaf(w, v, acc[u]);
+                        for (int q4 = 0; q4 < kBlock / 4; ++q4) {
+                            const f32x4_t x = *reinterpret_cast<const f32x4_t *>(vrow + 4 * q4);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) w8[4 * q4 + e] = x[e];
+                        }
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < kBlock; ++tt) {
+                        const float w = bcast(pv, kBlock * bb + tt);
+                        const float v = kb0 + tt <= p ? w8[tt] : 0.f;
+                        acc[u] = fmaf(w, v, acc[u]);
+                    }
                 }
             }
         }
+        phys = check(kc + 64 + lane, raw_next);
     }
     float lt = l;
     float al = 1.f;
@@ -2118,10 +2157,11 @@ __global__ __launch_bounds__(64) void attn_f32(AttnParams P) {
 // Every read is issued first: the tokens' slots, the group's K pieces in the
 // tile's order (piece p is chunk p / 16 of token p % 16, so that a whole
 // block goes out in contiguous 16-byte pieces) and its V rows row-major,
-// which go to LDS before the one barrier. Where the 16 tokens fill one block in order (a prefill
-// chunk, a verify window), the K tile and the transposed V tile are written
-// as whole 16-byte pieces, the V columns gathered from LDS; otherwise each
-// token's K chunks are 16-byte stores and its V values single-element stores.
+// which go to LDS before the one barrier. Where the 16 tokens fill one
+// block in order (a prefill chunk, a verify window), the K tile and the
+// transposed V tile are written as whole 16-byte pieces, the V columns
+// gathered from LDS; otherwise each token's K chunks are 16-byte stores and
+// its V values single-element stores.
 // ---------------------------------------------------------------------------
 template <typename T, int kMaxP>  // kMaxP: pieces per lane, 16 tokens x D / X pieces over 256 lanes
 __global__ __launch_bounds__(256) void scatter_kernel(const T *__restrict__ kn, const T *__restrict__ vn,
