@@ -71,6 +71,21 @@ def test_decode_batch_group_sizes(pk, Hq, Hkv, D):
     _check(pk, w, n, (2200 // 16) * 16, oracle_sample=[0, 5, 10, 11, 12])
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(64, 8, 64), (16, 8, 128), (32, 8, 128), (12, 4, 128), (8, 8, 64)])
+def test_decode_batch_group_sizes_at_the_prompt_end(pk, Hq, Hkv, D):
+    """A 2900-token prompt: the split holding its end (2048-3071) is a group
+    item too, its first three quarters shared and the members' last quarters
+    computed member by member (G = 8: two members a group, G = 2, 4, 3, 1:
+    four), contexts ending inside that split and past it, a last group of
+    three sequences."""
+    rng = np.random.default_rng(Hq * 100 + Hkv + D)
+    n = 11
+    ctxs = [2900 + int(x) for x in rng.integers(1, 700, size=n)] + [900, 4000]
+    w = custom("bf16", Hq, Hkv, D, ctxs, [1] * len(ctxs), seed=int(rng.integers(1 << 30)), sinks=True,
+               shared_prefix=2900, n_shared=n)
+    _check(pk, w, n, (2900 // 16) * 16, oracle_sample=[0, 5, 10, 11, 12])
+
+
 def test_more_heads_per_group_than_a_tile_shares(pk):
     """16 query heads per KV head: no groups (a member fills the tile), the plain grid."""
     w = custom("bf16", 32, 2, 64, [1500, 1700, 1600], [1, 1, 1], seed=401, shared_prefix=1300, n_shared=3)
