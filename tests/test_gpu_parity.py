@@ -176,11 +176,13 @@ def test_workspace_reuse(pk):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [16, 48, 64, 128, 256])
 def test_scatter_patterns_bit_exact(pk, dtype, D):
     """kv_append_scatter against the oracle scatter on slot patterns that mix
     whole blocks written in order (the 16-byte-piece path), runs shifted
-    inside blocks, reversed runs, skipped slots (-1) and a ragged last group."""
+    inside blocks, reversed runs, skipped slots (-1) and a ragged last group.
+    Head sizes from 16 to 256 take one, two or four 16-byte pieces per lane,
+    and rows that leave lanes without a piece of their own."""
     import torch
     import oracle
     rng = np.random.default_rng(31 + D + (dtype == "bf16"))
