@@ -119,7 +119,8 @@ class _Pool:
         self.ptr, self.num_blocks, self.block_size = ptr, num_blocks, block_size
 
     def __del__(self):
-        if getattr(self, "ptr", None):
+        # at interpreter exit the module's globals may already be cleared
+        if getattr(self, "ptr", None) and _lib is not None:
             _lib.kv_pool_destroy(self.ptr)
             self.ptr = None
 

@@ -2655,9 +2655,19 @@ static void launch_fold(const AttnParams &P, hipStream_t st) {
 }
 
 template <int D, int KF, bool MASKED>
-static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
+static void launch_sequential(const AttnParams &P, int total_rows, hipStream_t st) {
+    const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
+    hipLaunchKernelGGL((attn_sequential<D, KF, MASKED>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
+}
+
+// The split and fold launches go to `st`; the sequential shape, when the
+// batch has rows for it, to `seq_st`. When that is another stream it is
+// launched first, so that its long row blocks are dispatched first.
+template <int D, int KF, bool MASKED>
+static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st, hipStream_t seq_st) {
     const int rows_per_seq = max_q_len * P.G;
     const bool fold = P.max_splits > 1;
+    if (rows_per_seq > kParRows && seq_st != st) launch_sequential<D, KF, MASKED>(P, total_rows, seq_st);
     if (P.G > kParRows) {
         // Every sequence brings at least G > 32 rows to its KV head: all of
         // them take the sequential shape, and the split and fold launches
@@ -2697,16 +2707,62 @@ static void launch_mfma(const AttnParams &P, int max_q_len, int total_rows, hipS
         if (fold)
             launch_fold<D, 2>(P, st);
     }
-    if (rows_per_seq > kParRows) {
-        const int64_t items = ((int64_t)total_rows * P.G + kSeqRows - 1) / kSeqRows + P.num_seqs;
-        hipLaunchKernelGGL((attn_sequential<D, KF, MASKED>), dim3((unsigned)(items * P.Hkv)), dim3(256), 0, st, P);
-    }
+    if (rows_per_seq > kParRows && seq_st == st) launch_sequential<D, KF, MASKED>(P, total_rows, st);
 }
 
 template <int D, int KF>
-static void launch_mfma_vis(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st) {
-    if (P.tree_mask || P.window > 0) launch_mfma<D, KF, true>(P, max_q_len, total_rows, st);
-    else launch_mfma<D, KF, false>(P, max_q_len, total_rows, st);
+static void launch_mfma_vis(const AttnParams &P, int max_q_len, int total_rows, hipStream_t st,
+                            hipStream_t seq_st) {
+    if (P.tree_mask || P.window > 0) launch_mfma<D, KF, true>(P, max_q_len, total_rows, st, seq_st);
+    else launch_mfma<D, KF, false>(P, max_q_len, total_rows, st, seq_st);
+}
+
+// A batch holding both prefill chunks and decode rows, captured into a
+// graph, runs its two shapes on two streams: the sequential launch beside
+// the split launch, which is bound by its dispatch and drain, not by the
+// compute units the sequential shape keeps busy. The launches share no
+// buffer: the sequential shape writes only its own rows' outputs, and the
+// split and fold launches skip those rows. Each device has one side stream,
+// at the default priority, forked from the caller's stream and joined back
+// into it by two events; in the graph these become two edges. Eager calls
+// keep both launches on the caller's stream: there the event pair costs
+// more host and queue time than the overlap saves.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool tried = false;
+};
+// Held from the fork's record to the join's, so that every wait sees the
+// record of its own call.
+static std::mutex g_side_mu;
+
+// The side stream of the device `st` belongs to, created at the first call
+// with both shapes on that device that is not under graph capture (a capture
+// uses it, never creates it); nullptr where there is none (the sequential
+// launch then stays on `st`). Called with g_side_mu held.
+static const SideStream *side_stream(hipStream_t st) {
+    static SideStream side[64];
+    int dev = 0, cur = 0;
+    if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    SideStream &x = side[dev];
+    if (x.s || x.tried) return x.s ? &x : nullptr;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) return nullptr;
+    x.tried = true;  // a failed creation leaves this device on one stream
+    const bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+        if (x.join) (void)hipEventDestroy(x.join);
+        if (x.fork) (void)hipEventDestroy(x.fork);
+        if (x.s) (void)hipStreamDestroy(x.s);
+        x.s = nullptr;
+        x.fork = x.join = nullptr;
+    }
+    if (cur != dev) (void)hipSetDevice(cur);
+    return x.s ? &x : nullptr;
 }
 
 }  // namespace pkv
@@ -2787,7 +2843,7 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                         float scale, const float *sinks, float *out, void *workspace, size_t workspace_bytes,
                         void *hip_stream, const AppendArgs *app, const MaskArgs *mk,
-                        const PrefixArgs *pre = nullptr) {
+                        const PrefixArgs *pre = nullptr, bool may_fork = true) {
     if (dtype != KV_BF16 && dtype != KV_F32 && dtype != KV_FP8 && dtype != KV_FP4)
         PKV_FAIL(KV_EUNSUPPORTED, "paged_attention_forward: dtype %d not supported", dtype);
     if (head_dim != 64 && head_dim != 128)
@@ -2925,22 +2981,46 @@ static int forward_impl(const void *q, const void *k_pool, const void *v_pool, i
         }
     }
 
+    // both shapes in one batch, under graph capture: the sequential one on
+    // the side stream
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    const SideStream *sd = nullptr;
+    hipStream_t seq_st = st;
+    if (may_fork && dtype != KV_F32 && (int64_t)max_q_len * P.G > kParRows && P.G <= kParRows) {
+        side_lock.lock();
+        sd = side_stream(st);
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (sd && hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive &&
+            hipEventRecord(sd->fork, st) == hipSuccess && hipStreamWaitEvent(sd->s, sd->fork, 0) == hipSuccess) {
+            seq_st = sd->s;
+        } else {
+            sd = nullptr;
+            side_lock.unlock();
+        }
+    }
     (void)hipGetLastError();
     if (dtype == KV_BF16) {
-        if (head_dim == 64) launch_mfma_vis<64, kKvBf16>(P, max_q_len, total_q_rows, st);
-        else launch_mfma_vis<128, kKvBf16>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, kKvBf16>(P, max_q_len, total_q_rows, st, seq_st);
+        else launch_mfma_vis<128, kKvBf16>(P, max_q_len, total_q_rows, st, seq_st);
     } else if (dtype == KV_FP8) {
-        if (head_dim == 64) launch_mfma_vis<64, kKvFp8>(P, max_q_len, total_q_rows, st);
-        else launch_mfma_vis<128, kKvFp8>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, kKvFp8>(P, max_q_len, total_q_rows, st, seq_st);
+        else launch_mfma_vis<128, kKvFp8>(P, max_q_len, total_q_rows, st, seq_st);
     } else if (dtype == KV_FP4) {
-        if (head_dim == 64) launch_mfma_vis<64, kKvFp4>(P, max_q_len, total_q_rows, st);
-        else launch_mfma_vis<128, kKvFp4>(P, max_q_len, total_q_rows, st);
+        if (head_dim == 64) launch_mfma_vis<64, kKvFp4>(P, max_q_len, total_q_rows, st, seq_st);
+        else launch_mfma_vis<128, kKvFp4>(P, max_q_len, total_q_rows, st, seq_st);
     } else {
         const dim3 grid(total_q_rows, num_q_heads);
         if (head_dim == 64) hipLaunchKernelGGL((attn_f32<64>), grid, dim3(64), 0, st, P);
         else hipLaunchKernelGGL((attn_f32<128>), grid, dim3(64), 0, st, P);
     }
     const hipError_t e = hipGetLastError();
+    if (sd) {
+        // the caller's stream waits for the side stream's launch
+        hipError_t j = hipEventRecord(sd->join, sd->s);
+        if (j == hipSuccess) j = hipStreamWaitEvent(st, sd->join, 0);
+        if (j != hipSuccess)
+            PKV_FAIL(KV_EDEVICE, "paged_attention_forward: joining the side stream failed: %s", hipGetErrorString(j));
+    }
     if (e != hipSuccess)
         PKV_FAIL(KV_EDEVICE, "paged_attention_forward: launch failed: %s", hipGetErrorString(e));
     return KV_OK;
@@ -2986,7 +3066,7 @@ int paged_attention_forward_noalloc(const void *q, const void *k_pool, const voi
     return pkv::forward_impl(q, k_pool, v_pool, dtype, block_tables, max_blocks_per_seq, context_lens,
                              query_start_loc, num_seqs, total_q_rows, max_q_len, max_context_len, num_q_heads,
                              num_kv_heads, head_dim, block_size, num_blocks, scale, sinks, out, ws,
-                             pkv::kScratchBytes, hip_stream, nullptr, nullptr);
+                             pkv::kScratchBytes, hip_stream, nullptr, nullptr, nullptr, /*may_fork=*/false);
 }
 
 int paged_attention_prefix_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,

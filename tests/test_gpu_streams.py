@@ -63,3 +63,76 @@ def test_side_stream_with_allocations_on_the_current_stream(pk, kind):
     torch.cuda.synchronize()
     for o in outs:
         np.testing.assert_array_equal(_bits(o), want)
+
+
+def _mixed(dtype, seed):
+    """Decode rows beside two prefill chunks: the chunks (more than 32 rows
+    per KV head) take the sequential launch, the decode rows the split
+    launch."""
+    return custom(dtype, 32, 8, 128, [3000, 1100, 700, 2500, 1500, 900], [1, 300, 1, 64, 1, 1], seed=seed,
+                  sinks=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp4"])
+def test_mixed_batch_on_two_streams(pk, dtype):
+    """A batch with prefill chunks and decode rows, called eagerly (both
+    launches on the caller's stream). Sampled rows of both shapes match the
+    oracle; the whole output equals, bit for bit, the no-workspace entry
+    point's; a call on a stream other than the current one, with the current
+    stream allocating and filling memory meanwhile, gives the same bits."""
+    import torch
+    from gpu_util import TOL, max_err, oracle_rows
+    from paged_kv_attention_block_amd.staging import stage
+    w = _mixed(dtype, 511)
+    print(f"\n[case] two streams {dtype}", flush=True)
+    st = stage(w)
+    got = run_forward(pk, st, w).cpu().numpy()
+    qsl = [int(x) for x in w.qsl]
+    rows = [qsl[0], qsl[2], qsl[4], qsl[5], qsl[1], qsl[1] + 137, qsl[2] - 1, qsl[3], qsl[4] - 1]
+    want = oracle_rows(w, rows)
+    assert max_err(got[rows], want) < TOL[dtype]
+    serial = pk.paged_attention_forward_noalloc(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens,
+                                                st.qsl, st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks,
+                                                out=torch.empty_like(st.out))
+    np.testing.assert_array_equal(_bits(serial), got.view(np.uint32))
+    side = torch.cuda.Stream()
+    outs, junk = [], []
+    for _ in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        outs.append(pk.paged_attention_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens,
+                                               st.qsl, st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks,
+                                               stream=side))
+        junk.append(torch.full((st.out.numel() + 4096,), float("nan"), dtype=torch.float32, device=st.q.device))
+    torch.cuda.synchronize()
+    for o in outs:
+        np.testing.assert_array_equal(_bits(o), got.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp4"])
+def test_mixed_batch_in_a_graph(pk, dtype):
+    """The same batch captured into a HIP graph, where the chunks' launch
+    runs on the library's side stream beside the decode rows' launches (the
+    side stream joins the capture through the fork event and rejoins the
+    caller's stream through the join event). Every replay equals the eager
+    call bit for bit, with eager calls and synchronizations between the
+    replays."""
+    import torch
+    from paged_kv_attention_block_amd.staging import stage
+    w = _mixed(dtype, 521)
+    print(f"\n[case] graph {dtype}", flush=True)
+    st = stage(w)
+    want = _bits(run_forward(pk, st, w))
+    out = torch.empty_like(st.out)
+    ws = torch.empty_like(st.workspace)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pk.paged_attention_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens, st.qsl,
+                                   st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=out, workspace=ws)
+    for i in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits(out), want, err_msg=f"replay {i}")
+        np.testing.assert_array_equal(_bits(run_forward(pk, st, w)), want, err_msg=f"eager after replay {i}")
+        torch.cuda.synchronize()
