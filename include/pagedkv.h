@@ -372,6 +372,15 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t total_q_rows,
  * Supported: head_dim 64 or 128, block_size 16, dtype KV_BF16, KV_F32,
  * KV_FP8 or KV_FP4 (q in bf16, pools of 8- or 4-bit tiles: the keys and
  * values are the stored codes times their scales).
+ * Streams: every launch is ordered on hip_stream. A batch with both prefill
+ * chunks (more than 32 rows per sequence and KV head) and shorter rows,
+ * captured into a graph on hip_stream, runs the prefill launch on a side
+ * stream the library keeps for the device (created, at default priority, by
+ * the first such call made outside capture; without one the capture stays
+ * on hip_stream), forked from hip_stream and joined back into it by events,
+ * so the two launches run side by side in the graph. Calls made at the same
+ * time from several host threads on one device must not mix a capture with
+ * calls outside it: the side stream belongs to the capture until it ends.
  * Errors: KV_EINVAL, KV_EUNSUPPORTED, KV_EDEVICE.
  */
 int paged_attention_forward(const void *q, const void *k_pool, const void *v_pool, int32_t dtype,
@@ -424,7 +433,8 @@ int paged_attention_prefix_forward(const void *q, const void *k_pool, const void
  * nothing. Every call on one device shares that device's array, and the
  * array needs no clearing (each call writes every split state it reads), so
  * calls that may overlap on one device (different streams, or several host
- * threads) race and must be serialized by the caller.
+ * threads) race and must be serialized by the caller. Every launch stays
+ * on hip_stream (no side stream, under capture or not).
  * Errors: those of paged_attention_forward; KV_EINVAL also when the batch
  * needs more than 64 MiB of split states (paged_attention_workspace_size of
  * its sizes), with the number in the message; KV_EDEVICE when the scratch
