@@ -108,31 +108,49 @@ def test_mixed_batch_on_two_streams(pk, dtype):
         np.testing.assert_array_equal(_bits(o), got.view(np.uint32))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp4"])
-def test_mixed_batch_in_a_graph(pk, dtype):
+@pytest.mark.parametrize("dtype,window", [("bf16", 0), ("fp4", 0), ("bf16", 200), ("fp8", 700)])
+def test_mixed_batch_in_a_graph(pk, dtype, window):
     """The same batch captured into a HIP graph, where the chunks' launch
     runs on the library's side stream beside the decode rows' launches (the
     side stream joins the capture through the fork event and rejoins the
     caller's stream through the join event). Every replay equals the eager
     call bit for bit, with eager calls and synchronizations between the
-    replays."""
+    replays. With a sliding window the masked instances take the same two
+    streams."""
     import torch
     from paged_kv_attention_block_amd.staging import stage
-    w = _mixed(dtype, 521)
-    print(f"\n[case] graph {dtype}", flush=True)
+    w = _mixed(dtype, 521 + window)
+    print(f"\n[case] graph {dtype} window={window}", flush=True)
     st = stage(w)
-    want = _bits(run_forward(pk, st, w))
+
+    def call(out=None, ws=None):
+        if window:
+            return pk.paged_attention_masked_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables,
+                                                     st.context_lens, st.qsl, st.max_q_len, st.max_context_len,
+                                                     w.scale, sinks=st.sinks, sliding_window=window,
+                                                     out=out if out is not None else st.out,
+                                                     workspace=ws if ws is not None else st.workspace)
+        return pk.paged_attention_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens, st.qsl,
+                                          st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks,
+                                          out=out if out is not None else st.out,
+                                          workspace=ws if ws is not None else st.workspace)
+
+    want = _bits(call())
+    if window:
+        # the window is real: the last row of the 300-row chunk differs from its unmasked value
+        full = _bits(run_forward(pk, st, w))
+        r = int(w.qsl[2]) - 1
+        assert not np.array_equal(full[r], want[r])
     out = torch.empty_like(st.out)
     ws = torch.empty_like(st.workspace)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        pk.paged_attention_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens, st.qsl,
-                                   st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=out, workspace=ws)
+        call(out, ws)
     for i in range(3):
         out.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(_bits(out), want, err_msg=f"replay {i}")
-        np.testing.assert_array_equal(_bits(run_forward(pk, st, w)), want, err_msg=f"eager after replay {i}")
+        np.testing.assert_array_equal(_bits(call()), want, err_msg=f"eager after replay {i}")
         torch.cuda.synchronize()
