@@ -2751,15 +2751,18 @@ static const SideStream *side_stream(hipStream_t st) {
     if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
     if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) return nullptr;
     x.tried = true;  // a failed creation leaves this device on one stream
-    const bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
-                    hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
-                    hipEventCreateWithFlags(&x.join, hipEventDisableTiming) == hipSuccess;
-    if (!ok) {
-        if (x.join) (void)hipEventDestroy(x.join);
-        if (x.fork) (void)hipEventDestroy(x.fork);
-        if (x.s) (void)hipStreamDestroy(x.s);
-        x.s = nullptr;
-        x.fork = x.join = nullptr;
+    hipStream_t sn = nullptr;
+    hipEvent_t fk = nullptr, jn = nullptr;
+    const bool s_ok = hipStreamCreateWithFlags(&sn, hipStreamNonBlocking) == hipSuccess;
+    const bool f_ok = s_ok && hipEventCreateWithFlags(&fk, hipEventDisableTiming) == hipSuccess;
+    const bool j_ok = f_ok && hipEventCreateWithFlags(&jn, hipEventDisableTiming) == hipSuccess;
+    if (j_ok) {
+        x.s = sn;
+        x.fork = fk;
+        x.join = jn;
+    } else {  // release only what was created
+        if (f_ok) (void)hipEventDestroy(fk);
+        if (s_ok) (void)hipStreamDestroy(sn);
     }
     if (cur != dev) (void)hipSetDevice(cur);
     return x.s ? &x : nullptr;
