@@ -1698,6 +1698,12 @@ __global__ __launch_bounds__(256) void attn_fold(AttnParams P) {
     const int s = blockIdx.x, kvh = blockIdx.y;
     const int cell = blockIdx.z * CPG + tid / LPC;  // rho = r * G + hl within the sequence
     const int e = (tid % LPC) * 4;                  // the lane's first channel
+    // Every kernel argument the fold reads, in scalar registers before the
+    // first branch: one round trip for all of them (a workgroup per CU meets
+    // a cold scalar cache) instead of one after each branch.
+    asm volatile("" ::"s"(P.decode_only), "s"(P.G), "s"(P.total_rows), "s"(P.Hq), "s"(P.max_splits),
+                 "s"(P.grid_splits), "s"(P.window), "s"(P.qsl), "s"(P.ctx_lens), "s"(P.ws_ml), "s"(P.ws_acc),
+                 "s"(P.out), "s"(P.sinks));
     int q0, q_len;
     if (P.decode_only) {
         q0 = s;
