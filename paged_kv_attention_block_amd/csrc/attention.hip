@@ -1076,6 +1076,19 @@ __device__ inline int split_of_slot(int z, int max_splits) {
 // number of keys and the short items come last. The price is a round trip:
 // the block ids wait for the context lengths. Returns false for a slot past
 // all of them. The item computed is the same whichever workgroup takes it.
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP: row shifts
+// within each row of 16 lanes, then the row totals through the row
+// broadcasts of lanes 15 and 31 (no LDS round trip, unlike lane shuffles).
+__device__ inline int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 __device__ inline bool balanced_item(const AttnParams &P, int rank, int cap_rows, int lane, int &s, int &j, int &ctx,
                                      int &qa, int &qb) {
     const bool in = lane < P.num_seqs;
@@ -1093,15 +1106,7 @@ __device__ inline bool balanced_item(const AttnParams &P, int rank, int cap_rows
     const int nE = ok ? P.max_splits - ns : 0;
     // inclusive scans over the lanes, two 16-bit counts per word
     const int v0 = nA | (nE << 16), v1 = part | (nB << 16);
-    int i0 = v0, i1 = v1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int u0 = __shfl_up(i0, o, 64), u1 = __shfl_up(i1, o, 64);
-        if (lane >= o) {
-            i0 += u0;
-            i1 += u1;
-        }
-    }
+    const int i0 = wave_incl_scan(v0), i1 = wave_incl_scan(v1);
     const int t0 = __builtin_amdgcn_readlane(i0, 63), t1 = __builtin_amdgcn_readlane(i1, 63);
     const int NA = t0 & 0xffff, NE = t0 >> 16, NP = t1 & 0xffff, NB = t1 >> 16;
     int r = rank, cls, hi, cnt;
@@ -1814,12 +1819,7 @@ __device__ inline bool find_seq_item(const int32_t *qsl, int S, int G, int item,
             const int rows = (qsl[t + 1] - qsl[t]) * G;
             nb = rows > kParRows ? (rows + kSeqRows - 1) / kSeqRows : 0;
         }
-        int incl = nb;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += v;
-        }
+        const int incl = wave_incl_scan(nb);
         const int excl = incl - nb;
         const bool hit = t < S && item >= base + excl && item < base + incl;
         const unsigned long long mask = __ballot(hit);
