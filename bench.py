@@ -11,7 +11,8 @@ touches more memory than the 256 MB last-level cache holds and the reported
 bandwidth is HBM bandwidth. Block allocation (kv_pool_alloc) happens once per
 batch on the host and is timed separately.
 
-Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus above 1 is refused: the library runs on one GPU
+(the path would shard by KV heads or sequences; no collective is built).
 """
 from __future__ import annotations
 
@@ -279,7 +280,7 @@ def summarize_profile(d, workload, commands, producer=False):
     title = "Producer kernel (kv_qknorm_rope_scatter)" if producer else "Attention kernels"
     lines = [f"# {title}, workload {workload}", "",
              f"Source digest (sha256/16 of {os.path.basename(src)}): `{source_digest(src)}`", "",
-             "Commands (repository root, rocprofv3 output under gpurun_out/):", ""]
+             "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in commands]
     lines += ["", "## Kernel durations (rocprofv3 --kernel-trace --stats)", "",
               "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
@@ -348,7 +349,7 @@ def summarize_mfma(d, workload, commands):
         acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     lines = [f"# MFMA and VALU counters, workload {workload}", "",
              f"Source digest (sha256/16 of {os.path.basename(ATTN_SOURCE)}): `{source_digest()}`", "",
-             "Command (repository root, rocprofv3 output under gpurun_out/):", ""]
+             "Command (run from the repository root):", ""]
     lines += [f"    {c}" for c in commands]
     lines += ["", "Per dispatch, averaged over the run's dispatches of each kernel. MFMA utilisation:",
               "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), as rocprofv3's MfmaUtil;",
@@ -479,7 +480,7 @@ def main(argv=None):
         return summarize_mfma(args.summarize_mfma, args.workload, args.commands)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+        print("bench.py: the library runs on one GPU only; multi-GPU runs are not supported "
               "(--gpus must be 1).", file=sys.stderr)
         return 2
 
