@@ -154,3 +154,40 @@ def test_mixed_batch_in_a_graph(pk, dtype, window):
         np.testing.assert_array_equal(_bits(out), want, err_msg=f"replay {i}")
         np.testing.assert_array_equal(_bits(call()), want, err_msg=f"eager after replay {i}")
         torch.cuda.synchronize()
+
+
+def test_two_mixed_graphs_replayed_side_by_side(pk):
+    """Two mixed batches, each captured into its own graph (both graphs hold
+    branches on the library's side stream), replayed at the same time on two
+    streams, several times: every replay equals its eager call bit for bit."""
+    import torch
+    from paged_kv_attention_block_amd.staging import stage
+    cases = []
+    for seed, dtype in ((531, "bf16"), (532, "fp4")):
+        w = _mixed(dtype, seed)
+        st = stage(w)
+        want = _bits(run_forward(pk, st, w))
+        out = torch.empty_like(st.out)
+        ws = torch.empty_like(st.workspace)
+        cases.append((w, st, want, out, ws))
+    print("\n[case] two graphs side by side", flush=True)
+    torch.cuda.synchronize()
+    graphs = []
+    for w, st, _, out, ws in cases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            pk.paged_attention_forward(st.q, st.k_pools[0], st.v_pools[0], st.tables, st.context_lens, st.qsl,
+                                       st.max_q_len, st.max_context_len, w.scale, sinks=st.sinks, out=out,
+                                       workspace=ws)
+        graphs.append(g)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i in range(3):
+        for _, _, _, out, _ in cases:
+            out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for g, s in zip(graphs, streams):
+            with torch.cuda.stream(s):
+                g.replay()
+        torch.cuda.synchronize()
+        for k, (_, _, want, out, _) in enumerate(cases):
+            np.testing.assert_array_equal(_bits(out), want, err_msg=f"graph {k} replay {i}")
